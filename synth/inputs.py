@@ -1,0 +1,266 @@
+"""Workload shapes and seeded input recipes (no arithmetic of the method).
+
+Workloads mirror the pages' setting: a denoising block of 32 positions, a main
+branch plus B drafts arranged as a parent tree of depth at most 4, drafts that
+add one to four newly unmasked positions where hidden states diverge strongly
+and stay close to the parent elsewhere.  The closeness is drawn so that, at the
+first layer, 72 % of draft rows have relative residual <= 0.1 and 88 % have
+<= 0.3 -- the redundancy profile reported in the SpecFold summary (paperlayer.ai,
+§3.1) and the Korean review (onedev.kr, section "어떻게 동작하나").  Model
+sizes follow the 1.5B / 7B / 14B-class shapes of the evaluated model families.
+
+Seeds: every tensor comes from ``default_rng([base_seed, step, layer, tensor_id])``.
+Weights and prefix caches use ``step = 0`` so they stay fixed across the steps of
+a multi-step workload; hidden states and trees use ``layer = 0``.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+# tensor ids inside a seed tuple
+_T_LN1, _T_WQKV, _T_WO, _T_LN2, _T_WGU, _T_WDOWN, _T_PK, _T_PV = range(8)
+_T_TREE, _T_MAIN, _T_CHILD = 10, 11, 12
+
+# Log-normal law of a draft row's relative distance r (non-unmasked rows) chosen so
+# that, with E[#unmasked]/N = 2.5/32, P(r <= 0.1) = 0.72 and P(r <= 0.3) = 0.88 over
+# all draft rows (unmasked rows sit near sqrt(2) and never fold at delta <= 0.7).
+LOGNORMAL_MU = -3.2335
+LOGNORMAL_SIGMA = 1.2003
+
+
+@dataclass(frozen=True)
+class Shape:
+    """Sizes of one verification layer.
+
+    n_branch = B + 1 (main + drafts); block = N positions per branch;
+    hidden = D; n_q_heads / n_kv_heads = Hq / Hkv (grouped-query attention);
+    head_dim = d; ffn = F (SwiGLU width); prefix_len = P shared prefix tokens.
+    """
+
+    n_branch: int
+    block: int
+    hidden: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    ffn: int
+    prefix_len: int
+    rms_eps: float = 1e-6
+    rope_theta: float = 10000.0
+
+    @property
+    def rows(self) -> int:
+        return self.n_branch * self.block
+
+    @property
+    def qkv_out(self) -> int:
+        return (self.n_q_heads + 2 * self.n_kv_heads) * self.head_dim
+
+    def with_branches(self, n_branch: int) -> "Shape":
+        return Shape(n_branch, self.block, self.hidden, self.n_q_heads, self.n_kv_heads,
+                     self.head_dim, self.ffn, self.prefix_len, self.rms_eps, self.rope_theta)
+
+    def weight_bytes_bf16(self) -> int:
+        d, dq = self.hidden, self.n_q_heads * self.head_dim
+        return 2 * (self.qkv_out * d + d * dq + 3 * self.ffn * d + 2 * d)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    shape: Shape
+    base_seed: int
+    delta: float
+    layers: int = 1
+    steps: int = 1
+    tree: str = "random"            # "random" (depth <= 4) or "chain"
+    child_law: str = "lognormal"    # "lognormal" (with unmasked rows) or "tiny"
+    branch_sweep: tuple = ()
+    delta_sweep: tuple = ()
+    note: str = ""
+
+
+WORKLOADS: dict[str, Workload] = {
+    # tiny single layer: hidden 64, 4 q heads / 2 kv heads, head_dim 16, FFN 128,
+    # block 8, main + 2 drafts in a chain main<-d1<-d2, prefix 16, delta 0.1, seed 0
+    "tiny": Workload("tiny", Shape(3, 8, 64, 4, 2, 16, 128, 16), 0, 0.1,
+                     tree="chain", child_law="tiny"),
+    # one layer at 1.5B-class shape, B = 8 drafts, prefix 512
+    "layer-1.5b": Workload("layer-1.5b", Shape(9, 32, 1536, 12, 2, 128, 8960, 512), 1, 0.1),
+    # 28-layer stack at 1.5B-class shape, prefix 2048, 8 steps with a new tree each step
+    "stack-1.5b": Workload("stack-1.5b", Shape(9, 32, 1536, 12, 2, 128, 8960, 2048), 2, 0.1,
+                           layers=28, steps=8),
+    # 28-layer stack at 7B-class shape, prefix 2048
+    "stack-7b": Workload("stack-7b", Shape(9, 32, 3584, 28, 4, 128, 18944, 2048), 3, 0.1,
+                         layers=28),
+    # one layer at 14B-class shape, prefix 4096, swept over B and delta
+    "sweep-14b": Workload("sweep-14b", Shape(9, 32, 5120, 40, 8, 128, 13824, 4096), 4, 0.1,
+                          branch_sweep=(2, 4, 6, 8),
+                          delta_sweep=(0.0, 0.01, 0.1, 0.2, 0.3, 0.5, 0.7)),
+}
+
+
+# ---------------------------------------------------------------- bfloat16 rounding
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round to bfloat16 (round to nearest, ties to even); return the uint16 bit patterns."""
+    x32 = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    u = x32.view(np.uint32).astype(np.uint64)
+    rounded = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    nan = np.isnan(x32)
+    if nan.any():
+        rounded = np.where(nan, np.uint16(0x7FC0), rounded)
+    return rounded
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """float32 array holding the bfloat16-rounded values of ``x``."""
+    return bf16_bits_to_f32(bf16_bits(x))
+
+
+# ---------------------------------------------------------------- draws
+
+def _rng(base_seed: int, step: int, layer: int, tensor_id: int) -> np.random.Generator:
+    return np.random.default_rng([base_seed, step, layer, tensor_id])
+
+
+def layer_weights(shape: Shape, base_seed: int, layer: int, random_norm: bool = False) -> dict:
+    """Random-init weights of one layer, float32, already rounded to bfloat16.
+
+    Linear weights are N(0, 0.02^2) in torch ``Linear.weight`` layout ([out][in]):
+    w_qkv [(Hq+2Hkv)d, D] (Q heads, then K heads, then V heads), w_o [D, Hq d],
+    w_gate_up [2F, D] (gate rows, then up rows), w_down [D, F].  RMSNorm weights are
+    ones unless ``random_norm`` (tests use 1 + 0.1 N(0,1) so a misplaced norm weight shows).
+    """
+    D, F = shape.hidden, shape.ffn
+    dq = shape.n_q_heads * shape.head_dim
+
+    def lin(tid, rows, cols):
+        w = _rng(base_seed, 0, layer, tid).standard_normal((rows, cols), dtype=np.float32)
+        w *= np.float32(0.02)
+        return bf16_round(w)
+
+    def norm(tid):
+        if not random_norm:
+            return np.ones(D, dtype=np.float32)
+        g = _rng(base_seed, 0, layer, tid).standard_normal(D, dtype=np.float32)
+        return bf16_round(1.0 + 0.1 * g)
+
+    return {
+        "ln1": norm(_T_LN1),
+        "w_qkv": lin(_T_WQKV, shape.qkv_out, D),
+        "w_o": lin(_T_WO, D, dq),
+        "ln2": norm(_T_LN2),
+        "w_gate_up": lin(_T_WGU, 2 * F, D),
+        "w_down": lin(_T_WDOWN, D, F),
+    }
+
+
+def prefix_kv(shape: Shape, base_seed: int, layer: int) -> tuple[np.ndarray, np.ndarray]:
+    """Shared prefix K and V caches [P, Hkv, d], N(0,1), bfloat16-rounded, taken as already
+    rotary-embedded (they were written by earlier passes)."""
+    sz = (shape.prefix_len, shape.n_kv_heads, shape.head_dim)
+    k = _rng(base_seed, 0, layer, _T_PK).standard_normal(sz, dtype=np.float32)
+    v = _rng(base_seed, 0, layer, _T_PV).standard_normal(sz, dtype=np.float32)
+    return bf16_round(k), bf16_round(v)
+
+
+def parent_tree(n_branch: int, base_seed: int, step: int, kind: str = "random",
+                max_depth: int = 4) -> np.ndarray:
+    """Parent map par[0..B]: par[0] = -1, 0 <= par[i] < i.
+
+    "random": draft i picks its parent uniformly among earlier branches whose depth is
+    below ``max_depth`` (so no branch is deeper than ``max_depth``).  "chain": par[i] = i-1.
+    "star": every draft hangs off main.
+    """
+    par = np.full(n_branch, -1, dtype=np.int32)
+    if kind == "chain":
+        par[1:] = np.arange(n_branch - 1, dtype=np.int32)
+        return par
+    if kind == "star":
+        par[1:] = 0
+        return par
+    rng = _rng(base_seed, step, 0, _T_TREE)
+    depth = np.zeros(n_branch, dtype=np.int64)
+    for i in range(1, n_branch):
+        cands = [j for j in range(i) if depth[j] < max_depth]
+        p = int(cands[rng.integers(len(cands))])
+        par[i] = p
+        depth[i] = depth[p] + 1
+    return par
+
+
+def main_hidden(shape: Shape, base_seed: int, step: int) -> np.ndarray:
+    """Main branch block hidden state [N, D], N(0,1), float64."""
+    return _rng(base_seed, step, 0, _T_MAIN).standard_normal((shape.block, shape.hidden))
+
+
+def child_hidden(parent_rows: np.ndarray, r: np.ndarray, unmasked: np.ndarray,
+                 rng: np.random.Generator) -> np.ndarray:
+    """Build a draft block from its parent block.
+
+    Newly unmasked positions get a fresh N(0,1) row.  Every other position is the
+    parent's row plus a random direction scaled to ``r[n]`` times the parent row's
+    Euclidean length, so the child's distance to its parent, relative to the parent's
+    length, is exactly ``r[n]`` in exact arithmetic.
+    """
+    n, dim = parent_rows.shape
+    g = rng.standard_normal((n, dim))
+    fresh = rng.standard_normal((n, dim))
+    plen = np.sqrt(np.sum(parent_rows * parent_rows, axis=1, keepdims=True))
+    glen = np.sqrt(np.sum(g * g, axis=1, keepdims=True))
+    out = parent_rows + (r[:, None] * plen) * (g / glen)
+    out[unmasked] = fresh[unmasked]
+    return out
+
+
+def step_inputs(shape: Shape, base_seed: int, step: int, tree: str = "random",
+                child_law: str = "lognormal", parent: np.ndarray | None = None) -> dict:
+    """Hidden states of all branches for one verification step.
+
+    Returns ``{"parent": int32[B+1], "H": float64[B+1, N, D], "r": float64[B+1, N],
+    "unmasked": bool[B+1, N]}``; ``r`` is the drawn relative distance of each draft row
+    (NaN for main and for unmasked rows).  Children are built in branch order from the
+    (already built) parent block.
+    """
+    B1, N = shape.n_branch, shape.block
+    if parent is None:
+        parent = parent_tree(B1, base_seed, step, tree)
+    parent = np.asarray(parent, dtype=np.int32)
+    rng = _rng(base_seed, step, 0, _T_CHILD)
+    H = np.empty((B1, N, shape.hidden))
+    H[0] = main_hidden(shape, base_seed, step)
+    r_all = np.full((B1, N), np.nan)
+    unm_all = np.zeros((B1, N), dtype=bool)
+    for i in range(1, B1):
+        if child_law == "tiny":
+            small = rng.random(N) < 0.7
+            r = np.where(small, rng.uniform(0.01, 0.08, N), rng.uniform(0.15, 1.0, N))
+            unmasked = np.zeros(N, dtype=bool)
+        else:
+            u = int(rng.integers(1, 5))
+            unmasked = np.zeros(N, dtype=bool)
+            unmasked[rng.choice(N, size=min(u, N), replace=False)] = True
+            r = rng.lognormal(LOGNORMAL_MU, LOGNORMAL_SIGMA, N)
+        H[i] = child_hidden(H[parent[i]], r, unmasked, rng)
+        r_all[i] = np.where(unmasked, np.nan, r)
+        unm_all[i] = unmasked
+    return {"parent": parent, "H": H, "r": r_all, "unmasked": unm_all}
+
+
+def expected_fold_fraction(delta: float, n_block: int = 32) -> float:
+    """Layer-0 folded fraction of draft rows implied by the log-normal law (unmasked
+    rows never fold for delta < sqrt(2))."""
+    if delta <= 0:
+        return 0.0
+    z = (math.log(delta) - LOGNORMAL_MU) / LOGNORMAL_SIGMA
+    phi = 0.5 * (1.0 + math.erf(z / math.sqrt(2.0)))
+    return (1.0 - 2.5 / n_block) * phi
