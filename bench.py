@@ -1,0 +1,275 @@
+"""Throughput of the folded multi-branch verification layer on one MI355X.
+
+One step = one pass of the whole hot path -- gate, compaction, fold-source resolution,
+sparse QKV, folded attention, output projection, sparse FFN and fold-inherit -- over one
+verification batch (main + B drafts), through ``specfold_verify_layer``.
+
+Workload (seeded, synthetic): one layer at 1.5B-class shape (hidden 1536, 12 q / 2 kv heads,
+head_dim 128, SwiGLU 8960), block 32, main + 8 drafts in a random tree of depth <= 4, prefix
+512 tokens, delta 0.1.  Timing replays a HIP graph of K steps bracketed by events; inputs are
+resident in HBM before the timed region.  Regime "cold" rotates through copies of the layer's
+weights totalling more than the 256 MB Infinity Cache, so every step streams its weights from
+HBM as a layer of a real stack does; "warm" reuses one copy.
+
+Prints one JSON line (see the README of the measurement in the design doc for every field).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "verified branch-tokens/s per layer stack at delta=0.1; speedup vs dense delta=0"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
+                    help="keep replaying (untimed) at least this long before timing, so clocks have ramped")
+    ap.add_argument("--workload", default="layer-1.5b")
+    ap.add_argument("--regime", choices=["cold", "warm"], default="cold")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--stage-calls", type=int, default=30, help="eager calls timed per launch with events")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration runs)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_layer_rho_amd import specfold as sf
+    from synth import WORKLOADS, bf16_round, layer_weights, prefix_kv, step_inputs
+
+    wl = WORKLOADS[args.workload]
+    sh = wl.shape
+    R, D, F = sh.rows, sh.hidden, sh.ffn
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev).to(torch.bfloat16)
+
+    t0 = time.time()
+    w_host = layer_weights(sh, wl.base_seed, 0)
+    pk_h, pv_h = prefix_kv(sh, wl.base_seed, 0)
+    inp = step_inputs(sh, wl.base_seed, 0, tree=wl.tree, child_law=wl.child_law)
+    parent = inp["parent"]
+    H_host = bf16_round(inp["H"].astype(np.float32))
+    w0 = {k: to_dev(v) for k, v in w_host.items()}
+    pk, pv = to_dev(pk_h), to_dev(pv_h)
+    H_in = to_dev(H_host.reshape(R, D))
+    print(f"[bench] inputs ready in {time.time() - t0:.1f}s: {args.workload}, R={R}, "
+          f"weights {sh.weight_bytes_bf16() / 1e6:.1f} MB/layer", file=sys.stderr, flush=True)
+
+    # weight copies: cold rotates through enough of them to overflow the 256 MB cache
+    n_copies = 1 if args.regime == "warm" else max(2, int(np.ceil(600e6 / sh.weight_bytes_bf16())))
+    copies = [w0] + [{k: v.clone() for k, v in w0.items()} for _ in range(n_copies - 1)]
+    lws = [sf.layer_weights_struct(c) for c in copies]
+    pf = sf.prefix_view(pk, pv)
+    ws = sf.new_workspace(sh)
+    H_out = torch.empty((R, D), dtype=torch.bfloat16, device=dev)
+    stats = {"fold": torch.zeros(R, dtype=torch.uint8, device=dev),
+             "rec_count": torch.zeros(1, dtype=torch.int32, device=dev)}
+
+    def step(delta, k):
+        sf.verify_layer(sh, parent, lws[k % n_copies], pf, None, H_in, delta, H_out, ws, stats=stats)
+
+    # ---------------------------------------------------------------- eager reference + counts
+    results = {}
+    for delta in (wl.delta, 0.0):
+        step(delta, 0)
+        torch.cuda.synchronize()
+        results[delta] = {"H_out": H_out.clone(), "fold": stats["fold"].cpu().numpy().copy(),
+                          "M": int(stats["rec_count"].item())}
+
+    # ---------------------------------------------------------------- graph-timed throughput
+    def timed(delta, steps, warmup):
+        # one captured graph runs a full rotation of the weight copies
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for k in range(n_copies):
+                step(delta, k)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for k in range(n_copies):
+                step(delta, k)
+        reps = max(1, steps // n_copies)
+        wreps = max(1, warmup // n_copies)
+        t_w = time.perf_counter()
+        done = 0
+        while done < wreps or time.perf_counter() - t_w < args.warmup_seconds:
+            g.replay()
+            done += 1
+            if done % 64 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        # every replay reproduces the eager result bit for bit
+        if not torch.equal(H_out.view(torch.int16), results[delta]["H_out"].view(torch.int16)):
+            raise RuntimeError("graph replay differs from the eager call")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        ms = e0.elapsed_time(e1)
+        n = reps * n_copies
+        if not torch.equal(H_out.view(torch.int16), results[delta]["H_out"].view(torch.int16)):
+            raise RuntimeError("graph replay differs from the eager call")
+        del g
+        return {"steps": n, "ms_per_step": ms / n, "wall_ms_per_step": 1e3 * wall / n,
+                "branch_tokens_per_s": R * n / (ms / 1e3)}
+
+    folded = timed(wl.delta, args.steps, args.warmup)
+    dense = timed(0.0, args.steps, args.warmup)
+    print(f"[bench] folded {folded['ms_per_step'] * 1e3:.1f} us/step, dense {dense['ms_per_step'] * 1e3:.1f} "
+          f"us/step", file=sys.stderr, flush=True)
+
+    # ---------------------------------------------------------------- per-launch durations (events)
+    def stage_times(delta):
+        tm = sf.StageTimer()
+        acc = None
+        for k in range(args.stage_calls):
+            sf.verify_layer(sh, parent, lws[k % n_copies], pf, None, H_in, delta, H_out, ws, stats=stats,
+                            trace=tm.trace)
+            torch.cuda.synchronize()
+            t = tm.elapsed_ms()
+            if k >= 3:
+                acc = t if acc is None else {n: acc[n] + t[n] for n in acc}
+        tm.close()
+        cnt = args.stage_calls - 3
+        return {n: 1e3 * v / cnt for n, v in acc.items()}     # microseconds
+
+    st_f = stage_times(wl.delta)
+    st_d = stage_times(0.0)
+
+    M = results[wl.delta]["M"]
+    fold = results[wl.delta]["fold"].reshape(sh.n_branch, sh.block)
+    fold_frac = float(fold[1:].mean()) if sh.n_branch > 1 else 0.0
+
+    # dominant kernel: the FFN gate/up projection (59 % of the layer's weight bytes)
+    gu_bytes = 2 * (2 * F * D) + 2 * M * D + 2 * M * F
+    gu_us = st_f["gate_up_swiglu_gemm"]
+    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
+    roofline = {"kernel": "gate_up_swiglu_gemm", "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None, "avg_us": round(gu_us, 2), "bytes_per_launch": gu_bytes,
+                "tflops": round(2 * M * 2 * F * D / (gu_us * 1e-6) / 1e12, 1)}
+
+    # whole-layer roofline at the vendor peaks: sum over kernels of max(bytes/BW, flops/MFMA)
+    def layer_roof_us(m):
+        Nq, Do = (sh.n_q_heads + 2 * sh.n_kv_heads) * sh.head_dim, sh.n_q_heads * sh.head_dim
+        t = 0.0
+        for flops, byts in ((2 * m * Nq * D, 2 * Nq * D), (2 * R * Do * D, 2 * Do * D),
+                            (2 * m * 2 * F * D, 2 * 2 * F * D), (2 * m * F * D, 2 * F * D),
+                            (4 * sh.head_dim * sh.n_q_heads * (sh.prefix_len * m + sh.block * R),
+                             4 * sh.prefix_len * sh.n_kv_heads * sh.head_dim)):
+            t += max(flops / (BF16_PEAK_TFLOPS * 1e12), byts / (HBM_PEAK_GBS * 1e9))
+        return t * 1e6
+
+    out = {
+        "metric": METRIC,
+        "value": round(folded["branch_tokens_per_s"], 1),
+        "unit": "branch-tokens/s",
+        "n_gpus": 1,
+        "steps": folded["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": round(folded["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random weights, prefix KV and parent-linked draft hidden states)",
+        "config": {"workload": args.workload, "hidden": D, "n_q_heads": sh.n_q_heads, "n_kv_heads": sh.n_kv_heads,
+                   "head_dim": sh.head_dim, "ffn": F, "block": sh.block, "drafts": sh.n_branch - 1,
+                   "prefix": sh.prefix_len, "delta": wl.delta, "rows": R, "regime": args.regime,
+                   "weight_copies": n_copies, "timing": "HIP graph replay, events", "parallelism": "single GPU"},
+        "speedup_vs_dense": round(dense["ms_per_step"] / folded["ms_per_step"], 4),
+        "dense": {"value": round(dense["branch_tokens_per_s"], 1), "ms_per_step": round(dense["ms_per_step"], 5),
+                  "rec_rows": results[0.0]["M"]},
+        "fold_fraction_drafts": round(fold_frac, 4),
+        "rec_rows": M,
+        "layer_roofline_frac": {"folded": round(layer_roof_us(M) / (folded["ms_per_step"] * 1e3), 4),
+                                "dense": round(layer_roof_us(R) / (dense["ms_per_step"] * 1e3), 4)},
+        "roofline": roofline,
+        "stages_us": {"folded": {k: round(v, 2) for k, v in st_f.items()},
+                      "dense": {k: round(v, 2) for k, v in st_d.items()}},
+        "wall_ms_per_step": round(folded["wall_ms_per_step"], 5),
+    }
+
+    if args.copy_probe_mb > 0:
+        n = args.copy_probe_mb * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).uniform_()
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        out["copy_probe_bytes"] = 4 * n
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"], out["verified"] = cpu_baseline_leg(
+            sh, wl, parent, H_host, w_host, pk_h, pv_h, results[wl.delta], args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_leg(sh, wl, parent, H_host, w_host, pk_h, pv_h, gpu_res, seconds):
+    """Time the CPU oracle on the bench's first input (bounded), and check the GPU's output of that
+    same step against it (teacher-forced on the GPU's mask within 1e-4 of delta)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+
+    H = H_host.astype(np.float64)
+    fold_g = gpu_res["fold"].reshape(sh.n_branch, sh.block).astype(bool)
+    rho_o, fold_o = oracle.gate(H, parent, wl.delta)
+    band = np.abs(rho_o - wl.delta) < 1e-4
+    ok_mask = bool(np.array_equal(fold_g[~band], fold_o[~band]))
+    ref = oracle.verify_layer(H, parent, w_host, pk_h, pv_h, wl.delta, sh, fold=fold_g)
+    got = gpu_res["H_out"].float().cpu().numpy().astype(np.float64).reshape(H.shape)
+    err = float(np.linalg.norm(got - ref["H_out"]) / np.linalg.norm(ref["H_out"]))
+    verified = ok_mask and err <= 2e-2 and gpu_res["M"] == ref["rec_rows"].size
+
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.verify_layer(H, parent, w_host, pk_h, pv_h, wl.delta, sh)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= 200:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    cpu = {"value": round(sh.rows * n / el, 1), "unit": "branch-tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{n} float64 oracle passes of the bench's first step ({sh.rows} rows) in {el:.1f}s",
+           "seconds": round(el, 2)}
+    return cpu, {"ok": bool(verified), "rel_l2": round(err, 6), "mask_match_outside_band": ok_mask}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,572 @@
+// C ABI of the folded verification layer: argument checks, workspace layout and the launch
+// sequence of each entry point.  Every check runs before the first launch, so a call that
+// returns an error has enqueued nothing.
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <cmath>
+
+#include "../../include/specfold.h"
+#include "kernels.h"
+
+using namespace specfold;
+
+namespace {
+
+static_assert(kMaxBranches == SPECFOLD_MAX_BRANCHES, "branch limit mismatch");
+
+constexpr int kMaxGateBlock = 1 << 20;   // positions per branch accepted by gate/compact/resolve
+
+struct Dims {
+    int nb, N, R, D, Hq, Hkv, hd, F, P, Nq, Do;
+    float eps, theta;
+};
+
+struct Layout {
+    int nt_qkv, nt_o, nt_gu, nt_down;
+    size_t rho, fold, inv_rms, rec_rows, rec_count, branch_off, row_slot, src_branch, src_slot;
+    size_t xn1, xn2, q_c, k_c, v_c, attn, h_mid, act, gemm_part, attn_o, attn_ml;
+    size_t total;
+    int s_qkv, s_o, s_down, chunk_len, n_chunks;
+};
+
+inline size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+Dims dims_of(const specfold_shape& s) {
+    Dims d;
+    d.nb = s.n_branch; d.N = s.block; d.R = s.n_branch * s.block; d.D = s.hidden;
+    d.Hq = s.n_q_heads; d.Hkv = s.n_kv_heads; d.hd = s.head_dim; d.F = s.ffn; d.P = s.prefix_len;
+    d.Nq = (s.n_q_heads + 2 * s.n_kv_heads) * s.head_dim; d.Do = s.n_q_heads * s.head_dim;
+    d.eps = s.rms_eps; d.theta = s.rope_theta;
+    return d;
+}
+
+// K-split count of a partial-sum projection: enough workgroups (>= ~256) to spread the weight
+// stream over the 256 CUs, while every split keeps at least 8 32-wide k-steps.
+int pick_splits(int nout, int k, int nt) {
+    const int groups = (nout + 16 * nt - 1) / (16 * nt);
+    const int nks = k / 32;
+    int s = (256 + groups - 1) / groups;
+    const int cap = nks / 8 > 1 ? nks / 8 : 1;
+    if (s > cap) s = cap;
+    if (s < 1) s = 1;
+    return s;
+}
+
+Layout layout_of(const Dims& d) {
+    Layout L;
+    L.nt_qkv = 4; L.nt_o = 4; L.nt_gu = 4; L.nt_down = 4;
+    L.s_qkv = pick_splits(d.Nq, d.D, L.nt_qkv);
+    L.s_o = pick_splits(d.D, d.Do, L.nt_o);
+    L.s_down = pick_splits(d.D, d.F, L.nt_down);
+    L.chunk_len = d.P <= 1024 ? 256 : 512;
+    L.n_chunks = d.P > 0 ? (d.P + L.chunk_len - 1) / L.chunk_len : 0;
+    const size_t R = static_cast<size_t>(d.R);
+    size_t off = 0;
+    auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+    L.rho = take(R * 4);
+    L.fold = take(R);
+    L.inv_rms = take(R * 4);
+    L.rec_rows = take(R * 4);
+    L.rec_count = take(4);
+    L.branch_off = take((static_cast<size_t>(d.nb) + 1) * 4);
+    L.row_slot = take(R * 4);
+    L.src_branch = take(R * 4);
+    L.src_slot = take(R * 4);
+    L.xn1 = take(R * d.D * 2);
+    L.xn2 = take(R * d.D * 2);
+    L.q_c = take(R * d.Hq * d.hd * 2);
+    L.k_c = take(R * d.Hkv * d.hd * 2);
+    L.v_c = take(R * d.Hkv * d.hd * 2);
+    L.attn = take(R * d.Do * 2);
+    L.h_mid = take(R * d.D * 2);
+    L.act = take(R * d.F * 2);
+    size_t part = static_cast<size_t>(L.s_qkv) * R * d.Nq;
+    const size_t po = static_cast<size_t>(L.s_o) * R * d.D;
+    const size_t pd = static_cast<size_t>(L.s_down) * R * d.D;
+    if (po > part) part = po;
+    if (pd > part) part = pd;
+    L.gemm_part = take(part * 4);
+    L.attn_o = take(static_cast<size_t>(L.n_chunks) * R * d.Hq * d.hd * 4);
+    L.attn_ml = take(static_cast<size_t>(L.n_chunks) * R * d.Hq * 2 * 4);
+    L.total = off;
+    return L;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int dev(const void* p) {
+    if (!p) return SPECFOLD_ERR_NULL;
+    return aligned16(p) ? SPECFOLD_OK : SPECFOLD_ERR_ALIGN;
+}
+
+int opt_dev(const void* p) { return p ? dev(p) : SPECFOLD_OK; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+// sizes every entry point relies on
+int check_rows_shape(const specfold_shape* s, int max_block) {
+    if (!s) return SPECFOLD_ERR_NULL;
+    if (s->n_branch < 1 || s->block < 1 || s->hidden < 1) return SPECFOLD_ERR_SHAPE;
+    if (s->n_branch > SPECFOLD_MAX_BRANCHES || s->block > max_block) return SPECFOLD_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(s->n_branch) * s->block > (1 << 24)) return SPECFOLD_ERR_UNSUPPORTED;
+    if (s->hidden % 64 != 0) return SPECFOLD_ERR_UNSUPPORTED;
+    if (!(s->rms_eps >= 0.f) || !std::isfinite(s->rms_eps)) return SPECFOLD_ERR_SHAPE;
+    return SPECFOLD_OK;
+}
+
+// full layer sizes (attention and projections)
+int check_layer_shape(const specfold_shape* s) {
+    int e = check_rows_shape(s, SPECFOLD_MAX_BLOCK);
+    if (e) return e;
+    if (s->n_q_heads < 1 || s->n_kv_heads < 1 || s->head_dim < 1 || s->ffn < 1 || s->prefix_len < 0)
+        return SPECFOLD_ERR_SHAPE;
+    if (s->n_q_heads % s->n_kv_heads != 0) return SPECFOLD_ERR_SHAPE;
+    if (!(s->rope_theta > 0.f) || !std::isfinite(s->rope_theta)) return SPECFOLD_ERR_SHAPE;
+    const int hd = s->head_dim;
+    if (hd != 16 && hd != 32 && hd != 64 && hd != 128) return SPECFOLD_ERR_UNSUPPORTED;
+    if (s->ffn % 64 != 0 || (s->n_q_heads * hd) % 64 != 0) return SPECFOLD_ERR_UNSUPPORTED;
+    if (((s->n_q_heads + 2 * s->n_kv_heads) * hd) % 32 != 0) return SPECFOLD_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(s->hidden) * s->ffn > (int64_t(1) << 31)) return SPECFOLD_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(s->prefix_len) > (int64_t(1) << 24)) return SPECFOLD_ERR_UNSUPPORTED;
+    return SPECFOLD_OK;
+}
+
+int check_tree(const int32_t* par, int nb, ParentMap& out) {
+    if (!par) return SPECFOLD_ERR_NULL;
+    if (par[0] != -1) return SPECFOLD_ERR_TREE;
+    out.p[0] = -1;
+    for (int i = 1; i < nb; ++i) {
+        if (par[i] < 0 || par[i] >= i) return SPECFOLD_ERR_TREE;
+        out.p[i] = par[i];
+    }
+    for (int i = nb; i < kMaxBranches; ++i) out.p[i] = -1;
+    return SPECFOLD_OK;
+}
+
+int check_ws(const void* ws, size_t ws_bytes, const Layout& L) {
+    if (!ws) return SPECFOLD_ERR_WORKSPACE;
+    if (!aligned16(ws)) return SPECFOLD_ERR_ALIGN;
+    if (ws_bytes < L.total) return SPECFOLD_ERR_WORKSPACE;
+    return SPECFOLD_OK;
+}
+
+int check_prefix(const specfold_prefix_kv* pf, const Dims& d) {
+    if (d.P == 0) return SPECFOLD_OK;
+    if (!pf) return SPECFOLD_ERR_NULL;
+    int e;
+    if ((e = dev(pf->k)) || (e = dev(pf->v))) return e;
+    const int64_t st[4] = {pf->k_stride_tok, pf->k_stride_head, pf->v_stride_tok, pf->v_stride_head};
+    for (int64_t x : st) {
+        if (x < 0) return SPECFOLD_ERR_SHAPE;
+        if (x % 8 != 0) return SPECFOLD_ERR_ALIGN;
+    }
+    if (d.P > 1 && (pf->k_stride_tok == 0 || pf->v_stride_tok == 0)) return SPECFOLD_ERR_SHAPE;
+    return SPECFOLD_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off); }
+
+thread_local char g_last_error[256] = "";
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return SPECFOLD_OK;
+    snprintf(g_last_error, sizeof g_last_error, "%s (%d): %s", hipGetErrorName(e), static_cast<int>(e),
+             hipGetErrorString(e));
+    return SPECFOLD_ERR_HIP;
+}
+
+struct Tracer {
+    const specfold_trace* t;
+    hipStream_t st;
+    int k = 0;
+    void begin() {
+        if (t && t->events && 2 * k + 1 < t->n_events && t->events[2 * k])
+            (void)hipEventRecord(static_cast<hipEvent_t>(t->events[2 * k]), st);
+    }
+    void end() {
+        if (t && t->events && 2 * k + 1 < t->n_events && t->events[2 * k + 1])
+            (void)hipEventRecord(static_cast<hipEvent_t>(t->events[2 * k + 1]), st);
+        ++k;
+    }
+};
+
+const char* const kStageNames[] = {
+    "gate_rmsnorm", "qkv_gemm_compact_resolve", "qkv_rope_epilogue", "attn_prefix", "attn_block_merge",
+    "oproj_gemm", "oproj_residual_rmsnorm", "gate_up_swiglu_gemm", "down_gemm", "down_inherit_epilogue",
+};
+constexpr int kStages = sizeof(kStageNames) / sizeof(kStageNames[0]);
+
+// ---------------------------------------------------------------- launch sequences (no checks)
+
+// QKV projection of the recompute rows of xn (RMSNorm'd rows): rows come from a device list
+// (rec_rows/rec_count) or, when fc is given, from the fold flags compacted in the GEMM itself.
+hipError_t run_qkv(const Dims& d, const Layout& L, const uint16_t* xn, const int32_t* rec_rows,
+                   const int32_t* rec_count, const uint16_t* w_qkv, uint16_t* q_c, uint16_t* k_c, uint16_t* v_c,
+                   void* ws, hipStream_t st, Tracer* tr, const GemmArgs* fc) {
+    GemmArgs g = fc ? *fc : GemmArgs{};
+    g.A = xn; g.lda = d.D; g.a_rows = rec_rows; g.a_row_limit = d.R; g.m_count = rec_count;
+    g.m_cap = d.R; g.W = w_qkv; g.K = d.D; g.Nout = d.Nq;
+    g.partial = at<float>(ws, L.gemm_part);
+    if (tr) tr->begin();
+    hipError_t e = launch_gemm_partial(g, L.s_qkv, d.R, L.nt_qkv, st);
+    if (tr) tr->end();
+    if (e != hipSuccess) return e;
+    QkvEpiArgs q{};
+    q.part = g.partial; q.splits = L.s_qkv; q.m_cap = d.R; q.m_count = rec_count; q.rec_rows = rec_rows;
+    q.R = d.R; q.N = d.N; q.Hq = d.Hq; q.Hkv = d.Hkv; q.hd = d.hd; q.P = d.P;
+    for (int j = 0; j < d.hd / 2; ++j)
+        q.inv_freq[j] = std::pow(static_cast<double>(d.theta), -2.0 * j / static_cast<double>(d.hd));
+    q.q_c = q_c; q.k_c = k_c; q.v_c = v_c;
+    if (tr) tr->begin();
+    e = launch_qkv_epilogue(q, st);
+    if (tr) tr->end();
+    return e;
+}
+
+hipError_t run_attention(const Dims& d, const Layout& L, const uint16_t* q_c, const uint16_t* k_c,
+                         const uint16_t* v_c, const int32_t* rec_count, const int32_t* src_slot,
+                         const specfold_prefix_kv* pf, uint16_t* attn, float* lse, void* ws,
+                         hipStream_t st, Tracer* tr) {
+    AttnArgs a{};
+    a.q_c = q_c; a.k_c = k_c; a.v_c = v_c; a.m_count = rec_count; a.m_cap = d.R; a.src_slot = src_slot;
+    a.nb = d.nb; a.N = d.N; a.Hq = d.Hq; a.Hkv = d.Hkv; a.hd = d.hd; a.P = d.P;
+    if (d.P > 0) {
+        a.pk = pf->k; a.pv = pf->v;
+        a.pk_st = pf->k_stride_tok; a.pk_sh = pf->k_stride_head;
+        a.pv_st = pf->v_stride_tok; a.pv_sh = pf->v_stride_head;
+    }
+    a.chunk_len = L.chunk_len; a.n_chunks = L.n_chunks;
+    a.part_o = at<float>(ws, L.attn_o); a.part_ml = at<float>(ws, L.attn_ml);
+    a.attn = attn; a.lse = lse;
+    a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d.hd)));
+    if (tr) tr->begin();
+    hipError_t e = launch_attn_prefix(a, st);
+    if (tr) tr->end();
+    if (e != hipSuccess) return e;
+    if (tr) tr->begin();
+    e = launch_attn_block(a, st);
+    if (tr) tr->end();
+    return e;
+}
+
+hipError_t run_out_proj(const Dims& d, const Layout& L, const uint16_t* attn, const uint16_t* H,
+                        const uint16_t* w_o, uint16_t* h_mid, const uint16_t* ln2, uint16_t* xn2, void* ws,
+                        hipStream_t st, Tracer* tr) {
+    GemmArgs g{};
+    g.A = attn; g.lda = d.Do; g.a_rows = nullptr; g.a_row_limit = d.R; g.m_count = nullptr;
+    g.m_fixed = d.R; g.m_cap = d.R; g.W = w_o; g.K = d.Do; g.Nout = d.D;
+    g.partial = at<float>(ws, L.gemm_part);
+    if (tr) tr->begin();
+    hipError_t e = launch_gemm_partial(g, L.s_o, d.R, L.nt_o, st);
+    if (tr) tr->end();
+    if (e != hipSuccess) return e;
+    if (tr) tr->begin();
+    e = launch_oproj_epilogue(g.partial, L.s_o, d.R, d.D, H, h_mid, ln2, d.eps, xn2, st);
+    if (tr) tr->end();
+    return e;
+}
+
+// FFN of the recompute rows of xn2 (RMSNorm'd h_mid) + fold-inherit + residual.
+hipError_t run_ffn(const Dims& d, const Layout& L, const uint16_t* xn2, const uint16_t* h_mid,
+                   const int32_t* rec_rows, const int32_t* rec_count, const int32_t* src_slot,
+                   const uint16_t* w_gate_up, const uint16_t* w_down, uint16_t* H_out, void* ws, hipStream_t st,
+                   Tracer* tr) {
+    GemmArgs g{};
+    g.A = xn2; g.lda = d.D; g.a_rows = rec_rows; g.a_row_limit = d.R; g.m_count = rec_count;
+    g.m_cap = d.R; g.W = w_gate_up; g.K = d.D; g.Nout = 2 * d.F;
+    g.act = at<uint16_t>(ws, L.act); g.F = d.F;
+    if (tr) tr->begin();
+    hipError_t e = launch_gemm_swiglu(g, d.R, L.nt_gu, st);
+    if (tr) tr->end();
+    if (e != hipSuccess) return e;
+    GemmArgs h{};
+    h.A = g.act; h.lda = d.F; h.a_rows = nullptr; h.a_row_limit = d.R; h.m_count = rec_count;
+    h.m_cap = d.R; h.W = w_down; h.K = d.F; h.Nout = d.D;
+    h.partial = at<float>(ws, L.gemm_part);
+    if (tr) tr->begin();
+    e = launch_gemm_partial(h, L.s_down, d.R, L.nt_down, st);
+    if (tr) tr->end();
+    if (e != hipSuccess) return e;
+    if (tr) tr->begin();
+    e = launch_down_epilogue(h.partial, L.s_down, d.R, rec_count, rec_rows, src_slot, d.nb, d.N, d.D, h_mid,
+                             H_out, st);
+    if (tr) tr->end();
+    return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+int specfold_version(void) { return SPECFOLD_VERSION; }
+
+const char* specfold_last_error(void) { return g_last_error; }
+
+const char* specfold_status_str(int status) {
+    switch (status) {
+        case SPECFOLD_OK: return "ok";
+        case SPECFOLD_ERR_NULL: return "required pointer is NULL";
+        case SPECFOLD_ERR_SHAPE: return "sizes out of range or inconsistent";
+        case SPECFOLD_ERR_TREE: return "invalid parent map (need par[0] = -1 and 0 <= par[i] < i)";
+        case SPECFOLD_ERR_ALIGN: return "device pointer or stride not 16-byte aligned";
+        case SPECFOLD_ERR_WORKSPACE: return "workspace missing or too small";
+        case SPECFOLD_ERR_UNSUPPORTED: return "shape outside the implemented kernels";
+        case SPECFOLD_ERR_ALIAS: return "output overlaps an input";
+        case SPECFOLD_ERR_HIP: return "HIP runtime rejected a launch";
+        default: return "unknown status";
+    }
+}
+
+size_t specfold_workspace_bytes(const specfold_shape* shape) {
+    if (check_layer_shape(shape) != SPECFOLD_OK) return 0;
+    return layout_of(dims_of(*shape)).total;
+}
+
+int specfold_stage_count(void) { return kStages; }
+
+const char* specfold_stage_name(int stage) {
+    return (stage >= 0 && stage < kStages) ? kStageNames[stage] : nullptr;
+}
+
+int specfold_event_create(void** event) {
+    if (!event) return SPECFOLD_ERR_NULL;
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return SPECFOLD_ERR_HIP;
+    *event = e;
+    return SPECFOLD_OK;
+}
+
+int specfold_event_destroy(void* event) {
+    if (!event) return SPECFOLD_ERR_NULL;
+    return hip_status(hipEventDestroy(static_cast<hipEvent_t>(event)));
+}
+
+int specfold_event_elapsed_ms(void* start, void* stop, float* ms) {
+    if (!start || !stop || !ms) return SPECFOLD_ERR_NULL;
+    return hip_status(hipEventElapsedTime(ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop)));
+}
+
+int specfold_gate(const specfold_shape* shape, const int32_t* parent_host, const specfold_bf16* H,
+                  float delta, const float* rho_in, float* rho, uint8_t* fold, float* inv_rms,
+                  void* stream) {
+    int e = check_rows_shape(shape, kMaxGateBlock);
+    if (e) return e;
+    ParentMap par;
+    if ((e = check_tree(parent_host, shape->n_branch, par))) return e;
+    const bool need_h = (rho_in == nullptr) || (inv_rms != nullptr);
+    if (need_h && (e = dev(H))) return e;
+    if ((e = opt_dev(rho_in)) || (e = dev(rho)) || (e = dev(fold)) || (e = opt_dev(inv_rms))) return e;
+    const size_t R = static_cast<size_t>(shape->n_branch) * shape->block;
+    if (overlaps(rho, R * 4, fold, R) || (inv_rms && (overlaps(inv_rms, R * 4, rho, R * 4) ||
+                                                      overlaps(inv_rms, R * 4, fold, R))))
+        return SPECFOLD_ERR_ALIAS;
+    if (need_h && (overlaps(H, R * shape->hidden * 2, rho, R * 4) || overlaps(H, R * shape->hidden * 2, fold, R)))
+        return SPECFOLD_ERR_ALIAS;
+    GateParams p{};
+    p.H = H; p.par = par; p.nb = shape->n_branch; p.N = shape->block; p.D = shape->hidden;
+    p.delta = delta; p.rho_in = rho_in; p.rho = rho; p.fold = fold; p.inv_rms = inv_rms;
+    p.eps = shape->rms_eps; p.ln = nullptr; p.xn = nullptr; p.fold_copy = nullptr;
+    return hip_status(launch_gate(p, static_cast<hipStream_t>(stream)));
+}
+
+int specfold_compact(const specfold_shape* shape, const uint8_t* fold, int32_t* rec_rows,
+                     int32_t* rec_count, int32_t* branch_off, int32_t* row_slot, void* stream) {
+    int e = check_rows_shape(shape, kMaxGateBlock);
+    if (e) return e;
+    if ((e = dev(fold)) || (e = dev(rec_rows)) || (e = dev(rec_count)) || (e = dev(branch_off)) ||
+        (e = dev(row_slot)))
+        return e;
+    const size_t R = static_cast<size_t>(shape->n_branch) * shape->block;
+    const size_t nbo = (static_cast<size_t>(shape->n_branch) + 1) * 4;
+    if (overlaps(rec_rows, R * 4, row_slot, R * 4) || overlaps(rec_rows, R * 4, branch_off, nbo) ||
+        overlaps(row_slot, R * 4, branch_off, nbo) || overlaps(rec_count, 4, rec_rows, R * 4) ||
+        overlaps(rec_count, 4, row_slot, R * 4) || overlaps(rec_count, 4, branch_off, nbo) ||
+        overlaps(fold, R, rec_rows, R * 4) || overlaps(fold, R, row_slot, R * 4))
+        return SPECFOLD_ERR_ALIAS;
+    CompactParams p{};
+    p.fold = fold; p.R = static_cast<int>(R); p.N = shape->block; p.nb = shape->n_branch;
+    p.rec_rows = rec_rows; p.rec_count = rec_count; p.branch_off = branch_off; p.row_slot = row_slot;
+    return hip_status(launch_compact(p, static_cast<hipStream_t>(stream)));
+}
+
+int specfold_resolve_sources(const specfold_shape* shape, const int32_t* parent_host,
+                             const uint8_t* fold, const int32_t* row_slot, int32_t* src_branch,
+                             int32_t* src_slot, void* stream) {
+    int e = check_rows_shape(shape, kMaxGateBlock);
+    if (e) return e;
+    ParentMap par;
+    if ((e = check_tree(parent_host, shape->n_branch, par))) return e;
+    if ((e = dev(fold)) || (e = dev(row_slot)) || (e = dev(src_branch)) || (e = dev(src_slot))) return e;
+    const size_t R = static_cast<size_t>(shape->n_branch) * shape->block;
+    if (overlaps(src_branch, R * 4, src_slot, R * 4) || overlaps(src_branch, R * 4, row_slot, R * 4) ||
+        overlaps(src_slot, R * 4, row_slot, R * 4) || overlaps(src_branch, R * 4, fold, R) ||
+        overlaps(src_slot, R * 4, fold, R))
+        return SPECFOLD_ERR_ALIAS;
+    ResolveParams p{};
+    p.fold = fold; p.par = par; p.nb = shape->n_branch; p.N = shape->block; p.R = static_cast<int>(R);
+    p.row_slot = row_slot; p.src_branch = src_branch; p.src_slot = src_slot;
+    return hip_status(launch_resolve(p, static_cast<hipStream_t>(stream)));
+}
+
+int specfold_sparse_qkv(const specfold_shape* shape, const specfold_bf16* H, const float* inv_rms,
+                        const int32_t* rec_rows, const int32_t* rec_count, const specfold_bf16* ln1,
+                        const specfold_bf16* w_qkv, specfold_bf16* q_c, specfold_bf16* k_c,
+                        specfold_bf16* v_c, void* ws, size_t ws_bytes, void* stream) {
+    int e = check_layer_shape(shape);
+    if (e) return e;
+    const Dims d = dims_of(*shape);
+    const Layout L = layout_of(d);
+    if ((e = dev(H)) || (e = dev(inv_rms)) || (e = dev(rec_rows)) || (e = dev(rec_count)) || (e = dev(ln1)) ||
+        (e = dev(w_qkv)) || (e = dev(q_c)) || (e = dev(k_c)) || (e = dev(v_c)))
+        return e;
+    if ((e = check_ws(ws, ws_bytes, L))) return e;
+    const size_t R = d.R, nq = R * d.Hq * d.hd * 2, nk = R * d.Hkv * d.hd * 2;
+    if (overlaps(q_c, nq, k_c, nk) || overlaps(q_c, nq, v_c, nk) || overlaps(k_c, nk, v_c, nk) ||
+        overlaps(q_c, nq, H, R * d.D * 2) || overlaps(k_c, nk, H, R * d.D * 2) || overlaps(v_c, nk, H, R * d.D * 2) ||
+        overlaps(ws, ws_bytes, q_c, nq) || overlaps(ws, ws_bytes, k_c, nk) || overlaps(ws, ws_bytes, v_c, nk))
+        return SPECFOLD_ERR_ALIAS;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint16_t* xn = at<uint16_t>(ws, L.xn1);
+    hipError_t he = launch_row_norm(H, d.R, d.D, inv_rms, d.eps, ln1, xn, st);
+    if (he != hipSuccess) return hip_status(he);
+    return hip_status(run_qkv(d, L, xn, rec_rows, rec_count, w_qkv, q_c, k_c, v_c, ws, st, nullptr, nullptr));
+}
+
+int specfold_folded_attention(const specfold_shape* shape, const specfold_bf16* q_c,
+                              const specfold_bf16* k_c, const specfold_bf16* v_c,
+                              const int32_t* rec_rows, const int32_t* rec_count, const int32_t* src_slot,
+                              const specfold_prefix_kv* prefix, specfold_bf16* attn, float* lse,
+                              void* ws, size_t ws_bytes, void* stream) {
+    int e = check_layer_shape(shape);
+    if (e) return e;
+    const Dims d = dims_of(*shape);
+    const Layout L = layout_of(d);
+    (void)rec_rows;
+    if ((e = dev(q_c)) || (e = dev(k_c)) || (e = dev(v_c)) || (e = dev(rec_count)) || (e = dev(src_slot)) ||
+        (e = dev(attn)) || (e = opt_dev(lse)))
+        return e;
+    if ((e = check_prefix(prefix, d))) return e;
+    if ((e = check_ws(ws, ws_bytes, L))) return e;
+    const size_t R = d.R, na = R * d.Do * 2;
+    if (overlaps(attn, na, q_c, R * d.Hq * d.hd * 2) || overlaps(attn, na, k_c, R * d.Hkv * d.hd * 2) ||
+        overlaps(attn, na, v_c, R * d.Hkv * d.hd * 2) || overlaps(attn, na, ws, ws_bytes) ||
+        (lse && (overlaps(lse, R * d.Hq * 4, attn, na) || overlaps(lse, R * d.Hq * 4, ws, ws_bytes))))
+        return SPECFOLD_ERR_ALIAS;
+    return hip_status(run_attention(d, L, q_c, k_c, v_c, rec_count, src_slot, prefix, attn, lse, ws,
+                                    static_cast<hipStream_t>(stream), nullptr));
+}
+
+int specfold_out_proj(const specfold_shape* shape, const specfold_bf16* attn, const specfold_bf16* H,
+                      const specfold_bf16* w_o, specfold_bf16* h_mid, void* ws, size_t ws_bytes,
+                      void* stream) {
+    int e = check_layer_shape(shape);
+    if (e) return e;
+    const Dims d = dims_of(*shape);
+    const Layout L = layout_of(d);
+    if ((e = dev(attn)) || (e = dev(H)) || (e = dev(w_o)) || (e = dev(h_mid))) return e;
+    if ((e = check_ws(ws, ws_bytes, L))) return e;
+    const size_t nh = static_cast<size_t>(d.R) * d.D * 2;
+    if (overlaps(h_mid, nh, H, nh) || overlaps(h_mid, nh, attn, static_cast<size_t>(d.R) * d.Do * 2) ||
+        overlaps(h_mid, nh, ws, ws_bytes))
+        return SPECFOLD_ERR_ALIAS;
+    return hip_status(run_out_proj(d, L, attn, H, w_o, h_mid, nullptr, nullptr, ws, static_cast<hipStream_t>(stream),
+                                   nullptr));
+}
+
+int specfold_sparse_ffn(const specfold_shape* shape, const specfold_bf16* h_mid, const int32_t* rec_rows,
+                        const int32_t* rec_count, const int32_t* src_slot, const specfold_bf16* ln2,
+                        const specfold_bf16* w_gate_up, const specfold_bf16* w_down, specfold_bf16* H_out,
+                        void* ws, size_t ws_bytes, void* stream) {
+    int e = check_layer_shape(shape);
+    if (e) return e;
+    const Dims d = dims_of(*shape);
+    const Layout L = layout_of(d);
+    if ((e = dev(h_mid)) || (e = dev(rec_rows)) || (e = dev(rec_count)) || (e = dev(src_slot)) || (e = dev(ln2)) ||
+        (e = dev(w_gate_up)) || (e = dev(w_down)) || (e = dev(H_out)))
+        return e;
+    if ((e = check_ws(ws, ws_bytes, L))) return e;
+    const size_t nh = static_cast<size_t>(d.R) * d.D * 2;
+    if (overlaps(H_out, nh, h_mid, nh) || overlaps(H_out, nh, ws, ws_bytes) || overlaps(h_mid, nh, ws, ws_bytes))
+        return SPECFOLD_ERR_ALIAS;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint16_t* xn = at<uint16_t>(ws, L.xn2);
+    hipError_t he = launch_row_norm(h_mid, d.R, d.D, nullptr, d.eps, ln2, xn, st);
+    if (he != hipSuccess) return hip_status(he);
+    return hip_status(run_ffn(d, L, xn, h_mid, rec_rows, rec_count, src_slot, w_gate_up, w_down, H_out, ws, st,
+                              nullptr));
+}
+
+int specfold_verify_layer(const specfold_shape* shape, const int32_t* parent_host,
+                          const specfold_layer_weights* w, const specfold_prefix_kv* prefix,
+                          const specfold_bf16* H_in, float delta, specfold_bf16* H_out,
+                          specfold_layer_stats* stats, const specfold_trace* trace, void* ws,
+                          size_t ws_bytes, void* stream) {
+    int e = check_layer_shape(shape);
+    if (e) return e;
+    const Dims d = dims_of(*shape);
+    const Layout L = layout_of(d);
+    ParentMap par;
+    if ((e = check_tree(parent_host, d.nb, par))) return e;
+    if (!w) return SPECFOLD_ERR_NULL;
+    if ((e = dev(w->ln1)) || (e = dev(w->w_qkv)) || (e = dev(w->w_o)) || (e = dev(w->ln2)) ||
+        (e = dev(w->w_gate_up)) || (e = dev(w->w_down)) || (e = dev(H_in)) || (e = dev(H_out)))
+        return e;
+    if (stats && ((e = opt_dev(stats->rho)) || (e = opt_dev(stats->fold)) || (e = opt_dev(stats->rec_count)) ||
+                  (e = opt_dev(stats->src_slot))))
+        return e;
+    if ((e = check_prefix(prefix, d))) return e;
+    if ((e = check_ws(ws, ws_bytes, L))) return e;
+    const size_t nh = static_cast<size_t>(d.R) * d.D * 2;
+    if (overlaps(H_out, nh, H_in, nh) || overlaps(H_out, nh, ws, ws_bytes) || overlaps(H_in, nh, ws, ws_bytes))
+        return SPECFOLD_ERR_ALIAS;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    Tracer tr{trace, st};
+
+    GateParams g{};
+    g.H = H_in; g.par = par; g.nb = d.nb; g.N = d.N; g.D = d.D; g.delta = delta; g.rho_in = nullptr;
+    g.rho = (stats && stats->rho) ? stats->rho : at<float>(ws, L.rho);
+    g.fold = at<uint8_t>(ws, L.fold); g.inv_rms = at<float>(ws, L.inv_rms); g.eps = d.eps;
+    g.ln = w->ln1; g.xn = at<uint16_t>(ws, L.xn1); g.fold_copy = stats ? stats->fold : nullptr;
+    tr.begin();
+    hipError_t he = launch_gate(g, st);
+    tr.end();
+    if (he != hipSuccess) return hip_status(he);
+
+    // the QKV GEMM compacts the fold flags itself and publishes the recompute list and sources
+    int32_t* rec_rows = at<int32_t>(ws, L.rec_rows);
+    int32_t* rec_count = at<int32_t>(ws, L.rec_count);
+    int32_t* src_slot = at<int32_t>(ws, L.src_slot);
+    GemmArgs fc{};
+    fc.fc_fold = g.fold; fc.fc_R = d.R; fc.fc_N = d.N; fc.fc_nb = d.nb; fc.fc_par = par;
+    fc.fc_rec_rows = rec_rows; fc.fc_rec_count = rec_count; fc.fc_branch_off = at<int32_t>(ws, L.branch_off);
+    fc.fc_row_slot = at<int32_t>(ws, L.row_slot); fc.fc_src_branch = at<int32_t>(ws, L.src_branch);
+    fc.fc_src_slot = src_slot;
+    fc.fc_count_copy = stats ? stats->rec_count : nullptr;
+    fc.fc_src_slot_copy = stats ? stats->src_slot : nullptr;
+
+    uint16_t* q_c = at<uint16_t>(ws, L.q_c);
+    uint16_t* k_c = at<uint16_t>(ws, L.k_c);
+    uint16_t* v_c = at<uint16_t>(ws, L.v_c);
+    uint16_t* attn = at<uint16_t>(ws, L.attn);
+    uint16_t* h_mid = at<uint16_t>(ws, L.h_mid);
+    uint16_t* xn2 = at<uint16_t>(ws, L.xn2);
+    if ((he = run_qkv(d, L, g.xn, rec_rows, rec_count, w->w_qkv, q_c, k_c, v_c, ws, st, &tr, &fc)) != hipSuccess)
+        return hip_status(he);
+    if ((he = run_attention(d, L, q_c, k_c, v_c, rec_count, src_slot, prefix, attn, nullptr, ws, st, &tr)) !=
+        hipSuccess)
+        return hip_status(he);
+    if ((he = run_out_proj(d, L, attn, H_in, w->w_o, h_mid, w->ln2, xn2, ws, st, &tr)) != hipSuccess)
+        return hip_status(he);
+    if ((he = run_ffn(d, L, xn2, h_mid, rec_rows, rec_count, src_slot, w->w_gate_up, w->w_down, H_out, ws, st,
+                      &tr)) != hipSuccess)
+        return hip_status(he);
+    return SPECFOLD_OK;
+}
+
+}  // extern "C"

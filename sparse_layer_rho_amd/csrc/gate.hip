@@ -1,0 +1,240 @@
+// Gate, compaction, fold-source resolution and row RMSNorm.
+//
+// Gate [SpecFold review, "무엇과 다른가"]: per draft row (i, n) with parent p = par(i),
+// rho = |H_i[n] - H_p[n]| / |H_p[n]| and the row folds when rho <= delta; main rows bypass
+// the gate [SpecFold summary, App. B].  One 64-lane wave owns one row: the lanes stream the
+// child and parent rows in 16-byte chunks (coalesced), accumulate in fp32 and reduce with
+// cross-lane shuffles.  The same loads give the row's sum of squares, i.e. its RMSNorm scale,
+// and -- when asked -- the normalised row the QKV projection consumes (RMSNorm weight applied,
+// rounded to bf16), so the layer input is read from HBM once.
+//
+// Compaction [SpecFold summary, App. B]: an exclusive scan of the recompute flags in row order
+// (wave ballots + a cross-wave scan in LDS) writes the global list, the per-branch offsets and
+// the inverse map row -> slot.
+//
+// Sources [SpecFold summary, App. B and §A.3]: every row walks its fold chain up the parent map
+// (at most n_branch steps; branch 0 always terminates) -- rows are independent, so one
+// order-free launch covers all branches.
+#include "kernels.h"
+
+namespace specfold {
+
+namespace {
+
+constexpr int kRowCache = 10;   // 16-byte chunks per lane kept in registers (D <= 5120)
+
+__device__ __forceinline__ float rho_of(float a, float b) {
+    if (b > 0.f) return sqrtf(a) / sqrtf(b);
+    if (a > 0.f) return __builtin_inff();
+    if (a == 0.f) return 0.f;
+    return __builtin_nanf("");
+}
+
+// xn chunk = bf16(x * s * ln) for the 8 elements of chunk k of a row
+__device__ __forceinline__ uint4 norm_chunk(const float* x, float s, const uint16_t* ln, int k) {
+    float y[8];
+    if (ln) {
+        float w[8];
+        unpack8(*reinterpret_cast<const uint4*>(ln + 8 * k), w);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = x[e] * s * w[e];
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = x[e] * s;
+    }
+    return pack8(y);
+}
+
+// one wave computes rho, fold, inv_rms (and optionally the normalised row) of one row
+__device__ __forceinline__ void gate_row(const GateParams& p, int row, int lane) {
+    const int i = row / p.N, n = row - i * p.N;
+    const bool need_pair = (i > 0) && (p.rho_in == nullptr);
+    const bool need_rows = need_pair || (p.inv_rms != nullptr) || (p.xn != nullptr);
+    const int nch = p.D >> 3;
+    float a = 0.f, b = 0.f, ss = 0.f;
+    uint4 cache[kRowCache];
+    const uint4* c = reinterpret_cast<const uint4*>(p.H + static_cast<size_t>(row) * p.D);
+    if (need_rows) {
+        const uint4* q = need_pair
+            ? reinterpret_cast<const uint4*>(p.H + (static_cast<size_t>(p.par.p[i]) * p.N + n) * p.D)
+            : nullptr;
+#pragma unroll
+        for (int t = 0; t < kRowCache; ++t) {
+            const int k = lane + t * kWave;
+            if (k < nch) {
+                cache[t] = c[k];
+                float x[8];
+                unpack8(cache[t], x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+                if (need_pair) {
+                    float yv[8];
+                    unpack8(q[k], yv);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float d = x[e] - yv[e];
+                        a += d * d;
+                        b += yv[e] * yv[e];
+                    }
+                }
+            }
+        }
+        for (int k = lane + kRowCache * kWave; k < nch; k += kWave) {
+            float x[8];
+            unpack8(c[k], x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+            if (need_pair) {
+                float yv[8];
+                unpack8(q[k], yv);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float d = x[e] - yv[e];
+                    a += d * d;
+                    b += yv[e] * yv[e];
+                }
+            }
+        }
+        a = wave_sum(a);
+        b = wave_sum(b);
+        ss = wave_sum(ss);
+    }
+    const float inv = 1.0f / sqrtf(ss / static_cast<float>(p.D) + p.eps);
+    if (lane == 0) {
+        float r = 0.f;
+        bool f = false;
+        if (i > 0) {
+            r = p.rho_in ? p.rho_in[row] : rho_of(a, b);
+            f = r <= p.delta;                      // NaN compares false: recompute
+        }
+        p.rho[row] = r;
+        p.fold[row] = f ? 1 : 0;
+        if (p.fold_copy) p.fold_copy[row] = f ? 1 : 0;
+        if (p.inv_rms) p.inv_rms[row] = inv;
+    }
+    if (p.xn) {
+        uint4* o = reinterpret_cast<uint4*>(p.xn + static_cast<size_t>(row) * p.D);
+#pragma unroll
+        for (int t = 0; t < kRowCache; ++t) {
+            const int k = lane + t * kWave;
+            if (k < nch) {
+                float x[8];
+                unpack8(cache[t], x);
+                o[k] = norm_chunk(x, inv, p.ln, k);
+            }
+        }
+        for (int k = lane + kRowCache * kWave; k < nch; k += kWave) {
+            float x[8];
+            unpack8(c[k], x);
+            o[k] = norm_chunk(x, inv, p.ln, k);
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void gate_kernel(const GateParams p) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row < p.nb * p.N) gate_row(p, row, threadIdx.x & (kWave - 1));
+}
+
+// block-wide exclusive scan of recompute flags, blockDim.x threads, rows in ascending order
+__global__ __launch_bounds__(1024) void compact_kernel(const CompactParams p) {
+    __shared__ int s_wave_tot[16];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    const int nw = blockDim.x >> 6;
+    int base = 0;
+    for (int r0 = 0; r0 < p.R; r0 += blockDim.x) {
+        const int r = r0 + tid;
+        const bool rec = (r < p.R) && (p.fold[r] == 0);
+        const uint64_t m = __ballot(rec);
+        const int excl = __popcll(m & ((1ull << lane) - 1ull));
+        if (lane == 0) s_wave_tot[wave] = __popcll(m);
+        __syncthreads();
+        int woff = 0, tot = 0;
+        for (int w = 0; w < nw; ++w) {
+            const int t = s_wave_tot[w];
+            woff += (w < wave) ? t : 0;
+            tot += t;
+        }
+        const int slot = base + woff + excl;
+        if (r < p.R) {
+            p.row_slot[r] = rec ? slot : -1;
+            if (rec) p.rec_rows[slot] = r;
+            if (r % p.N == 0) p.branch_off[r / p.N] = slot;
+        }
+        base += tot;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        p.rec_count[0] = base;
+        p.branch_off[p.nb] = base;
+    }
+}
+
+__global__ __launch_bounds__(256) void resolve_kernel(const ResolveParams p) {
+    const int r = blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= p.R) return;
+    const int i = r / p.N, n = r - i * p.N;
+    int j = i;
+    for (int s = 0; s < p.nb && j > 0 && p.fold[j * p.N + n] != 0; ++s) j = p.par.p[j];
+    p.src_branch[r] = j;
+    p.src_slot[r] = p.row_slot[j * p.N + n];
+}
+
+// one wave per row: xn = bf16(X * s * ln)
+__global__ __launch_bounds__(256) void row_norm_kernel(const uint16_t* __restrict__ X, int R, int D,
+                                                       const float* inv_rms, float eps,
+                                                       const uint16_t* ln, uint16_t* __restrict__ xn) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (row >= R) return;
+    const int nch = D >> 3;
+    const uint4* c = reinterpret_cast<const uint4*>(X + static_cast<size_t>(row) * D);
+    float s;
+    if (inv_rms) {
+        s = inv_rms[row];
+    } else {
+        float ss = 0.f;
+        for (int k = lane; k < nch; k += kWave) {
+            float x[8];
+            unpack8(c[k], x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+        }
+        ss = wave_sum(ss);
+        s = 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
+    }
+    uint4* o = reinterpret_cast<uint4*>(xn + static_cast<size_t>(row) * D);
+    for (int k = lane; k < nch; k += kWave) {
+        float x[8];
+        unpack8(c[k], x);
+        o[k] = norm_chunk(x, s, ln, k);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gate(const GateParams& p, hipStream_t st) {
+    const int R = p.nb * p.N;
+    if (R <= 0) return hipSuccess;
+    hipLaunchKernelGGL(gate_kernel, dim3((R + 3) / 4), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_compact(const CompactParams& p, hipStream_t st) {
+    hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_resolve(const ResolveParams& p, hipStream_t st) {
+    if (p.R <= 0) return hipSuccess;
+    hipLaunchKernelGGL(resolve_kernel, dim3((p.R + 255) / 256), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_row_norm(const uint16_t* X, int R, int D, const float* inv_rms, float eps, const uint16_t* ln,
+                           uint16_t* xn, hipStream_t st) {
+    if (R <= 0) return hipSuccess;
+    hipLaunchKernelGGL(row_norm_kernel, dim3((R + 3) / 4), dim3(256), 0, st, X, R, D, inv_rms, eps, ln, xn);
+    return hipGetLastError();
+}
+
+}  // namespace specfold

@@ -1,0 +1,133 @@
+"""The C ABI loads, exports every declared symbol, and rejects bad arguments on the host
+before launching anything (CPU only: every call here fails validation, so no kernel runs)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_layer_rho_amd import specfold as sf
+from synth import WORKLOADS
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "specfold.h")
+L = sf.lib()
+FAKE = 0x10000          # aligned stand-in device address: never dereferenced by failing calls
+MISALIGNED = 0x10008
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(specfold_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(sf.EXPORTS)
+
+
+def test_version_status_and_stages():
+    assert L.specfold_version() == 1
+    for code in range(-8, 1):
+        assert L.specfold_status_str(code)
+    assert sf.stage_names()[0] == "gate_rmsnorm"
+    assert L.specfold_last_error() == b""
+    assert L.specfold_stage_name(99) is None
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workspace_bytes_positive(name):
+    assert sf.workspace_bytes(WORKLOADS[name].shape) > 0
+
+
+def _shape(**kw):
+    base = WORKLOADS["tiny"].shape
+    vals = {f: getattr(base, f) for f in ("n_branch", "block", "hidden", "n_q_heads", "n_kv_heads",
+                                          "head_dim", "ffn", "prefix_len", "rms_eps", "rope_theta")}
+    vals.update(kw)
+    return sf.Shape(*[vals[f] for f, _ in sf.Shape._fields_])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=24), -6), (dict(n_q_heads=3), -2), (dict(n_branch=0), -2), (dict(block=65), -6),
+    (dict(n_branch=65), -6), (dict(hidden=96), -6), (dict(ffn=100), -6), (dict(prefix_len=-1), -2),
+    (dict(rope_theta=0.0), -2),
+])
+def test_workspace_bytes_rejects_bad_shapes(kw, code):
+    sh = _shape(**kw)
+    assert L.specfold_workspace_bytes(ctypes.byref(sh)) == 0
+
+
+def _parent(vals):
+    arr = (ctypes.c_int32 * len(vals))(*vals)
+    return ctypes.cast(arr, ctypes.c_void_p), arr
+
+
+@pytest.mark.parametrize("par,code", [([0, 0, 1], -3), ([-1, 1, 1], -3), ([-1, 0, 2], -3), ([-1, 0, -1], -3)])
+def test_gate_rejects_bad_tree(par, code):
+    sh = _shape()
+    p, keep = _parent(par)
+    st = L.specfold_gate(ctypes.byref(sh), p, FAKE, 0.1, None, FAKE, FAKE * 2, None, None)
+    assert st == code
+
+
+def test_gate_rejects_null_misaligned_alias():
+    sh = _shape()
+    p, keep = _parent([-1, 0, 1])
+    assert L.specfold_gate(ctypes.byref(sh), p, None, 0.1, None, FAKE, FAKE * 2, None, None) == -1
+    assert L.specfold_gate(ctypes.byref(sh), p, MISALIGNED, 0.1, None, FAKE, FAKE * 2, None, None) == -4
+    # rho and fold overlap
+    assert L.specfold_gate(ctypes.byref(sh), p, FAKE * 8, 0.1, None, FAKE, FAKE, None, None) == -7
+    assert L.specfold_gate(None, p, FAKE, 0.1, None, FAKE, FAKE * 2, None, None) == -1
+
+
+def test_compact_and_resolve_validation():
+    sh = _shape()
+    p, keep = _parent([-1, 0, 1])
+    assert L.specfold_compact(ctypes.byref(sh), FAKE, None, FAKE * 2, FAKE * 3, FAKE * 4, None) == -1
+    assert L.specfold_compact(ctypes.byref(sh), FAKE, FAKE * 2, FAKE * 2, FAKE * 3, FAKE * 4, None) == -7
+    assert L.specfold_resolve_sources(ctypes.byref(sh), p, FAKE, FAKE * 2, FAKE * 3, FAKE * 3, None) == -7
+    bad, keep2 = _parent([-1, 5, 1])
+    assert L.specfold_resolve_sources(ctypes.byref(sh), bad, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None) == -3
+
+
+def test_layer_entry_points_reject_small_workspace_and_alias():
+    sh = _shape()
+    need = L.specfold_workspace_bytes(ctypes.byref(sh))
+    ws = 0x40000000
+    args = [FAKE * k for k in range(1, 11)]
+    # sparse_qkv: too small a workspace
+    # (H, inv_rms, rec_rows, rec_count, ln1, w_qkv, q_c, k_c, v_c)
+    assert L.specfold_sparse_qkv(ctypes.byref(sh), *args[:9], ws, need - 1, None) == -5
+    assert L.specfold_sparse_qkv(ctypes.byref(sh), *args[:9], None, need, None) == -5
+    # q_c overlaps k_c
+    assert L.specfold_sparse_qkv(ctypes.byref(sh), *args[:6], FAKE * 20, FAKE * 20, FAKE * 30, ws, need, None) == -7
+    # out_proj: h_mid == H
+    assert L.specfold_out_proj(ctypes.byref(sh), FAKE, FAKE * 2, FAKE * 3, FAKE * 2, ws, need, None) == -7
+    # sparse_ffn: H_out == h_mid
+    assert L.specfold_sparse_ffn(ctypes.byref(sh), FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 5, FAKE * 6,
+                                 FAKE * 7, FAKE, ws, need, None) == -7
+
+
+def test_verify_layer_validation():
+    sh = _shape()
+    need = L.specfold_workspace_bytes(ctypes.byref(sh))
+    ws = 0x40000000
+    p, keep = _parent([-1, 0, 1])
+    w = sf.LayerWeights(*(FAKE * k for k in range(1, 7)))
+    pf = sf.PrefixKV(FAKE * 8, FAKE * 9, 32, 16, 32, 16)
+    H_in, H_out = 0x20000000, 0x30000000
+    call = lambda **kw: L.specfold_verify_layer(
+        ctypes.byref(kw.get("sh", sh)), kw.get("p", p), ctypes.byref(kw.get("w", w)), ctypes.byref(kw.get("pf", pf)),
+        kw.get("H_in", H_in), 0.1, kw.get("H_out", H_out), None, None, kw.get("ws", ws), kw.get("wsb", need), None)
+    assert call(H_out=H_in) == -7
+    assert call(wsb=16) == -5
+    bad, keep2 = _parent([-1, 0, 3])
+    assert call(p=bad) == -3
+    assert call(w=sf.LayerWeights(FAKE, None, FAKE, FAKE, FAKE, FAKE)) == -1
+    assert call(pf=sf.PrefixKV(FAKE * 8, FAKE * 9, 33, 16, 32, 16)) == -4
+    assert call(sh=_shape(block=80)) == -6

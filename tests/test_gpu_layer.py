@@ -1,0 +1,130 @@
+"""GPU parity of the whole folded layer (specfold_verify_layer) against the oracle,
+teacher-forced on the GPU's own bf16 input and mask (the mask may differ only where
+|rho - delta| < 1e-4), plus edge cases, determinism and full-size workloads."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_case import LayerCase, rel_l2
+from synth import WORKLOADS, Shape, layer_weights, parent_tree, prefix_kv, step_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["tiny", "layer-1.5b"])
+def test_verify_layer_matches_oracle(name):
+    wl = WORKLOADS[name]
+    case = LayerCase.workload(name)
+    res = case.run(wl.delta)
+    _, err = case.check(wl.delta, res)
+    print(f"{name}: rel L2 {err:.2e}, update rel err {case.last_update_err:.2e}, "
+          f"M = {res['rec_count']} of {case.shape.rows}")
+
+
+@pytest.mark.parametrize("shape,tree", [
+    (Shape(1, 32, 128, 4, 2, 32, 192, 40), "random"),        # B = 0: a plain dense layer
+    (Shape(4, 20, 128, 4, 1, 64, 256, 0), "random"),         # no prefix, ragged rows (R = 80)
+    (Shape(9, 8, 192, 6, 3, 32, 320, 100), "chain"),         # deep fold chains, ragged prefix chunk
+    (Shape(17, 64, 256, 8, 2, 64, 320, 300), "random"),      # R = 1088: GEMMs loop over row passes
+    (Shape(5, 33, 128, 2, 2, 64, 128, 513), "star"),         # N not a multiple of 16
+])
+def test_verify_layer_edge_shapes(shape, tree):
+    case = LayerCase(shape, 11, tree=tree, random_norm=True, weight_scale=8.0)
+    for delta in (0.0, 0.1, 0.3):
+        res = case.run(delta)
+        case.check(delta, res)
+
+
+def test_delta_zero_is_dense_per_branch():
+    wl = WORKLOADS["tiny"]
+    case = LayerCase.workload("tiny")
+    res = case.run(0.0)
+    assert res["fold"][1:].sum() == 0 and res["rec_count"] == case.shape.rows
+    for i in range(case.shape.n_branch):
+        dense = oracle.dense_branch_layer(case.H[i], case.w, case.pk, case.pv, case.shape)
+        assert rel_l2(res["H_out"][i], dense) < 2e-2
+    del wl
+
+
+def test_delta_infinite_every_draft_inherits_main():
+    """All drafts fold, inherit main's Q/K/V and FFN output: every draft's update equals
+    main's, up to the bf16 rounding of h_mid and H_out (weights scaled so the update is O(1))."""
+    case = LayerCase.workload("tiny", weight_scale=10.0)
+    res = case.run(float("inf"))
+    assert res["fold"][1:].all() and res["rec_count"] == case.shape.block
+    upd = res["H_out"] - case.H
+    for i in range(1, case.shape.n_branch):
+        assert rel_l2(upd[i], upd[0]) < 2e-2
+    case.check(float("inf"), res)
+
+
+def test_identical_draft_and_nan_row():
+    sh = WORKLOADS["tiny"].shape
+    inp = step_inputs(sh, 0, 0, tree="chain", child_law="tiny")
+    H = inp["H"].copy()
+    H[2] = H[1]
+    case = LayerCase(sh, 0, H=H, parent=inp["parent"])
+    res = case.run(0.1)
+    assert res["fold"][2].all()
+    assert np.array_equal(res["H_out_bits"].reshape(3, 8, -1)[2], res["H_out_bits"].reshape(3, 8, -1)[1])
+    # a NaN in a draft row: rho is NaN, the row is recomputed (and its own output is NaN)
+    H2 = case.H.copy()
+    H2[1, 3, 5] = np.nan
+    res2 = case.run(0.1, H=H2)
+    assert res2["fold"][1, 3] == 0 and np.isnan(res2["rho"][1, 3])
+
+
+def test_deterministic_bitwise_and_workspace_reuse():
+    wl = WORKLOADS["layer-1.5b"]
+    case = LayerCase.workload("layer-1.5b")
+    from sparse_layer_rho_amd import specfold as sf
+    ws = sf.new_workspace(case.shape)
+    ws[256:].fill_(0xFF)                      # poison everything but the counters
+    a = case.run(wl.delta, ws=ws)
+    b = case.run(wl.delta, ws=ws)
+    assert np.array_equal(a["H_out_bits"], b["H_out_bits"])
+    assert np.array_equal(a["src_slot"], b["src_slot"]) and a["rec_count"] == b["rec_count"]
+    assert int(ws[:4].view(torch.int32).item()) == 0     # ticket counter left at zero
+    c = case.run(0.0, ws=ws)                  # a different M on the same workspace
+    case.check(0.0, c)
+
+
+def test_stack_accumulates_divergence_and_matches_per_layer():
+    """Six layers of the 1.5B-shape stack at prefix 2048; every layer re-gates on the GPU's own
+    output of the previous layer and is checked teacher-forced."""
+    wl = WORKLOADS["stack-1.5b"]
+    sh = wl.shape
+    inp = step_inputs(sh, wl.base_seed, 0)
+    H = inp["H"]
+    rhos = []
+    for layer in range(6):
+        case = LayerCase(sh, wl.base_seed, layer=layer, H=H, parent=inp["parent"])
+        res = case.run(wl.delta)
+        _, err = case.check(wl.delta, res)
+        rhos.append(res["rho"])
+        print(f"layer {layer}: fold {res['fold'][1:].mean():.3f} rel L2 {err:.2e} "
+              f"update rel err {case.last_update_err:.2e}")
+        H = res["H_out"]
+    # every layer gates on its own input: the residuals move from layer to layer
+    assert not np.allclose(rhos[0][1:], rhos[-1][1:], rtol=1e-3)
+
+
+def test_layer_7b_shape():
+    wl = WORKLOADS["stack-7b"]
+    case = LayerCase(wl.shape, wl.base_seed, layer=13)
+    res = case.run(wl.delta)
+    _, err = case.check(wl.delta, res)
+    print(f"7b layer 13: rel L2 {err:.2e}")
+
+
+@pytest.mark.parametrize("B", [2, 8])
+def test_layer_14b_shape_sweep_points(B):
+    wl = WORKLOADS["sweep-14b"]
+    sh = wl.shape.with_branches(B + 1)
+    case = LayerCase(sh, wl.base_seed)
+    for delta in (0.0, 0.1, 0.7):
+        res = case.run(delta)
+        _, err = case.check(delta, res)
+        print(f"14b B={B} delta={delta}: fold {res['fold'][1:].mean():.3f} rel L2 {err:.2e}")

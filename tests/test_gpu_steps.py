@@ -1,0 +1,219 @@
+"""GPU parity of each C-ABI step against the oracle (integer outputs bit-exact)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_case import DEV, LayerCase, dev_bf16, host, random_mask, rel_l2
+from sparse_layer_rho_amd import specfold as sf
+from synth import WORKLOADS, Shape, parent_tree
+
+pytestmark = pytest.mark.gpu
+
+I32, U8, F32 = torch.int32, torch.uint8, torch.float32
+
+
+def _gate(case, delta, rho_in=None):
+    sh = case.shape
+    R = sh.n_branch * sh.block
+    rho = torch.full((R,), float("nan"), device=DEV)
+    fold = torch.full((R,), 9, dtype=U8, device=DEV)
+    inv = torch.full((R,), float("nan"), device=DEV)
+    sf.gate(sh, case.parent, dev_bf16(case.H.reshape(R, -1)), delta, rho, fold, inv,
+            rho_in=None if rho_in is None else torch.from_numpy(rho_in.astype(np.float32).ravel()).to(DEV))
+    torch.cuda.synchronize()
+    return (rho.cpu().numpy().reshape(sh.n_branch, sh.block), fold.cpu().numpy().reshape(sh.n_branch, sh.block),
+            inv.cpu().numpy())
+
+
+def _compact_resolve(shape, parent, fold):
+    R = shape.n_branch * shape.block
+    f = torch.from_numpy(fold.astype(np.uint8).ravel()).to(DEV)
+    rec = torch.full((R,), -5, dtype=I32, device=DEV)
+    cnt = torch.full((1,), -5, dtype=I32, device=DEV)
+    off = torch.full((shape.n_branch + 1,), -5, dtype=I32, device=DEV)
+    slot = torch.full((R,), -5, dtype=I32, device=DEV)
+    sb = torch.full((R,), -5, dtype=I32, device=DEV)
+    ss = torch.full((R,), -5, dtype=I32, device=DEV)
+    sf.compact(shape, f, rec, cnt, off, slot)
+    sf.resolve_sources(shape, parent, f, slot, sb, ss)
+    torch.cuda.synchronize()
+    M = int(cnt.item())
+    return rec.cpu().numpy()[:M], M, off.cpu().numpy(), slot.cpu().numpy(), sb.cpu().numpy(), ss.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", ["tiny", "layer-1.5b"])
+def test_gate_matches_oracle(name):
+    wl = WORKLOADS[name]
+    case = LayerCase.workload(name)
+    rho, fold, inv = _gate(case, wl.delta)
+    rho_o, fold_o = oracle.gate(case.H, case.parent, wl.delta)
+    band = np.abs(rho_o - wl.delta) < 1e-4
+    assert np.array_equal(fold.astype(bool)[~band], fold_o[~band])
+    np.testing.assert_allclose(rho, rho_o, rtol=5e-5, atol=1e-7)
+    ms = np.mean(case.H.reshape(-1, case.shape.hidden) ** 2, axis=1)
+    np.testing.assert_allclose(inv, 1.0 / np.sqrt(ms + case.shape.rms_eps), rtol=1e-5)
+
+
+def test_gate_identical_draft_folds_all_and_large_flat_input():
+    sh = Shape(9, 512, 1536, 12, 2, 128, 8960, 0)
+    rng = np.random.default_rng(0)
+    H = rng.standard_normal((9, 512, 1536))
+    parent = parent_tree(9, 5, 0)
+    for i in range(1, 9):
+        H[i] = H[parent[i]] + 0.05 * rng.standard_normal((512, 1536))
+    H[4] = H[parent[4]]
+    case = LayerCase(sh, 0, H=H, parent=parent)
+    rho, fold, _ = _gate(case, 0.1)
+    assert fold[4].all() and np.all(rho[4] == 0)
+    rho_o, fold_o = oracle.gate(case.H, parent, 0.1)
+    band = np.abs(rho_o - 0.1) < 1e-4
+    assert np.array_equal(fold.astype(bool)[~band], fold_o[~band])
+
+
+def test_gate_threshold_bit_exact_when_fed_rho():
+    """Fed the same rho values, the GPU mask is exactly float32(rho) <= float32(delta)."""
+    case = LayerCase.workload("tiny")
+    d32 = np.float32(0.1)
+    vals = np.array([0.0, d32, np.nextafter(d32, np.float32(1)), np.nextafter(d32, np.float32(0)),
+                     np.inf, np.nan, 1e-30, 0.5], dtype=np.float32)
+    B1, N = case.shape.n_branch, case.shape.block
+    rho_in = np.resize(vals, B1 * N).reshape(B1, N).astype(np.float32)
+    _, fold, _ = _gate(case, 0.1, rho_in=rho_in)
+    expect = rho_in <= d32
+    expect[0] = False
+    assert np.array_equal(fold.astype(bool), expect)
+
+
+@pytest.mark.parametrize("B1,N,kind,p", [(3, 8, "chain", 0.7), (9, 32, "random", 0.72), (6, 20, "star", 0.5),
+                                         (64, 64, "random", 0.8), (9, 32, "random", 1.0), (9, 32, "random", 0.0),
+                                         (1, 17, "random", 0.5), (33, 40, "chain", 0.9)])
+def test_compact_and_resolve_bit_exact(B1, N, kind, p):
+    sh = Shape(B1, N, 64, 4, 2, 16, 128, 0)
+    rng = np.random.default_rng(B1 * 100 + N)
+    parent = parent_tree(B1, 7, 0, kind, max_depth=64 if kind == "chain" else 4)
+    fold = random_mask(sh, rng, p)
+    rec, M, off, slot, sb, ss = _compact_resolve(sh, parent, fold)
+    rec_o, slot_o, off_o = oracle.compact(fold)
+    src_o, src_slot_o = oracle.resolve(fold, parent, slot_o)
+    assert M == rec_o.size
+    assert np.array_equal(rec, rec_o)
+    assert np.array_equal(slot, slot_o)
+    assert np.array_equal(off, off_o)
+    assert np.array_equal(sb.reshape(B1, N), src_o)
+    assert np.array_equal(ss.reshape(B1, N), src_slot_o)
+
+
+def _oracle_steps(case, delta):
+    res = oracle.verify_layer(case.H, case.parent, case.w, case.pk, case.pv, delta, case.shape)
+    return res
+
+
+@pytest.mark.parametrize("name", ["tiny", "layer-1.5b"])
+def test_sparse_qkv_matches_oracle(name):
+    wl = WORKLOADS[name]
+    case = LayerCase.workload(name, random_norm=True)
+    sh = case.shape
+    R, D = sh.n_branch * sh.block, sh.hidden
+    ref = _oracle_steps(case, wl.delta)
+    _, fold_g, inv = _gate(case, wl.delta)
+    assert np.array_equal(fold_g.astype(bool), ref["fold"])
+    rec, M, off, slot, sb, ss = _compact_resolve(sh, case.parent, ref["fold"])
+    w, _, _ = case.device()
+    rec_t = torch.full((R,), 0, dtype=I32, device=DEV)
+    rec_t[:M] = torch.from_numpy(rec.astype(np.int32)).to(DEV)
+    cnt = torch.tensor([M], dtype=I32, device=DEV)
+    q = torch.full((R, sh.n_q_heads, sh.head_dim), float("nan"), dtype=torch.bfloat16, device=DEV)
+    k = torch.full((R, sh.n_kv_heads, sh.head_dim), float("nan"), dtype=torch.bfloat16, device=DEV)
+    v = torch.full_like(k, float("nan"))
+    ws = sf.new_workspace(sh)
+    sf.sparse_qkv(sh, dev_bf16(case.H.reshape(R, D)), torch.from_numpy(inv).to(DEV), rec_t, cnt, w["ln1"],
+                  w["w_qkv"], q, k, v, ws)
+    torch.cuda.synchronize()
+    for got, exp in ((q, ref["q_c"]), (k, ref["k_c"]), (v, ref["v_c"])):
+        g = host(got)[:M]
+        assert np.isfinite(g).all()
+        assert rel_l2(g, exp) < 1e-2
+
+
+@pytest.mark.parametrize("name", ["tiny", "layer-1.5b", "sweep-14b"])
+def test_folded_attention_matches_oracle(name):
+    wl = WORKLOADS[name]
+    case = LayerCase.workload(name)
+    sh = case.shape
+    R = sh.n_branch * sh.block
+    ref = _oracle_steps(case, wl.delta)
+    M = ref["rec_rows"].size
+    # bf16-rounded projections feed both sides
+    qc, kc, vc = (np.asarray(torch.from_numpy(ref[k].astype(np.float32)).to(torch.bfloat16).float(), np.float64)
+                  for k in ("q_c", "k_c", "v_c"))
+    attn_ref = np.empty((sh.n_branch, sh.block, sh.n_q_heads, sh.head_dim))
+    for i in range(sh.n_branch):
+        s = ref["src_slot"][i]
+        attn_ref[i] = oracle.attention_block(qc[s], kc[s], vc[s], case.pk, case.pv, sh)
+
+    def pad(x):
+        out = np.zeros((R,) + x.shape[1:], np.float32)
+        out[:M] = x
+        return dev_bf16(out)
+
+    _, pk, pv = case.device()
+    attn = torch.full((R, sh.n_q_heads * sh.head_dim), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((R, sh.n_q_heads), float("nan"), device=DEV)
+    rec_t = torch.zeros(R, dtype=I32, device=DEV)
+    rec_t[:M] = torch.from_numpy(ref["rec_rows"].astype(np.int32)).to(DEV)
+    cnt = torch.tensor([M], dtype=I32, device=DEV)
+    src = torch.from_numpy(ref["src_slot"].astype(np.int32).ravel()).to(DEV)
+    ws = sf.new_workspace(sh)
+    sf.folded_attention(sh, pad(qc), pad(kc), pad(vc), rec_t, cnt, src, pk, pv, attn, ws, lse=lse)
+    torch.cuda.synchronize()
+    got = host(attn)
+    assert np.isfinite(got).all()
+    assert rel_l2(got, attn_ref.reshape(R, -1)) < 1e-2
+    # log-sum-exp of the scaled scores for a few rows
+    G = sh.n_q_heads // sh.n_kv_heads
+    lse_h = lse.cpu().numpy()
+    for r in (0, R // 2, R - 1):
+        i, n = divmod(r, sh.block)
+        s = ref["src_slot"][i]
+        for h in (0, sh.n_q_heads - 1):
+            g = h // G
+            keys = np.concatenate([case.pk[:, g], kc[s][:, g]])
+            sc = keys @ qc[s[n], h] / np.sqrt(sh.head_dim)
+            mx = sc.max()
+            assert lse_h[r, h] == pytest.approx(mx + np.log(np.exp(sc - mx).sum()), rel=2e-3, abs=2e-3)
+
+
+@pytest.mark.parametrize("name", ["tiny", "layer-1.5b"])
+def test_out_proj_and_sparse_ffn_match_oracle(name):
+    wl = WORKLOADS[name]
+    case = LayerCase.workload(name, random_norm=True, weight_scale=10.0 if name == "tiny" else 1.0)
+    sh = case.shape
+    R, D = sh.n_branch * sh.block, sh.hidden
+    ref = _oracle_steps(case, wl.delta)
+    M = ref["rec_rows"].size
+    w, _, _ = case.device()
+    ws = sf.new_workspace(sh)
+    attn_b = dev_bf16(ref["attn"])
+    h_mid = torch.full((R, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    sf.out_proj(sh, attn_b, dev_bf16(case.H.reshape(R, D)), w["w_o"], h_mid, ws)
+    torch.cuda.synchronize()
+    hm = host(h_mid)
+    attn_r = host(attn_b)
+    exp_hmid = case.H.reshape(R, D) + attn_r @ case.w["w_o"].astype(np.float64).T
+    assert rel_l2(hm, exp_hmid) < 5e-3
+    # FFN on the GPU's own h_mid
+    rec_t = torch.zeros(R, dtype=I32, device=DEV)
+    rec_t[:M] = torch.from_numpy(ref["rec_rows"].astype(np.int32)).to(DEV)
+    cnt = torch.tensor([M], dtype=I32, device=DEV)
+    src = torch.from_numpy(ref["src_slot"].astype(np.int32).ravel()).to(DEV)
+    out = torch.full((R, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    sf.sparse_ffn(sh, h_mid, rec_t, cnt, src, w["ln2"], w["w_gate_up"], w["w_down"], out, ws)
+    torch.cuda.synchronize()
+    f = oracle.ffn_rows(hm[ref["rec_rows"]], case.w["ln2"], case.w["w_gate_up"], case.w["w_down"], sh)
+    exp_out = hm + f[ref["src_slot"].ravel()]
+    got = host(out)
+    assert np.isfinite(got).all()
+    assert rel_l2(got, exp_out) < 1e-2
+    assert rel_l2(got - hm, exp_out - hm) < 2e-2
