@@ -56,7 +56,7 @@ int pick_splits(int nout, int k, int nt) {
 
 Layout layout_of(const Dims& d) {
     Layout L;
-    L.nt_qkv = 4; L.nt_o = 4; L.nt_gu = 4; L.nt_down = 4;
+    L.nt_qkv = 4; L.nt_o = 4; L.nt_gu = 8; L.nt_down = 4;
     L.s_qkv = pick_splits(d.Nq, d.D, L.nt_qkv);
     L.s_o = pick_splits(d.D, d.Do, L.nt_o);
     L.s_down = pick_splits(d.D, d.F, L.nt_down);
@@ -131,7 +131,15 @@ int check_layer_shape(const specfold_shape* s) {
     if (hd != 16 && hd != 32 && hd != 64 && hd != 128) return SPECFOLD_ERR_UNSUPPORTED;
     if (s->ffn % 64 != 0 || (s->n_q_heads * hd) % 64 != 0) return SPECFOLD_ERR_UNSUPPORTED;
     if (((s->n_q_heads + 2 * s->n_kv_heads) * hd) % 32 != 0) return SPECFOLD_ERR_UNSUPPORTED;
-    if (static_cast<int64_t>(s->hidden) * s->ffn > (int64_t(1) << 31)) return SPECFOLD_ERR_UNSUPPORTED;
+    // every weight matrix and activation buffer a GEMM streams must stay below 1 GB (the
+    // kernels address them with 32-bit buffer offsets and out-of-range sentinels above 1 GB)
+    const int64_t gb = int64_t(1) << 30;
+    const int64_t R = static_cast<int64_t>(s->n_branch) * s->block;
+    const int64_t nq = static_cast<int64_t>(s->n_q_heads + 2 * s->n_kv_heads) * hd;
+    if (4 * static_cast<int64_t>(s->hidden) * s->ffn >= gb || 2 * nq * s->hidden >= gb ||
+        2 * static_cast<int64_t>(s->hidden) * s->n_q_heads * hd >= gb || 2 * R * s->ffn >= gb ||
+        2 * R * s->hidden >= gb)
+        return SPECFOLD_ERR_UNSUPPORTED;
     if (static_cast<int64_t>(s->prefix_len) > (int64_t(1) << 24)) return SPECFOLD_ERR_UNSUPPORTED;
     return SPECFOLD_OK;
 }

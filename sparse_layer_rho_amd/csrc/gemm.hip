@@ -1,18 +1,21 @@
 // Gathered-row bf16 GEMM on gfx950 MFMA: C[m][n] = sum_k A[row(m)][k] * W[n][k].
 //
 // The layer's projections are skinny: M (recompute rows, <= R = 288 at B = 8, N = 32) is small
-// and W [Nout][K] is large, so the kernel is built to stream W once from HBM at full rate:
-//   * a 256-thread workgroup (4 waves) owns NT 16-column tiles over all M rows and a range of K
-//     (grid.y splits K when the column tiles alone cannot fill the 256 CUs);
-//   * both operands move HBM/L2 -> LDS by buffer_load ... lds (no register staging) into a ring
-//     of ST stages, each stage holding KS 32-wide k-steps in MFMA fragment order (lane l's
-//     16 bytes at lane*16, so every LDS read is a conflict-free ds_read_b128);
-//   * addresses are branch-free: rows past M, column tiles past Nout and k-steps past the split
-//     use out-of-range buffer offsets, which read as zeros without touching memory -- so the
-//     number of loads in flight is static and the waits are exact vmcnt counts;
-//   * the 4 waves split the M tiles and share the weight fragments; v_mfma_f32_16x16x32_bf16
-//     with a weight fragment as the A operand and 16 activation rows as the B operand leaves
-//     each lane 4 consecutive output columns of one row.
+// and W [Nout][K] is large, so the kernel is built to stream W from HBM at full rate:
+//   * a 256-thread workgroup (4 waves) owns NT 16-row weight tiles (16*NT output columns), a
+//     chunk of 64*MTW activation rows and a range of K (grid.y splits K when the column tiles
+//     alone cannot fill the 256 CUs);
+//   * K advances in stages of 256: for its stage every wave loads 2 weight rows x 512 contiguous
+//     bytes per instruction (the access pattern HBM serves fastest), one stage ahead into
+//     registers, and writes them into LDS in an XOR-swizzled row-major layout, so the MFMA
+//     fragment reads (16 rows x 16 bytes per lane group) are conflict-free ds_read_b128;
+//   * each wave loads its own activation row tiles straight into registers in MFMA operand
+//     layout (they are L2-resident), double-buffered, so activations never touch LDS;
+//   * loads are branch-free: rows past M, column tiles past Nout and K past the split use
+//     out-of-range buffer offsets, which read as zeros without touching memory, and every wait
+//     is the compiler's own exact vmcnt;
+//   * v_mfma_f32_16x16x32_bf16 with a weight fragment as the A operand and 16 activation rows
+//     as the B operand leaves each lane 4 consecutive output columns of one row.
 // Rows come from an identity map, a device list, or -- fused -- from the fold flags: every
 // workgroup compacts them in LDS (ascending row order) and workgroup (0,0) also publishes the
 // recompute list, per-branch offsets, row -> slot map and fold sources
@@ -28,9 +31,13 @@ namespace specfold {
 
 namespace {
 
-constexpr uint32_t kOobRow = 0x40000000u;   // offset of a missing row / column tile (>= any buffer)
-constexpr uint32_t kOobK = 0x80000000u;     // added to every offset of a k-step past the split
+// Out-of-range offsets: a missing row / column tile adds kOobRow, K past the split adds kOobK.
+// Buffers are < 1 GB (checked by the host), so any sum involving either is out of range and the
+// two never wrap back into range together.
+constexpr uint32_t kOobRow = 0x40000000u;
+constexpr uint32_t kOobK = 0x80000000u;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
+constexpr int kStageK = 256;                // K elements per stage (512 bytes of a bf16 row)
 
 enum { EPI_PARTIAL = 0, EPI_SWIGLU = 1 };
 
@@ -38,41 +45,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
-    typedef __attribute__((address_space(3))) void lds_void;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds), 16, voff, 0, 0, 0);
-}
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-
-// ds_read_b128 issued as inline asm: the compiler cannot prove these reads miss the LDS bytes
-// that in-flight DMA is writing and would otherwise wait for all DMA before every read; the
-// ring-buffer protocol (exact vmcnt + barrier) already orders them.  Results are only valid
-// after lds_wait().
-__device__ __forceinline__ u32x4 lds_read16(const uint8_t* p) {
-    u32x4 v;
-    const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_u8*)(p)));
-    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(a));
-    return v;
-}
-
-// wait for every issued LDS read and pin the fragments after the wait
-template <int N>
-__device__ __forceinline__ void lds_wait(u32x4 (&v)[N]) {
+__device__ __forceinline__ void block_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
-
-__device__ __forceinline__ uint4 as_uint4(const u32x4& v) { return make_uint4(v.x, v.y, v.z, v.w); }
 
 // call f(std::integral_constant<int, n>) for a runtime n in [0, MAX]
 template <int MAX, int N = 0, typename F>
@@ -83,12 +64,6 @@ __device__ __forceinline__ void dispatch_count(int n, F&& f) {
     } else {
         f(std::integral_constant<int, MAX>{});
     }
-}
-
-__device__ __forceinline__ void block_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
 }
 
 // Compact the recompute rows (fold == 0) of R rows into s_rows (ascending), 256 threads.
@@ -144,19 +119,16 @@ __device__ int compact_in_lds(const GemmArgs& p, int32_t* s_rows, int* s_tot, bo
     return base;
 }
 
-template <int NT, int MTW, int KS, int ST, int EPI>
+template <int NT, int MTW, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmArgs p) {
-    constexpr int MP = 4 * MTW * 16;                       // rows per pass
-    constexpr int W_FR = KS * NT;                          // weight fragments per stage
-    constexpr int A_FR = 4 * MTW * KS;                     // activation fragments per stage
-    constexpr int STAGE = (W_FR + A_FR) * 1024;            // bytes per stage
-    constexpr int WLOADS = W_FR / 4;                       // weight DMA per wave per stage
-    constexpr int LPS = WLOADS + MTW * KS;                 // DMA per wave per stage
-    static_assert(NT % 4 == 0, "weight fragments must split over 4 waves");
-    static_assert((ST - 2) * LPS < 64, "vmcnt range");
+    constexpr int WROWS = 16 * NT;                 // weight rows per workgroup
+    constexpr int WBUF = WROWS * 512;              // LDS bytes of one weight stage
+    constexpr int WLD = WROWS / 8;                 // 16-byte weight loads per lane per stage
+    constexpr int MP = 64 * MTW;                   // activation rows per workgroup
+    static_assert(NT % 2 == 0 && WLD >= 1, "tile shape");
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ int s_tot[4];
-    int32_t* s_rows = reinterpret_cast<int32_t*>(smem + ST * STAGE);
+    int32_t* s_rows = reinterpret_cast<int32_t*>(smem + 2 * WBUF);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
@@ -180,152 +152,163 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmArgs p) {
     M = __builtin_amdgcn_readfirstlane(M);
     const int m0 = chunk * MP;
     if (tile >= p.n_tiles || m0 >= M) return;     // uniform: nothing for this workgroup
+    const int mrows = min(MP, M - m0);
+    const int mtiles = __builtin_amdgcn_readfirstlane((mrows + 15) >> 4);
 
-    // k-steps (32 wide) of this split, grouped in stages of KS
+    // K range of this split (in 32-wide k-steps) and its stages of 256
     const int nks = p.K / 32;
-    const int ks0 = static_cast<int>(static_cast<int64_t>(y) * nks / S);
-    const int ks1 = static_cast<int>(static_cast<int64_t>(y + 1) * nks / S);
-    const int nstages = (ks1 - ks0 + KS - 1) / KS;
+    const int k_begin = static_cast<int>(static_cast<int64_t>(y) * nks / S) * 32;
+    const int k_end = static_cast<int>(static_cast<int64_t>(y + 1) * nks / S) * 32;
+    const int nstages = (k_end - k_begin + kStageK - 1) / kStageK;
 
-    // weight fragment rows: fragment f = s*NT + nt, loaded by wave f % 4
-    const __amdgpu_buffer_rsrc_t rW = make_rsrc(p.W, static_cast<uint32_t>(static_cast<size_t>(p.Nout) * p.K * 2));
-    const int bx = tile;
-    auto col_of = [&](int nt) -> int {
+    auto col_of = [&](int nt) -> int {             // first output column of N-tile nt
         if (EPI == EPI_SWIGLU) {
-            const int j0 = bx * (NT / 2) * 16;
+            const int j0 = tile * (NT / 2) * 16;
             return nt < NT / 2 ? j0 + nt * 16 : p.F + j0 + (nt - NT / 2) * 16;
         }
-        return (bx * NT + nt) * 16;
+        return (tile * NT + nt) * 16;
     };
     auto col_ok = [&](int nt) -> bool {
-        return EPI == EPI_SWIGLU ? (bx * (NT / 2) + (nt % (NT / 2))) * 16 < p.F : col_of(nt) < p.Nout;
+        return EPI == EPI_SWIGLU ? (tile * (NT / 2) + (nt % (NT / 2))) * 16 < p.F : col_of(nt) < p.Nout;
     };
-    // wave w loads fragments f = 4q + w; with NT % 4 == 0 its k-step (4q)/NT is static
-    uint32_t woff[WLOADS];
-#pragma unroll
-    for (int q = 0; q < WLOADS; ++q) {
-        const int nt = (4 * q) % NT + wave;   // its k-step is added per stage (kadd)
-        woff[q] = col_ok(nt) ? static_cast<uint32_t>(((static_cast<size_t>(col_of(nt)) + (lane & 15)) * p.K +
-                                                     8 * (lane >> 4)) * 2)
-                             : kOobRow;
-    }
-    const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, static_cast<uint32_t>(static_cast<size_t>(p.a_row_limit) * p.lda * 2));
 
-    {
-        const int mrows = min(MP, M - m0);
-        const int mtiles = __builtin_amdgcn_readfirstlane((mrows + 15) >> 4);
-        uint32_t aoff[MTW];
+    // ---- weight loads: load q of this lane covers weight row r = (q*4 + wave)*2 + lane/32
+    // (of the tile's WROWS rows) and 16-byte chunk lane%32 of the stage's 512 bytes
+    const __amdgpu_buffer_rsrc_t rW = make_rsrc(p.W, static_cast<uint32_t>(static_cast<size_t>(p.Nout) * p.K * 2));
+    const int wchunk = lane & 31;
+    uint32_t wrow_off[WLD];
+    uint32_t wlds[WLD];
 #pragma unroll
-        for (int i = 0; i < MTW; ++i) {
-            const int m = (wave + 4 * i) * 16 + (lane & 15);
-            uint32_t o = kOobRow;
-            if (m < mrows) {
-                const int src = fused ? s_rows[m0 + m] : (p.a_rows ? p.a_rows[m0 + m] : m0 + m);
-                if (src >= 0 && src < p.a_row_limit)
-                    o = static_cast<uint32_t>((static_cast<size_t>(src) * p.lda + 8 * (lane >> 4)) * 2);
+    for (int q = 0; q < WLD; ++q) {
+        const int r = (q * 4 + wave) * 2 + (lane >> 5);
+        const int nt = r >> 4, rr = r & 15;
+        wrow_off[q] = col_ok(nt) ? static_cast<uint32_t>((static_cast<size_t>(col_of(nt)) + rr) * p.K * 2) : kOobRow;
+        wlds[q] = static_cast<uint32_t>(r * 512 + ((wchunk ^ rr) << 4));   // swizzled LDS slot
+    }
+    auto load_w = [&](int st, uint4 (&w)[WLD]) {
+        const int k = k_begin + st * kStageK + wchunk * 8;
+        const uint32_t kb = k < k_end ? static_cast<uint32_t>(k * 2) : kOobK;
+#pragma unroll
+        for (int q = 0; q < WLD; ++q) w[q] = buf_load16(rW, wrow_off[q] + kb);
+    };
+    auto store_w = [&](int buf, const uint4 (&w)[WLD]) {
+        uint8_t* b = smem + buf * WBUF;
+#pragma unroll
+        for (int q = 0; q < WLD; ++q) *reinterpret_cast<uint4*>(b + wlds[q]) = w[q];
+    };
+
+    // ---- activation loads: tile i of this wave = rows m0 + (wave + 4i)*16 + lane%16; k-step s of
+    // a stage reads logical chunk 4s + lane/16 (8 bf16) -- the MFMA B operand
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, static_cast<uint32_t>(static_cast<size_t>(p.a_row_limit) * p.lda * 2));
+    uint32_t arow_off[MTW];
+#pragma unroll
+    for (int i = 0; i < MTW; ++i) {
+        const int m = (wave + 4 * i) * 16 + (lane & 15);
+        uint32_t o = kOobRow;
+        if (m < mrows) {
+            const int src = fused ? s_rows[m0 + m] : (p.a_rows ? p.a_rows[m0 + m] : m0 + m);
+            if (src >= 0 && src < p.a_row_limit) o = static_cast<uint32_t>(static_cast<size_t>(src) * p.lda * 2);
+        }
+        arow_off[i] = o;
+    }
+
+    // the stage loop, specialised on this wave's number of active row tiles (no branch sits
+    // between the MFMAs) and unrolled by two for the register double buffers
+    auto run = [&](auto nact_c) {
+        constexpr int NACT = decltype(nact_c)::value;
+        constexpr int NA = NACT > 0 ? NACT : 1;
+        f32x4 acc[NA][NT];
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) acc[i][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        uint4 w0[WLD], w1[WLD];
+        uint4 a0[NA][8], a1[NA][8];
+
+        auto load_a = [&](int st, uint4 (&a)[NA][8]) {
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const int k = k_begin + st * kStageK + (4 * s + (lane >> 4)) * 8;
+                const uint32_t kb = k < k_end ? static_cast<uint32_t>(k * 2) : kOobK;
+#pragma unroll
+                for (int i = 0; i < NACT; ++i) a[i][s] = buf_load16(rA, arow_off[i] + kb);
             }
-            aoff[i] = o;
+        };
+        auto compute = [&](int buf, const uint4 (&a)[NA][8]) {
+            const uint8_t* b = smem + buf * WBUF;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                uint4 wf[NT];
+                const int c = 4 * s + (lane >> 4);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const int r = nt * 16 + (lane & 15);
+                    wf[nt] = *reinterpret_cast<const uint4*>(b + r * 512 + ((c ^ (lane & 15)) << 4));
+                }
+#pragma unroll
+                for (int i = 0; i < NACT; ++i)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) acc[i][nt] = mfma16x16x32(wf[nt], a[i][s], acc[i][nt]);
+            }
+        };
+
+        // stage it: W(it) in registers -> LDS buffer it%2 while W(it+1), A(it+1) are in flight
+        load_w(0, w0);
+        load_a(0, a0);
+        load_w(1, w1);
+        for (int it = 0; it < nstages; it += 2) {
+            store_w(0, w0);
+            block_barrier();
+            load_w(it + 2, w0);
+            load_a(it + 1, a1);
+            compute(0, a0);
+
+            store_w(1, w1);
+            block_barrier();
+            load_w(it + 3, w1);
+            load_a(it + 2, a0);
+            compute(1, a1);
         }
 
-        auto issue = [&](int stage, int kstage) {
-            uint8_t* sb = smem + stage * STAGE;
+        // epilogue: lane holds C[row m][cols col + 4*(lane>>4) + q]
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const int ks = ks0 + kstage * KS + s;
-                const uint32_t kadd = ks < ks1 ? static_cast<uint32_t>(ks * 64) : kOobK;
+        for (int i = 0; i < NACT; ++i) {
+            const int m = (wave + 4 * i) * 16 + (lane & 15);
+            if (m >= mrows) continue;
+            if (EPI == EPI_SWIGLU) {
 #pragma unroll
-                for (int q = 0; q < WLOADS; ++q)
-                    if ((4 * q) / NT == s) lds_dma16(rW, sb + (4 * q + wave) * 1024, woff[q] + kadd);
+                for (int nt = 0; nt < NT / 2; ++nt) {
+                    if (!col_ok(nt)) continue;
+                    float o[4];
 #pragma unroll
-                for (int i = 0; i < MTW; ++i)
-                    lds_dma16(rA, sb + (W_FR + (wave * MTW + i) * KS + s) * 1024, aoff[i] + kadd);
-            }
-        };
-
-#pragma unroll
-        for (int st = 0; st < ST - 1; ++st) issue(st, st);
-
-        // the k-loop, specialised on this wave's number of active row tiles so no branch sits
-        // between the MFMAs and the accumulators stay in place across iterations
-        auto kloop = [&](auto nact_c) {
-            constexpr int NACT = decltype(nact_c)::value;
-            constexpr int NA = NACT > 0 ? NACT : 1;
-            f32x4 acc[NA][NT];
-#pragma unroll
-            for (int i = 0; i < NA; ++i)
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) acc[i][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (int it = 0; it < nstages; ++it) {
-                wait_vmcnt<(ST - 2) * LPS>();
-                block_barrier();
-                const int nxt = it + ST - 1;
-                issue(nxt % ST, nxt);
-                const uint8_t* sb = smem + (it % ST) * STAGE;
-#pragma unroll
-                for (int s = 0; s < KS; ++s) {
-                    u32x4 fr[NT + (NACT > 0 ? NACT : 1)];
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) fr[nt] = lds_read16(sb + (s * NT + nt) * 1024 + lane * 16);
-#pragma unroll
-                    for (int i = 0; i < NACT; ++i)
-                        fr[NT + i] = lds_read16(sb + (W_FR + (wave * MTW + i) * KS + s) * 1024 + lane * 16);
-                    if (NACT == 0) fr[NT] = u32x4{0u, 0u, 0u, 0u};
-                    lds_wait(fr);
-#pragma unroll
-                    for (int i = 0; i < NACT; ++i) {
-                        const uint4 a = as_uint4(fr[NT + i]);
-#pragma unroll
-                        for (int nt = 0; nt < NT; ++nt)
-                            acc[i][nt] = mfma16x16x32(as_uint4(fr[nt]), a, acc[i][nt]);
+                    for (int q = 0; q < 4; ++q) {
+                        const float g = acc[i][nt][q], u = acc[i][nt + NT / 2][q];
+                        o[q] = g / (1.0f + expf(-g)) * u;
                     }
+                    *reinterpret_cast<uint2*>(p.act + static_cast<size_t>(m0 + m) * p.F + col_of(nt) + 4 * (lane >> 4)) =
+                        make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
                 }
+            } else {
+                float* dst = p.partial + (static_cast<size_t>(y) * p.m_cap + m0 + m) * p.Nout + 4 * (lane >> 4);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    if (col_ok(nt)) *reinterpret_cast<f32x4*>(dst + col_of(nt)) = acc[i][nt];
             }
-            wait_vmcnt<0>();
-            block_barrier();
-
-            // epilogue: lane holds C[row m][cols col + 4*(lane>>4) + q]
-#pragma unroll
-            for (int i = 0; i < NACT; ++i) {
-                const int m = (wave + 4 * i) * 16 + (lane & 15);
-                if (m >= mrows) continue;
-                if (EPI == EPI_SWIGLU) {
-#pragma unroll
-                    for (int nt = 0; nt < NT / 2; ++nt) {
-                        if (!col_ok(nt)) continue;
-                        float o[4];
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const float g = acc[i][nt][q], u = acc[i][nt + NT / 2][q];
-                            o[q] = g / (1.0f + expf(-g)) * u;
-                        }
-                        *reinterpret_cast<uint2*>(p.act + static_cast<size_t>(m0 + m) * p.F + col_of(nt) + 4 * (lane >> 4)) =
-                            make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-                    }
-                } else {
-                    float* dst = p.partial + (static_cast<size_t>(y) * p.m_cap + m0 + m) * p.Nout + 4 * (lane >> 4);
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-                        if (col_ok(nt)) *reinterpret_cast<f32x4*>(dst + col_of(nt)) = acc[i][nt];
-                }
-            }
-        };
-        // active tiles of this wave: i with wave + 4 i < mtiles
-        const int nact = mtiles > wave ? min(MTW, (mtiles - wave + 3) >> 2) : 0;
-        dispatch_count<MTW>(nact, kloop);
-    }
+        }
+    };
+    // active tiles of this wave: i with wave + 4 i < mtiles
+    const int nact = mtiles > wave ? min(MTW, (mtiles - wave + 3) >> 2) : 0;
+    dispatch_count<MTW>(nact, run);
 }
 
-// Kernel shapes: NT column tiles per workgroup, MTW row tiles per wave (64*MTW rows per
-// workgroup), KS k-steps per stage, ST stages.  LDS = ST*(KS*NT + 4*MTW*KS) KB + the row list.
-template <int NT, int MTW, int KS, int ST, int EPI>
+template <int NT, int MTW, int EPI>
 hipError_t launch_shape(GemmArgs a, int n_tiles, int splits, hipStream_t st) {
-    constexpr int STAGE = (KS * NT + 4 * MTW * KS) * 1024;
     constexpr int MP = 64 * MTW;
     a.n_tiles = n_tiles;
     a.m_chunks = (a.m_cap + MP - 1) / MP;
     if (a.m_chunks < 1) a.m_chunks = 1;
-    const size_t lds = static_cast<size_t>(ST) * STAGE + (a.fc_fold ? static_cast<size_t>(a.fc_R) * 4 : 0);
-    auto kern = gemm_kernel<NT, MTW, KS, ST, EPI>;
+    const size_t lds = 2 * static_cast<size_t>(16 * NT * 512) + (a.fc_fold ? static_cast<size_t>(a.fc_R) * 4 : 0);
+    auto kern = gemm_kernel<NT, MTW, EPI>;
     static size_t configured = 0;   // dynamic-LDS cap raised so far for this kernel
     if (lds > configured) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -340,15 +323,15 @@ hipError_t launch_shape(GemmArgs a, int n_tiles, int splits, hipStream_t st) {
 
 template <int EPI>
 hipError_t launch_cfg(const GemmArgs& a, int nt, int n_cols, int splits, int max_rows, hipStream_t st) {
-    // n_cols: output columns one tile of 16*NT weight rows stands for (SwiGLU pairs gate + up)
+    // a tile of 16*NT weight rows covers 16*NT output columns (SwiGLU: 8*NT gate + 8*NT up rows)
+    const int per = (EPI == EPI_SWIGLU ? 8 : 16) * nt;
+    const int tiles = (n_cols + per - 1) / per;
     if (nt == 8) {
-        const int tiles = (n_cols + (EPI == EPI_SWIGLU ? 64 : 128) - 1) / (EPI == EPI_SWIGLU ? 64 : 128);
-        if (max_rows <= 64) return launch_shape<8, 1, 2, 6, EPI>(a, tiles, splits, st);    // 6 x 24 KB
-        return launch_shape<8, 2, 2, 4, EPI>(a, tiles, splits, st);                        // 4 x 32 KB
+        if (max_rows <= 64) return launch_shape<8, 1, EPI>(a, tiles, splits, st);
+        return launch_shape<8, 2, EPI>(a, tiles, splits, st);
     }
-    const int tiles = (n_cols + (EPI == EPI_SWIGLU ? 32 : 64) - 1) / (EPI == EPI_SWIGLU ? 32 : 64);
-    if (max_rows <= 64) return launch_shape<4, 1, 2, 8, EPI>(a, tiles, splits, st);        // 8 x 16 KB
-    return launch_shape<4, 2, 2, 5, EPI>(a, tiles, splits, st);                            // 5 x 24 KB
+    if (max_rows <= 64) return launch_shape<4, 1, EPI>(a, tiles, splits, st);
+    return launch_shape<4, 2, EPI>(a, tiles, splits, st);
 }
 
 }  // namespace
