@@ -24,7 +24,7 @@ struct Dims {
 };
 
 struct Layout {
-    int nt_qkv, nt_o, nt_gu, nt_down;
+    GemmCfg c_qkv, c_o, c_gu, c_down;
     size_t rho, fold, inv_rms, rec_rows, rec_count, branch_off, row_slot, src_branch, src_slot;
     size_t xn1, xn2, q_c, k_c, v_c, attn, h_mid, act, gemm_part, attn_o, attn_ml;
     size_t total;
@@ -42,24 +42,37 @@ Dims dims_of(const specfold_shape& s) {
     return d;
 }
 
-// K-split count of a partial-sum projection: enough workgroups (>= ~256) to spread the weight
-// stream over the 256 CUs, while every split keeps at least 8 32-wide k-steps.
-int pick_splits(int nout, int k, int nt) {
-    const int groups = (nout + 16 * nt - 1) / (16 * nt);
-    const int nks = k / 32;
-    int s = (256 + groups - 1) / groups;
-    const int cap = nks / 8 > 1 ? nks / 8 : 1;
-    if (s > cap) s = cap;
-    if (s < 1) s = 1;
-    return s;
+// Tile shape, column groups and K split of one projection.  A workgroup streams 64 weight
+// rows (32 output columns of SwiGLU) against 128 activation rows (64 when R <= 64) through a
+// three-slot LDS ring, so two workgroups share a CU and hide each other's waits.  Partial-sum
+// projections split K until about 384 workgroups are busy (at least 4 stages of 64 per split).
+GemmCfg pick_gemm(int n_cols, int k, int max_rows, int busy_chunks, bool swiglu) {
+    GemmCfg c{};
+    c.swiglu = swiglu;
+    c.ntw = 4; c.wn = 1; c.tm = 2; c.nb = 3;
+    if (max_rows <= 64) { c.ntw = 2; c.wn = 2; c.tm = 2; c.nb = 3; }
+    const int cap = gemm_group_cols(c);
+    c.groups = (n_cols + cap - 1) / cap;
+    c.splits = 1;
+    if (!swiglu) {
+        const int busy = c.groups * (busy_chunks > 0 ? busy_chunks : 1);
+        int s = (384 + busy / 2) / busy;
+        const int smax = (k + 63) / 64 / 4;
+        if (s > smax) s = smax;
+        c.splits = s < 1 ? 1 : s;
+    }
+    return c;
 }
 
 Layout layout_of(const Dims& d) {
     Layout L;
-    L.nt_qkv = 4; L.nt_o = 4; L.nt_gu = 8; L.nt_down = 4;
-    L.s_qkv = pick_splits(d.Nq, d.D, L.nt_qkv);
-    L.s_o = pick_splits(d.D, d.Do, L.nt_o);
-    L.s_down = pick_splits(d.D, d.F, L.nt_down);
+    // the recompute projections expect one busy row chunk (folded M); o_proj has all R rows
+    L.c_qkv = pick_gemm(d.Nq, d.D, d.R, 1, false);
+    const int o_chunks = (d.R + gemm_chunk_rows(L.c_qkv) - 1) / gemm_chunk_rows(L.c_qkv);
+    L.c_o = pick_gemm(d.D, d.Do, d.R, o_chunks, false);
+    L.c_gu = pick_gemm(d.F, d.D, d.R, 1, true);
+    L.c_down = pick_gemm(d.D, d.F, d.R, 1, false);
+    L.s_qkv = L.c_qkv.splits; L.s_o = L.c_o.splits; L.s_down = L.c_down.splits;
     L.chunk_len = d.P <= 1024 ? 256 : 512;
     L.n_chunks = d.P > 0 ? (d.P + L.chunk_len - 1) / L.chunk_len : 0;
     const size_t R = static_cast<size_t>(d.R);
@@ -222,7 +235,7 @@ hipError_t run_qkv(const Dims& d, const Layout& L, const uint16_t* xn, const int
     g.m_cap = d.R; g.W = w_qkv; g.K = d.D; g.Nout = d.Nq;
     g.partial = at<float>(ws, L.gemm_part);
     if (tr) tr->begin();
-    hipError_t e = launch_gemm_partial(g, L.s_qkv, d.R, L.nt_qkv, st);
+    hipError_t e = launch_gemm(g, L.c_qkv, st);
     if (tr) tr->end();
     if (e != hipSuccess) return e;
     QkvEpiArgs q{};
@@ -271,7 +284,7 @@ hipError_t run_out_proj(const Dims& d, const Layout& L, const uint16_t* attn, co
     g.m_fixed = d.R; g.m_cap = d.R; g.W = w_o; g.K = d.Do; g.Nout = d.D;
     g.partial = at<float>(ws, L.gemm_part);
     if (tr) tr->begin();
-    hipError_t e = launch_gemm_partial(g, L.s_o, d.R, L.nt_o, st);
+    hipError_t e = launch_gemm(g, L.c_o, st);
     if (tr) tr->end();
     if (e != hipSuccess) return e;
     if (tr) tr->begin();
@@ -290,7 +303,7 @@ hipError_t run_ffn(const Dims& d, const Layout& L, const uint16_t* xn2, const ui
     g.m_cap = d.R; g.W = w_gate_up; g.K = d.D; g.Nout = 2 * d.F;
     g.act = at<uint16_t>(ws, L.act); g.F = d.F;
     if (tr) tr->begin();
-    hipError_t e = launch_gemm_swiglu(g, d.R, L.nt_gu, st);
+    hipError_t e = launch_gemm(g, L.c_gu, st);
     if (tr) tr->end();
     if (e != hipSuccess) return e;
     GemmArgs h{};
@@ -298,7 +311,7 @@ hipError_t run_ffn(const Dims& d, const Layout& L, const uint16_t* xn2, const ui
     h.m_cap = d.R; h.W = w_down; h.K = d.F; h.Nout = d.D;
     h.partial = at<float>(ws, L.gemm_part);
     if (tr) tr->begin();
-    e = launch_gemm_partial(h, L.s_down, d.R, L.nt_down, st);
+    e = launch_gemm(h, L.c_down, st);
     if (tr) tr->end();
     if (e != hipSuccess) return e;
     if (tr) tr->begin();

@@ -1,69 +1,120 @@
 // Gathered-row bf16 GEMM on gfx950 MFMA: C[m][n] = sum_k A[row(m)][k] * W[n][k].
 //
 // The layer's projections are skinny: M (recompute rows, <= R = 288 at B = 8, N = 32) is small
-// and W [Nout][K] is large, so the kernel is built to stream W from HBM at full rate:
-//   * a 256-thread workgroup (4 waves) owns NT 16-row weight tiles (16*NT output columns), a
-//     chunk of 64*MTW activation rows and a range of K (grid.y splits K when the column tiles
-//     alone cannot fill the 256 CUs);
-//   * K advances in stages of 256: for its stage every wave loads 2 weight rows x 512 contiguous
-//     bytes per instruction (the access pattern HBM serves fastest), one stage ahead into
-//     registers, and writes them into LDS in an XOR-swizzled row-major layout, so the MFMA
-//     fragment reads (16 rows x 16 bytes per lane group) are conflict-free ds_read_b128;
-//   * each wave loads its own activation row tiles straight into registers in MFMA operand
-//     layout (they are L2-resident), double-buffered, so activations never touch LDS;
-//   * loads are branch-free: rows past M, column tiles past Nout and K past the split use
-//     out-of-range buffer offsets, which read as zeros without touching memory, and every wait
-//     is the compiler's own exact vmcnt;
-//   * v_mfma_f32_16x16x32_bf16 with a weight fragment as the A operand and 16 activation rows
-//     as the B operand leaves each lane 4 consecutive output columns of one row.
+// and W [Nout][K] is large, so the kernel is built to keep many bytes of W in flight:
+//   * a 256-thread workgroup owns 16*NT weight rows (output columns), a chunk of MP activation
+//     rows and a range of K (grid.y splits K when the column tiles alone cannot fill the CUs);
+//   * K advances in stages of 64 elements.  Both operands of a stage move HBM/L2 -> LDS with
+//     buffer_load ... lds (no register staging) into a ring of NB stage slots, so NB-1 stages
+//     are in flight while one is multiplied.  One such load moves 8 rows x 128 contiguous
+//     bytes: every 4-lane quad reads one 64-byte segment, the pattern the texture path serves
+//     at full rate (loads straight into MFMA operand layout would touch four rows per quad);
+//   * inside a slot, row r keeps its 16-byte chunk c at position c ^ (r & 7), so the MFMA
+//     fragment reads (16 rows x one chunk) are conflict-free ds_read_b128;
+//   * the four waves form a (NT/2) x (8/NT) grid over (weight tiles, row tiles); each wave
+//     multiplies two 16-row weight tiles with TM 16-row activation tiles per 32-wide k-step;
+//   * loads are branch-free: rows past M, weight rows past Nout and K past the matrix use
+//     out-of-range buffer offsets, which read as zeros without touching memory;
+//   * waits are explicit: the ring's loads write no registers and the fragment reads are
+//     inline asm, so the compiler inserts no conservative drains; each wave waits on vmcnt for
+//     exactly the stage it is about to read and on lgkmcnt for its fragments.
 // Rows come from an identity map, a device list, or -- fused -- from the fold flags: every
 // workgroup compacts them in LDS (ascending row order) and workgroup (0,0) also publishes the
 // recompute list, per-branch offsets, row -> slot map and fold sources
 // [SpecFold summary, App. B: compaction and source resolution feed the projection].
 // Epilogues: fp32 partial sums (reduced in a fixed order by the next kernel, so results are
-// deterministic), or SwiGLU for the FFN's gate/up projection, where gate tile t and up tile
-// t + NT/2 meet in the same lane.
-#include <type_traits>
-
+// deterministic), or SwiGLU for the FFN's gate/up projection, where a wave's two weight tiles
+// are the gate and up rows of the same 16 output columns.
 #include "kernels.h"
 
 namespace specfold {
 
 namespace {
 
-// Out-of-range offsets: a missing row / column tile adds kOobRow, K past the split adds kOobK.
-// Buffers are < 1 GB (checked by the host), so any sum involving either is out of range and the
-// two never wrap back into range together.
+// Out-of-range offsets: a missing row adds kOobRow, K past the matrix adds kOobK.  Buffers are
+// < 1 GB (checked by the host), so any sum involving either is out of range and the two never
+// wrap back into range together.
 constexpr uint32_t kOobRow = 0x40000000u;
 constexpr uint32_t kOobK = 0x80000000u;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
-constexpr int kStageK = 256;                // K elements per stage (512 bytes of a bf16 row)
+constexpr int kStageK = 64;                 // K elements per stage
+constexpr int kRowB = 128;                  // bytes of one row in one stage
 
 enum { EPI_PARTIAL = 0, EPI_SWIGLU = 1 };
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
 }
 
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+// 16 bytes per lane, global -> LDS: lane l's bytes land at lds + 16 l (lds is wave-uniform)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds), 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_u8*)(p)));
+}
+
+// ds_read_b128 as inline asm: the compiler cannot see these reads, so it neither drains the
+// ring's loads before them nor waits for their results; lds_wait<N>() supplies that wait
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+
+// wait until at most N of this wave's LDS reads are outstanding, then pin the fragments after
+// the wait (the empty asm "modifies" them, so no use can be scheduled above it)
+template <int N, int C>
+__device__ __forceinline__ void lds_wait(u32x4 (&v)[C]) {
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(N) : "memory");
+#pragma unroll
+    for (int i = 0; i < C; ++i) asm volatile("" : "+v"(v[i]));
+}
+
+// fragments of N consecutive 16-row tiles (rows 16 apart) at addr
+template <int N, int I = 0>
+__device__ __forceinline__ void read_tiles(u32x4* f, uint32_t addr) {
+    if constexpr (I < N) {
+        f[I] = lds_read16<I * 16 * kRowB>(addr);
+        read_tiles<N, I + 1>(f, addr);
+    }
+}
+
+// wait until at most N of this wave's vector-memory operations are outstanding
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// vm_wait<QW * n> for a runtime n in [0, MAXN]
+template <int QW, int MAXN>
+__device__ __forceinline__ void vm_wait_stages(int n) {
+    if constexpr (MAXN <= 0) {
+        vm_wait<0>();
+    } else {
+        if (n >= MAXN) vm_wait<QW * MAXN>();
+        else vm_wait_stages<QW, MAXN - 1>(n);
+    }
+}
+
+__device__ __forceinline__ f32x4 mma(const u32x4& w, const u32x4& a, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), __builtin_bit_cast(bf16x8, a), c,
+                                                   0, 0, 0);
 }
 
 __device__ __forceinline__ void block_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-}
-
-// call f(std::integral_constant<int, n>) for a runtime n in [0, MAX]
-template <int MAX, int N = 0, typename F>
-__device__ __forceinline__ void dispatch_count(int n, F&& f) {
-    if constexpr (N < MAX) {
-        if (n == N) f(std::integral_constant<int, N>{});
-        else dispatch_count<MAX, N + 1>(n, f);
-    } else {
-        f(std::integral_constant<int, MAX>{});
-    }
 }
 
 // Compact the recompute rows (fold == 0) of R rows into s_rows (ascending), 256 threads.
@@ -119,196 +170,193 @@ __device__ int compact_in_lds(const GemmArgs& p, int32_t* s_rows, int* s_tot, bo
     return base;
 }
 
-template <int NT, int MTW, int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmArgs p) {
-    constexpr int WROWS = 16 * NT;                 // weight rows per workgroup
-    constexpr int WBUF = WROWS * 512;              // LDS bytes of one weight stage
-    constexpr int WLD = WROWS / 8;                 // 16-byte weight loads per lane per stage
-    constexpr int MP = 64 * MTW;                   // activation rows per workgroup
-    static_assert(NT % 2 == 0 && WLD >= 1, "tile shape");
+// Tile shape: WN x WM waves; each wave owns NTW 16-row weight tiles and TM 16-row activation
+// tiles; NB stage slots in the ring.
+template <int NTW, int WN, int TM, int NB>
+struct Tile {
+    static constexpr int WM = 4 / WN;              // waves along the row tiles
+    static constexpr int NT = NTW * WN;            // weight tiles per workgroup
+    static constexpr int WROWS = 16 * NT;          // weight rows per workgroup
+    static constexpr int MP = 16 * TM * WM;        // activation rows per workgroup
+    static constexpr int QWW = WROWS / 32;         // ring loads per wave per stage: weights
+    static constexpr int QW = (WROWS + MP) / 32;   //   ... weights + activations
+    static constexpr int SLOT = (WROWS + MP) * kRowB;
+    static constexpr int LDS = NB * SLOT;
+    static_assert(WN == 1 || WN == 2 || WN == 4, "wave grid");
+    static_assert(WROWS % 32 == 0 && MP % 32 == 0, "ring loads cover 8 rows per wave");
+    static_assert(TM >= 1 && NTW >= 1 && NTW * TM <= 16, "accumulators per wave");
+    static_assert(NB >= 2 && QW * (NB - 2) < 64, "ring depth");
+};
+
+template <int NTW, int WN, int TM, int NB, int EPI>
+__global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
+    using T = Tile<NTW, WN, TM, NB>;
+    constexpr int WROWS = T::WROWS, MP = T::MP, QWW = T::QWW, QW = T::QW, SLOT = T::SLOT;
+    static_assert(EPI != EPI_SWIGLU || NTW % 2 == 0, "SwiGLU tiles come in gate/up pairs");
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ int s_tot[4];
-    int32_t* s_rows = reinterpret_cast<int32_t*>(smem + 2 * WBUF);
+    int32_t* s_rows = reinterpret_cast<int32_t*>(smem + T::LDS);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
     const int y = blockIdx.y, S = gridDim.y;
-    // blockIdx.x -> (column tile, row chunk).  Consecutive workgroup ids go round-robin over the
-    // 8 XCDs, so the chunks of one tile get ids that share id % 8 and sit within 8*C of each
-    // other: they run on one XCD at about the same time and the tile's weights come from that
-    // XCD's L2 after the first chunk fetched them.
+    // blockIdx.x -> (column group, row chunk).  Consecutive workgroup ids go round-robin over
+    // the 8 XCDs, so the chunks of one group get ids that share id % 8 and sit within 8*C of
+    // each other: they run on one XCD at about the same time and the group's weights come from
+    // that XCD's L2 after the first chunk fetched them.
     const int C = p.m_chunks;
     const int id = blockIdx.x, grp = id / (8 * C), rem = id - grp * 8 * C;
-    const int chunk = rem >> 3, tile = grp * 8 + (rem & 7);
+    const int chunk = rem >> 3, g = grp * 8 + (rem & 7);
 
     int M;
     const bool fused = p.fc_fold != nullptr;
     if (fused) {
-        M = compact_in_lds(p, s_rows, s_tot, blockIdx.x == 0 && blockIdx.y == 0);   // (tile 0, chunk 0)
+        M = compact_in_lds(p, s_rows, s_tot, blockIdx.x == 0 && blockIdx.y == 0);   // (group 0, chunk 0)
     } else {
         M = p.m_count ? p.m_count[0] : p.m_fixed;
     }
     M = M < 0 ? 0 : (M > p.m_cap ? p.m_cap : M);
     M = __builtin_amdgcn_readfirstlane(M);
     const int m0 = chunk * MP;
-    if (tile >= p.n_tiles || m0 >= M) return;     // uniform: nothing for this workgroup
+    if (g >= p.n_groups || m0 >= M) return;       // uniform: nothing for this workgroup
     const int mrows = min(MP, M - m0);
-    const int mtiles = __builtin_amdgcn_readfirstlane((mrows + 15) >> 4);
 
-    // K range of this split (in 32-wide k-steps) and its stages of 256
-    const int nks = p.K / 32;
-    const int k_begin = static_cast<int>(static_cast<int64_t>(y) * nks / S) * 32;
-    const int k_end = static_cast<int>(static_cast<int64_t>(y + 1) * nks / S) * 32;
-    const int nstages = (k_end - k_begin + kStageK - 1) / kStageK;
+    // output columns [c0, c1) of this group: the columns spread evenly over the groups, in
+    // multiples of 4 (a lane stores 4 consecutive columns)
+    const int ncols = EPI == EPI_SWIGLU ? p.F : p.Nout;
+    const int c0 = static_cast<int>(static_cast<int64_t>(g) * (ncols / 4) / p.n_groups) * 4;
+    const int c1 = static_cast<int>(static_cast<int64_t>(g + 1) * (ncols / 4) / p.n_groups) * 4;
 
-    auto col_of = [&](int nt) -> int {             // first output column of N-tile nt
+    // K range of this split, in whole stages
+    const int nst_all = (p.K + kStageK - 1) / kStageK;
+    const int st_begin = static_cast<int>(static_cast<int64_t>(y) * nst_all / S);
+    const int nst = static_cast<int>(static_cast<int64_t>(y + 1) * nst_all / S) - st_begin;
+
+    // weight row of slot row r (r < WROWS), or -1 past the group.  SwiGLU slots interleave
+    // [gate 16 | up 16] pairs, so a wave's tile pair holds the gate and up rows of 16 columns.
+    auto w_row = [&](int r) -> int {
         if (EPI == EPI_SWIGLU) {
-            const int j0 = tile * (NT / 2) * 16;
-            return nt < NT / 2 ? j0 + nt * 16 : p.F + j0 + (nt - NT / 2) * 16;
+            const int col = c0 + (r >> 5) * 16 + (r & 15);
+            return col < c1 ? (((r >> 4) & 1) ? p.F + col : col) : -1;
         }
-        return (tile * NT + nt) * 16;
-    };
-    auto col_ok = [&](int nt) -> bool {
-        return EPI == EPI_SWIGLU ? (tile * (NT / 2) + (nt % (NT / 2))) * 16 < p.F : col_of(nt) < p.Nout;
+        const int col = c0 + r;
+        return col < c1 ? col : -1;
     };
 
-    // ---- weight loads: load q of this lane covers weight row r = (q*4 + wave)*2 + lane/32
-    // (of the tile's WROWS rows) and 16-byte chunk lane%32 of the stage's 512 bytes
+    // ---- ring loads: load q of this wave fills slot rows (q*4 + wave)*8 .. +8; lane l takes row
+    // (l >> 3) of those 8 and physical chunk l & 7, which holds logical chunk (l & 7) ^ (row & 7)
     const __amdgpu_buffer_rsrc_t rW = make_rsrc(p.W, static_cast<uint32_t>(static_cast<size_t>(p.Nout) * p.K * 2));
-    const int wchunk = lane & 31;
-    uint32_t wrow_off[WLD];
-    uint32_t wlds[WLD];
-#pragma unroll
-    for (int q = 0; q < WLD; ++q) {
-        const int r = (q * 4 + wave) * 2 + (lane >> 5);
-        const int nt = r >> 4, rr = r & 15;
-        wrow_off[q] = col_ok(nt) ? static_cast<uint32_t>((static_cast<size_t>(col_of(nt)) + rr) * p.K * 2) : kOobRow;
-        wlds[q] = static_cast<uint32_t>(r * 512 + ((wchunk ^ rr) << 4));   // swizzled LDS slot
-    }
-    auto load_w = [&](int st, uint4 (&w)[WLD]) {
-        const int k = k_begin + st * kStageK + wchunk * 8;
-        const uint32_t kb = k < k_end ? static_cast<uint32_t>(k * 2) : kOobK;
-#pragma unroll
-        for (int q = 0; q < WLD; ++q) w[q] = buf_load16(rW, wrow_off[q] + kb);
-    };
-    auto store_w = [&](int buf, const uint4 (&w)[WLD]) {
-        uint8_t* b = smem + buf * WBUF;
-#pragma unroll
-        for (int q = 0; q < WLD; ++q) *reinterpret_cast<uint4*>(b + wlds[q]) = w[q];
-    };
-
-    // ---- activation loads: tile i of this wave = rows m0 + (wave + 4i)*16 + lane%16; k-step s of
-    // a stage reads logical chunk 4s + lane/16 (8 bf16) -- the MFMA B operand
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, static_cast<uint32_t>(static_cast<size_t>(p.a_row_limit) * p.lda * 2));
-    uint32_t arow_off[MTW];
+    const int lchunk = (lane & 7) ^ ((lane >> 3) & 7);
+    uint32_t roff[QW];
 #pragma unroll
-    for (int i = 0; i < MTW; ++i) {
-        const int m = (wave + 4 * i) * 16 + (lane & 15);
+    for (int q = 0; q < QW; ++q) {
+        const int r = (q * 4 + wave) * 8 + (lane >> 3);
         uint32_t o = kOobRow;
-        if (m < mrows) {
-            const int src = fused ? s_rows[m0 + m] : (p.a_rows ? p.a_rows[m0 + m] : m0 + m);
-            if (src >= 0 && src < p.a_row_limit) o = static_cast<uint32_t>(static_cast<size_t>(src) * p.lda * 2);
+        if (q < QWW) {
+            const int gr = w_row(r);
+            if (gr >= 0) o = static_cast<uint32_t>(static_cast<size_t>(gr) * p.K * 2);
+        } else {
+            const int m = r - WROWS;
+            if (m < mrows) {
+                const int src = fused ? s_rows[m0 + m] : (p.a_rows ? p.a_rows[m0 + m] : m0 + m);
+                if (src >= 0 && src < p.a_row_limit) o = static_cast<uint32_t>(static_cast<size_t>(src) * p.lda * 2);
+            }
         }
-        arow_off[i] = o;
+        roff[q] = o + static_cast<uint32_t>(lchunk * 16);
+    }
+    auto issue = [&](int s) {                      // stage s of this split -> slot s % NB
+        uint8_t* slot = smem + (s % NB) * SLOT;
+        const int k0 = (st_begin + s) * kStageK;
+        const uint32_t kb = k0 + lchunk * 8 < p.K ? static_cast<uint32_t>(k0 * 2) : kOobK;
+#pragma unroll
+        for (int q = 0; q < QW; ++q) dma16(q < QWW ? rW : rA, slot + (q * 4 + wave) * 1024, roff[q] + kb);
+    };
+
+    // ---- fragment reads: lane reads row (lane & 15) of a 16-row tile, logical chunk
+    // 4t + (lane >> 4) in k-step t, which sits at physical chunk (that ^ (row & 7))
+    const int wn = wave % WN, wm = wave / WN;
+    const int fr = lane & 15, fc = lane >> 4;
+    const uint32_t lb0 = lds_addr(smem) + fr * kRowB + ((fc ^ (fr & 7)) << 4);
+    const uint32_t lb1 = lds_addr(smem) + fr * kRowB + (((4 + fc) ^ (fr & 7)) << 4);
+    f32x4 acc[TM][NTW];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int b) {
+        const uint32_t sw = static_cast<uint32_t>(b * SLOT + wn * NTW * 16 * kRowB);
+        const uint32_t sa = static_cast<uint32_t>(b * SLOT + (WROWS + wm * TM * 16) * kRowB);
+        u32x4 f0[NTW + TM], f1[NTW + TM];
+        // k-step 0 fragments, then k-step 1: lgkmcnt(NTW + TM) leaves only the second group pending
+        read_tiles<NTW>(f0, lb0 + sw);
+        read_tiles<TM>(f0 + NTW, lb0 + sa);
+        read_tiles<NTW>(f1, lb1 + sw);
+        read_tiles<TM>(f1 + NTW, lb1 + sa);
+        lds_wait<NTW + TM>(f0);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) acc[i][j] = mma(f0[j], f0[NTW + i], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);        // keep k-step 0's MFMAs ahead of the next wait
+        lds_wait<0>(f1);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) acc[i][j] = mma(f1[j], f1[NTW + i], acc[i][j]);
+    };
+
+    // ---- the ring: NB-1 stages in flight ahead of the one being multiplied
+#pragma unroll
+    for (int s = 0; s < NB - 1; ++s)
+        if (s < nst) issue(s);
+    for (int s = 0; s < nst; ++s) {
+        const int after = min(NB - 2, nst - 1 - s);   // stages this wave issued after s
+        vm_wait_stages<QW, NB - 2>(after);
+        block_barrier();                              // stage s landed for every wave; slot of s-1 free
+        if (s + NB - 1 < nst) issue(s + NB - 1);
+        compute(s % NB);
     }
 
-    // the stage loop, specialised on this wave's number of active row tiles (no branch sits
-    // between the MFMAs) and unrolled by two for the register double buffers
-    auto run = [&](auto nact_c) {
-        constexpr int NACT = decltype(nact_c)::value;
-        constexpr int NA = NACT > 0 ? NACT : 1;
-        f32x4 acc[NA][NT];
+    // ---- epilogue: lane holds C[row m][cols n0 + 4*(lane>>4) + q] of tile (i, j)
 #pragma unroll
-        for (int i = 0; i < NA; ++i)
+    for (int i = 0; i < TM; ++i) {
+        const int m = (wm * TM + i) * 16 + (lane & 15);
+        if (m >= mrows) continue;
+        if (EPI == EPI_SWIGLU) {
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) acc[i][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        uint4 w0[WLD], w1[WLD];
-        uint4 a0[NA][8], a1[NA][8];
-
-        auto load_a = [&](int st, uint4 (&a)[NA][8]) {
+            for (int j = 0; j < NTW; j += 2) {
+                const int col = c0 + (wn * (NTW / 2) + j / 2) * 16 + 4 * (lane >> 4);
+                if (col >= c1) continue;
+                float o[4];
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const int k = k_begin + st * kStageK + (4 * s + (lane >> 4)) * 8;
-                const uint32_t kb = k < k_end ? static_cast<uint32_t>(k * 2) : kOobK;
-#pragma unroll
-                for (int i = 0; i < NACT; ++i) a[i][s] = buf_load16(rA, arow_off[i] + kb);
-            }
-        };
-        auto compute = [&](int buf, const uint4 (&a)[NA][8]) {
-            const uint8_t* b = smem + buf * WBUF;
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                uint4 wf[NT];
-                const int c = 4 * s + (lane >> 4);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const int r = nt * 16 + (lane & 15);
-                    wf[nt] = *reinterpret_cast<const uint4*>(b + r * 512 + ((c ^ (lane & 15)) << 4));
+                for (int q = 0; q < 4; ++q) {
+                    const float gt = acc[i][j][q], up = acc[i][j + 1][q];
+                    o[q] = gt / (1.0f + expf(-gt)) * up;
                 }
-#pragma unroll
-                for (int i = 0; i < NACT; ++i)
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) acc[i][nt] = mfma16x16x32(wf[nt], a[i][s], acc[i][nt]);
+                *reinterpret_cast<uint2*>(p.act + static_cast<size_t>(m0 + m) * p.F + col) =
+                    make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
             }
-        };
-
-        // stage it: W(it) in registers -> LDS buffer it%2 while W(it+1), A(it+1) are in flight
-        load_w(0, w0);
-        load_a(0, a0);
-        load_w(1, w1);
-        for (int it = 0; it < nstages; it += 2) {
-            store_w(0, w0);
-            block_barrier();
-            load_w(it + 2, w0);
-            load_a(it + 1, a1);
-            compute(0, a0);
-
-            store_w(1, w1);
-            block_barrier();
-            load_w(it + 3, w1);
-            load_a(it + 2, a0);
-            compute(1, a1);
-        }
-
-        // epilogue: lane holds C[row m][cols col + 4*(lane>>4) + q]
+        } else {
+            float* dst = p.partial + (static_cast<size_t>(y) * p.m_cap + m0 + m) * p.Nout + 4 * (lane >> 4);
 #pragma unroll
-        for (int i = 0; i < NACT; ++i) {
-            const int m = (wave + 4 * i) * 16 + (lane & 15);
-            if (m >= mrows) continue;
-            if (EPI == EPI_SWIGLU) {
-#pragma unroll
-                for (int nt = 0; nt < NT / 2; ++nt) {
-                    if (!col_ok(nt)) continue;
-                    float o[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float g = acc[i][nt][q], u = acc[i][nt + NT / 2][q];
-                        o[q] = g / (1.0f + expf(-g)) * u;
-                    }
-                    *reinterpret_cast<uint2*>(p.act + static_cast<size_t>(m0 + m) * p.F + col_of(nt) + 4 * (lane >> 4)) =
-                        make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-                }
-            } else {
-                float* dst = p.partial + (static_cast<size_t>(y) * p.m_cap + m0 + m) * p.Nout + 4 * (lane >> 4);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    if (col_ok(nt)) *reinterpret_cast<f32x4*>(dst + col_of(nt)) = acc[i][nt];
+            for (int j = 0; j < NTW; ++j) {
+                const int col = c0 + (wn * NTW + j) * 16;
+                if (col + 4 * (lane >> 4) < c1) *reinterpret_cast<f32x4*>(dst + col) = acc[i][j];
             }
         }
-    };
-    // active tiles of this wave: i with wave + 4 i < mtiles
-    const int nact = mtiles > wave ? min(MTW, (mtiles - wave + 3) >> 2) : 0;
-    dispatch_count<MTW>(nact, run);
+    }
 }
 
-template <int NT, int MTW, int EPI>
-hipError_t launch_shape(GemmArgs a, int n_tiles, int splits, hipStream_t st) {
-    constexpr int MP = 64 * MTW;
-    a.n_tiles = n_tiles;
-    a.m_chunks = (a.m_cap + MP - 1) / MP;
+template <int NTW, int WN, int TM, int NB, int EPI>
+hipError_t launch_shape(GemmArgs a, int groups, int splits, hipStream_t st) {
+    using T = Tile<NTW, WN, TM, NB>;
+    a.n_groups = groups;
+    a.m_chunks = (a.m_cap + T::MP - 1) / T::MP;
     if (a.m_chunks < 1) a.m_chunks = 1;
-    const size_t lds = 2 * static_cast<size_t>(16 * NT * 512) + (a.fc_fold ? static_cast<size_t>(a.fc_R) * 4 : 0);
-    auto kern = gemm_kernel<NT, MTW, EPI>;
+    const size_t lds = static_cast<size_t>(T::LDS) + (a.fc_fold ? static_cast<size_t>(a.fc_R) * 4 : 0);
+    auto kern = gemm_kernel<NTW, WN, TM, NB, EPI>;
     static size_t configured = 0;   // dynamic-LDS cap raised so far for this kernel
     if (lds > configured) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -316,32 +364,33 @@ hipError_t launch_shape(GemmArgs a, int n_tiles, int splits, hipStream_t st) {
         if (e != hipSuccess) return e;
         configured = lds;
     }
-    const dim3 grid(((n_tiles + 7) / 8) * 8 * a.m_chunks, splits);
+    const dim3 grid(((groups + 7) / 8) * 8 * a.m_chunks, splits);
     hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, a);
     return hipGetLastError();
 }
 
-template <int EPI>
-hipError_t launch_cfg(const GemmArgs& a, int nt, int n_cols, int splits, int max_rows, hipStream_t st) {
-    // a tile of 16*NT weight rows covers 16*NT output columns (SwiGLU: 8*NT gate + 8*NT up rows)
-    const int per = (EPI == EPI_SWIGLU ? 8 : 16) * nt;
-    const int tiles = (n_cols + per - 1) / per;
-    if (nt == 8) {
-        if (max_rows <= 64) return launch_shape<8, 1, EPI>(a, tiles, splits, st);
-        return launch_shape<8, 2, EPI>(a, tiles, splits, st);
-    }
-    if (max_rows <= 64) return launch_shape<4, 1, EPI>(a, tiles, splits, st);
-    return launch_shape<4, 2, EPI>(a, tiles, splits, st);
-}
-
 }  // namespace
 
-hipError_t launch_gemm_partial(const GemmArgs& a, int splits, int max_rows, int nt, hipStream_t st) {
-    return launch_cfg<EPI_PARTIAL>(a, nt, a.Nout, splits, max_rows, st);
+int gemm_chunk_rows(const GemmCfg& c) {
+    return 16 * c.tm * (4 / c.wn);
 }
 
-hipError_t launch_gemm_swiglu(const GemmArgs& a, int max_rows, int nt, hipStream_t st) {
-    return launch_cfg<EPI_SWIGLU>(a, nt, a.F, 1, max_rows, st);
+int gemm_group_cols(const GemmCfg& c) {
+    return (c.swiglu ? 8 : 16) * c.ntw * c.wn;
+}
+
+size_t gemm_lds_bytes(const GemmCfg& c) {
+    return static_cast<size_t>(c.nb) * (16 * c.ntw * c.wn + gemm_chunk_rows(c)) * kRowB;
+}
+
+hipError_t launch_gemm(const GemmArgs& a, const GemmCfg& c, hipStream_t st) {
+#define SPECFOLD_GEMM_CASE(NTW_, WN_, TM_, NB_)                                                 \
+    if (c.ntw == NTW_ && c.wn == WN_ && c.tm == TM_ && c.nb == NB_)                             \
+        return c.swiglu ? launch_shape<NTW_, WN_, TM_, NB_, EPI_SWIGLU>(a, c.groups, 1, st)     \
+                        : launch_shape<NTW_, WN_, TM_, NB_, EPI_PARTIAL>(a, c.groups, c.splits, st);
+    SPECFOLD_GEMM_CASES(SPECFOLD_GEMM_CASE)
+#undef SPECFOLD_GEMM_CASE
+    return hipErrorInvalidValue;
 }
 
 }  // namespace specfold

@@ -62,7 +62,7 @@ struct GemmArgs {
     int m_cap;               // M is clamped to [0, m_cap]; outputs have m_cap rows
     const uint16_t* W;       // [Nout][K]
     int K, Nout;
-    int n_tiles, m_chunks;   // set by the launcher
+    int n_groups, m_chunks;  // set by the launcher
     float* partial;          // [splits][m_cap][Nout]   (partial-sum epilogue)
     uint16_t* act;           // [m_cap][F]              (SwiGLU epilogue)
     int F;
@@ -81,11 +81,23 @@ struct GemmArgs {
     int32_t* fc_src_slot_copy;
 };
 
-// splits = K-split count (grid.y); the partial buffer must hold splits * m_cap * Nout floats.
-// nt = 16-column tiles per workgroup (4 or 8); max_rows = upper bound of M (picks the row chunk).
-hipError_t launch_gemm_partial(const GemmArgs& a, int splits, int max_rows, int nt, hipStream_t st);
-// gate/up GEMM with SwiGLU: Nout = 2F (gate rows then up rows), no K split; act = silu(g) * u.
-hipError_t launch_gemm_swiglu(const GemmArgs& a, int max_rows, int nt, hipStream_t st);
+// Tile shape of one launch: a workgroup covers the output columns of one of `groups` even
+// column groups (at most gemm_group_cols), a chunk of gemm_chunk_rows rows and one of `splits`
+// K ranges (grid.y; the partial buffer holds splits * m_cap * Nout floats).  Its 4 waves form a
+// wn x (4/wn) grid; a wave owns ntw 16-row weight tiles and tm 16-row activation tiles; nb stage
+// slots form the LDS ring.  swiglu: the gate/up GEMM (Nout = 2F, gate rows then up rows, no K
+// split) writing act = silu(g) * u.
+struct GemmCfg {
+    int ntw, wn, tm, nb, groups, splits;
+    bool swiglu;
+};
+// the (ntw, wn, tm, nb) shapes compiled
+#define SPECFOLD_GEMM_CASES(X) \
+    X(4, 1, 2, 3) X(2, 2, 2, 3)
+int gemm_chunk_rows(const GemmCfg& c);
+int gemm_group_cols(const GemmCfg& c);
+size_t gemm_lds_bytes(const GemmCfg& c);
+hipError_t launch_gemm(const GemmArgs& a, const GemmCfg& c, hipStream_t st);
 
 // ------------------------------------------------------------------ GEMM epilogues
 struct QkvEpiArgs {
