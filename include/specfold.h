@@ -73,6 +73,8 @@ extern "C" {
 #define SPECFOLD_MAX_BRANCHES 64     /* n_branch = B + 1                                       */
 #define SPECFOLD_MAX_BLOCK    64     /* block positions N per branch (attention keeps the N    */
                                      /* block keys of a branch in LDS)                         */
+#define SPECFOLD_MAX_HIDDEN   5120   /* D: the gate keeps a whole row in one wave's registers  */
+#define SPECFOLD_MAX_QKV_WIDTH 8192  /* (n_q_heads + 2 n_kv_heads) * head_dim                  */
 /* head_dim in {16, 32, 64, 128}; hidden, ffn and n_q_heads*head_dim multiples of 64;
    n_q_heads a multiple of n_kv_heads. */
 

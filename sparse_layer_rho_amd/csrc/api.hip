@@ -57,7 +57,8 @@ GemmCfg pick_gemm(int n_cols, int k, int max_rows, int busy_chunks, bool swiglu)
     if (!swiglu) {
         const int busy = c.groups * (busy_chunks > 0 ? busy_chunks : 1);
         int s = (384 + busy / 2) / busy;
-        const int smax = (k + 63) / 64 / 4;
+        int smax = (k + 63) / 64 / 4;
+        if (smax > 32) smax = 32;                          // the epilogues batch up to 32 splits
         if (s > smax) s = smax;
         c.splits = s < 1 ? 1 : s;
     }
@@ -127,7 +128,7 @@ int check_rows_shape(const specfold_shape* s, int max_block) {
     if (s->n_branch < 1 || s->block < 1 || s->hidden < 1) return SPECFOLD_ERR_SHAPE;
     if (s->n_branch > SPECFOLD_MAX_BRANCHES || s->block > max_block) return SPECFOLD_ERR_UNSUPPORTED;
     if (static_cast<int64_t>(s->n_branch) * s->block > (1 << 24)) return SPECFOLD_ERR_UNSUPPORTED;
-    if (s->hidden % 64 != 0) return SPECFOLD_ERR_UNSUPPORTED;
+    if (s->hidden % 64 != 0 || s->hidden > SPECFOLD_MAX_HIDDEN) return SPECFOLD_ERR_UNSUPPORTED;
     if (!(s->rms_eps >= 0.f) || !std::isfinite(s->rms_eps)) return SPECFOLD_ERR_SHAPE;
     return SPECFOLD_OK;
 }
@@ -144,6 +145,7 @@ int check_layer_shape(const specfold_shape* s) {
     if (hd != 16 && hd != 32 && hd != 64 && hd != 128) return SPECFOLD_ERR_UNSUPPORTED;
     if (s->ffn % 64 != 0 || (s->n_q_heads * hd) % 64 != 0) return SPECFOLD_ERR_UNSUPPORTED;
     if (((s->n_q_heads + 2 * s->n_kv_heads) * hd) % 32 != 0) return SPECFOLD_ERR_UNSUPPORTED;
+    if ((s->n_q_heads + 2 * s->n_kv_heads) * hd > SPECFOLD_MAX_QKV_WIDTH) return SPECFOLD_ERR_UNSUPPORTED;
     // every weight matrix and activation buffer a GEMM streams must stay below 1 GB (the
     // kernels address them with 32-bit buffer offsets and out-of-range sentinels above 1 GB)
     const int64_t gb = int64_t(1) << 30;

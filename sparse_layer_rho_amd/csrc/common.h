@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace specfold {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -70,5 +72,29 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// ---- buffer loads.  A raw buffer resource bounds every load: offsets at or past its size
+// read as zeros without touching memory, which keeps loops branch-free (rows, columns or
+// splits past the end take an out-of-range offset) and lets every load of a batch be in
+// flight at once.  Buffers are < 1 GB (checked by the host), so kOob plus any in-range offset
+// stays out of range.
+constexpr uint32_t kOob = 0x40000000u;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ f32x4 buf_loadf4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
 
 }  // namespace specfold

@@ -10,6 +10,9 @@
 //          H_out[r] = h_mid[r] + f[src_slot[r]] [SpecFold summary, App. B: every position adds
 //          its own residual stream, which is never folded; §A.2: folded positions reuse the
 //          source's FFN output].
+// Every thread owns 4 consecutive columns of one row and issues all its loads (SPL split
+// partials, rounded up; splits past the last read zeros) before it adds anything, so a kernel
+// costs one memory round trip instead of one per split.
 #include "kernels.h"
 
 namespace specfold {
@@ -21,97 +24,145 @@ __device__ __forceinline__ int clamp_m(const int32_t* m_count, int cap) {
     return M < 0 ? 0 : (M > cap ? cap : M);
 }
 
-__global__ __launch_bounds__(256) void qkv_epilogue_kernel(const QkvEpiArgs a) {
-    const int m = blockIdx.x;
-    if (m >= clamp_m(a.m_count, a.m_cap)) return;
-    const int row = a.rec_rows[m];
-    const bool ok = row >= 0 && row < a.R;
-    const double pos = static_cast<double>(a.P + (ok ? row % a.N : 0));
-    const int heads = a.Hq + 2 * a.Hkv;
-    const int half = a.hd >> 1;
-    const int nq = heads * a.hd;
-    const float bad = ok ? 0.f : __builtin_nanf("");
-    for (int idx = threadIdx.x; idx < heads * half; idx += blockDim.x) {
-        const int hh = idx / half, j = idx - hh * half;
-        const int c1 = hh * a.hd + j, c2 = c1 + half;
-        float x1 = bad, x2 = bad;
-        for (int s = 0; s < a.splits; ++s) {
-            const float* pr = a.part + (static_cast<size_t>(s) * a.m_cap + m) * nq;
-            x1 += pr[c1];
-            x2 += pr[c2];
-        }
-        float y1 = x1, y2 = x2;
-        if (hh < a.Hq + a.Hkv) {
-            // angle (P + n) theta^(-2j/d) formed in double and reduced to [-pi, pi]
-            const double ang = pos * a.inv_freq[j];
-            const double twopi = 6.283185307179586476925286766559;
-            const float red = static_cast<float>(ang - twopi * rint(ang / twopi));
-            float sn, cs;
-            sincosf(red, &sn, &cs);
-            y1 = x1 * cs - x2 * sn;
-            y2 = x2 * cs + x1 * sn;
-        }
-        uint16_t* dst;
-        if (hh < a.Hq) dst = a.q_c + (static_cast<size_t>(m) * a.Hq + hh) * a.hd;
-        else if (hh < a.Hq + a.Hkv) dst = a.k_c + (static_cast<size_t>(m) * a.Hkv + (hh - a.Hq)) * a.hd;
-        else dst = a.v_c + (static_cast<size_t>(m) * a.Hkv + (hh - a.Hq - a.Hkv)) * a.hd;
-        dst[j] = f32_to_bf16(y1);
-        dst[j + half] = f32_to_bf16(y2);
-    }
+// sum over splits s < S, in ascending order, of the float4 at byte offset base + s * stride
+template <int SPL>
+__device__ __forceinline__ f32x4 sum_splits(__amdgpu_buffer_rsrc_t r, uint32_t base, uint32_t stride, int S) {
+    f32x4 v[SPL];
+#pragma unroll
+    for (int s = 0; s < SPL; ++s) v[s] = buf_loadf4(r, s < S ? base + s * stride : kOob);
+    f32x4 acc = v[0];
+#pragma unroll
+    for (int s = 1; s < SPL; ++s) acc += v[s];
+    return acc;
 }
 
-__device__ __forceinline__ void load_bf16x4(const uint16_t* p, float* f) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
+__device__ __forceinline__ void unpack4(const uint2 v, float* f) {
     f[0] = __uint_as_float(v.x << 16);
     f[1] = __uint_as_float(v.x & 0xffff0000u);
     f[2] = __uint_as_float(v.y << 16);
     f[3] = __uint_as_float(v.y & 0xffff0000u);
 }
 
-// one wave per row
-__global__ __launch_bounds__(256) void oproj_epilogue_kernel(const float* __restrict__ part, int splits, int R,
-                                                             int D, const uint16_t* __restrict__ H,
-                                                             uint16_t* __restrict__ h_mid,
-                                                             const uint16_t* __restrict__ ln, float eps,
-                                                             uint16_t* __restrict__ xn) {
-    const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-    if (r >= R) return;
+__device__ __forceinline__ uint2 pack4(const float* f) {
+    return make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+}
+
+// workgroup m = recompute slot m; thread u = (head, 4 consecutive rotary pairs j0 .. j0+3)
+template <int SPL>
+__global__ __launch_bounds__(1024) void qkv_epilogue_kernel(const QkvEpiArgs a) {
+    const int m = blockIdx.x;
+    const int heads = a.Hq + 2 * a.Hkv, half = a.hd >> 1, q4 = a.hd >> 3;
+    const int u = threadIdx.x;
+    if (m >= clamp_m(a.m_count, a.m_cap) || u >= heads * q4) return;
+    const int row = a.rec_rows[m];
+    const bool ok = row >= 0 && row < a.R;
+    const int nq = heads * a.hd;
+    const int hh = u / q4, j0 = (u - hh * q4) * 4;
+    const int c1 = hh * a.hd + j0;
+    const __amdgpu_buffer_rsrc_t rP =
+        make_rsrc(a.part, static_cast<uint32_t>(static_cast<size_t>(a.splits) * a.m_cap * nq * 4));
+    const uint32_t stride = static_cast<uint32_t>(a.m_cap) * nq * 4;
+    const uint32_t base = (static_cast<uint32_t>(m) * nq + c1) * 4;
+    f32x4 x1 = sum_splits<SPL>(rP, base, stride, a.splits);
+    f32x4 x2 = sum_splits<SPL>(rP, base + half * 4, stride, a.splits);
+    if (!ok) x1 = x2 = f32x4{1.f, 1.f, 1.f, 1.f} * __builtin_nanf("");
+    float y1[4], y2[4];
+    if (hh < a.Hq + a.Hkv) {
+        const double pos = static_cast<double>(a.P + (ok ? row % a.N : 0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            // angle (P + n) theta^(-2j/d) formed in double and reduced to [-pi, pi]
+            const double ang = pos * a.inv_freq[j0 + e];
+            const double twopi = 6.283185307179586476925286766559;
+            const float red = static_cast<float>(ang - twopi * rint(ang / twopi));
+            float sn, cs;
+            sincosf(red, &sn, &cs);
+            y1[e] = x1[e] * cs - x2[e] * sn;
+            y2[e] = x2[e] * cs + x1[e] * sn;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { y1[e] = x1[e]; y2[e] = x2[e]; }
+    }
+    uint16_t* dst;
+    if (hh < a.Hq) dst = a.q_c + (static_cast<size_t>(m) * a.Hq + hh) * a.hd;
+    else if (hh < a.Hq + a.Hkv) dst = a.k_c + (static_cast<size_t>(m) * a.Hkv + (hh - a.Hq)) * a.hd;
+    else dst = a.v_c + (static_cast<size_t>(m) * a.Hkv + (hh - a.Hq - a.Hkv)) * a.hd;
+    *reinterpret_cast<uint2*>(dst + j0) = pack4(y1);
+    *reinterpret_cast<uint2*>(dst + j0 + half) = pack4(y2);
+}
+
+// workgroup r = row r; thread t owns column quads t, t + blockDim.x, ... (MAXU of them)
+template <int SPL, int MAXU>
+__global__ __launch_bounds__(1024) void oproj_epilogue_kernel(const float* __restrict__ part, int splits, int R,
+                                                              int D, const uint16_t* __restrict__ H,
+                                                              uint16_t* __restrict__ h_mid,
+                                                              const uint16_t* __restrict__ ln, float eps,
+                                                              uint16_t* __restrict__ xn) {
+    __shared__ float s_ss[16];
+    const int r = blockIdx.x, tid = threadIdx.x, B = blockDim.x;
     const int D4 = D >> 2;
+    const __amdgpu_buffer_rsrc_t rP = make_rsrc(part, static_cast<uint32_t>(static_cast<size_t>(splits) * R * D * 4));
+    const __amdgpu_buffer_rsrc_t rH = make_rsrc(H, static_cast<uint32_t>(static_cast<size_t>(R) * D * 2));
+    const uint32_t stride = static_cast<uint32_t>(R) * D * 4;
+    f32x4 acc[MAXU];
+    uint2 hv[MAXU];
+#pragma unroll
+    for (int k = 0; k < MAXU; ++k) {
+        const int u = tid + k * B;
+        const bool valid = u < D4;
+        const uint32_t e = static_cast<uint32_t>(r) * D + 4 * u;
+        acc[k] = sum_splits<SPL>(rP, valid ? e * 4 : kOob, stride, splits);
+        hv[k] = buf_load8(rH, valid ? e * 2 : kOob);
+    }
     float ss = 0.f;
-    for (int c4 = lane; c4 < D4; c4 += 64) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < splits; ++s)
-            acc += *reinterpret_cast<const f32x4*>(part + (static_cast<size_t>(s) * R + r) * D + 4 * c4);
+#pragma unroll
+    for (int k = 0; k < MAXU; ++k) {
+        const int u = tid + k * B;
         float h[4];
-        load_bf16x4(H + static_cast<size_t>(r) * D + 4 * c4, h);
-        const uint2 hv = make_uint2(pack_bf16x2(h[0] + acc[0], h[1] + acc[1]), pack_bf16x2(h[2] + acc[2], h[3] + acc[3]));
-        *reinterpret_cast<uint2*>(h_mid + static_cast<size_t>(r) * D + 4 * c4) = hv;
-        const float q0 = __uint_as_float(hv.x << 16), q1 = __uint_as_float(hv.x & 0xffff0000u);
-        const float q2 = __uint_as_float(hv.y << 16), q3 = __uint_as_float(hv.y & 0xffff0000u);
-        ss += q0 * q0 + q1 * q1 + q2 * q2 + q3 * q3;
+        unpack4(hv[k], h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] += acc[k][e];
+        hv[k] = pack4(h);
+        if (u < D4) {
+            *reinterpret_cast<uint2*>(h_mid + static_cast<size_t>(r) * D + 4 * u) = hv[k];
+            unpack4(hv[k], h);                     // RMSNorm reads the bf16-rounded residual
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ss += h[e] * h[e];
+        }
     }
     if (!xn) return;
     ss = wave_sum(ss);
-    const float inv = 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
-    for (int c4 = lane; c4 < D4; c4 += 64) {
+    if ((tid & 63) == 0) s_ss[tid >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+    for (int w = 0; w < (B >> 6); ++w) tot += s_ss[w];
+    const float inv = 1.0f / sqrtf(tot / static_cast<float>(D) + eps);
+#pragma unroll
+    for (int k = 0; k < MAXU; ++k) {
+        const int u = tid + k * B;
+        if (u >= D4) continue;
         float h[4], w[4] = {1.f, 1.f, 1.f, 1.f};
-        load_bf16x4(h_mid + static_cast<size_t>(r) * D + 4 * c4, h);
-        if (ln) load_bf16x4(ln + 4 * c4, w);
-        *reinterpret_cast<uint2*>(xn + static_cast<size_t>(r) * D + 4 * c4) =
-            make_uint2(pack_bf16x2(h[0] * inv * w[0], h[1] * inv * w[1]), pack_bf16x2(h[2] * inv * w[2], h[3] * inv * w[3]));
+        unpack4(hv[k], h);
+        if (ln) unpack4(*reinterpret_cast<const uint2*>(ln + 4 * u), w);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = h[e] * inv * w[e];
+        *reinterpret_cast<uint2*>(xn + static_cast<size_t>(r) * D + 4 * u) = pack4(h);
     }
 }
 
 // workgroup b: reduces slot b (when b < M) into every row that inherits from it; also writes
 // NaN into row b when row b's source slot is invalid
-__global__ __launch_bounds__(256) void down_epilogue_kernel(const float* __restrict__ part, int splits, int m_cap,
-                                                            const int32_t* m_count, const int32_t* rec_rows,
-                                                            const int32_t* __restrict__ src_slot, int nb, int N,
-                                                            int D, const uint16_t* __restrict__ h_mid,
-                                                            uint16_t* __restrict__ H_out) {
+template <int SPL, int MAXU>
+__global__ __launch_bounds__(1024) void down_epilogue_kernel(const float* __restrict__ part, int splits, int m_cap,
+                                                             const int32_t* m_count, const int32_t* rec_rows,
+                                                             const int32_t* __restrict__ src_slot, int nb, int N,
+                                                             int D, const uint16_t* __restrict__ h_mid,
+                                                             uint16_t* __restrict__ H_out) {
+    constexpr int kBatch = 4;                      // inheriting rows loaded per round trip
     __shared__ int s_rows[kMaxBranches];
     __shared__ int s_cnt;
-    const int b = blockIdx.x;
+    const int b = blockIdx.x, tid = threadIdx.x, B = blockDim.x;
     const int M = clamp_m(m_count, m_cap);
     const int R = nb * N;
     const int D4 = D >> 2;
@@ -119,7 +170,7 @@ __global__ __launch_bounds__(256) void down_epilogue_kernel(const float* __restr
         const int sb = src_slot[b];
         if (sb < 0 || sb >= M) {
             const float nan = __builtin_nanf("");
-            for (int c4 = threadIdx.x; c4 < D4; c4 += blockDim.x)
+            for (int c4 = tid; c4 < D4; c4 += B)
                 *reinterpret_cast<uint2*>(H_out + static_cast<size_t>(b) * D + 4 * c4) =
                     make_uint2(pack_bf16x2(nan, nan), pack_bf16x2(nan, nan));
         }
@@ -128,43 +179,94 @@ __global__ __launch_bounds__(256) void down_epilogue_kernel(const float* __restr
     const int row = rec_rows[b];
     if (row < 0 || row >= R) return;
     const int n = row % N;
-    if (threadIdx.x == 0) s_cnt = 0;
+    if (tid == 0) s_cnt = 0;
     __syncthreads();
-    if (threadIdx.x < nb) {
-        const int r = threadIdx.x * N + n;
+    if (tid < nb) {
+        const int r = tid * N + n;
         if (src_slot[r] == b) s_rows[atomicAdd(&s_cnt, 1)] = r;
+    }
+    const __amdgpu_buffer_rsrc_t rP = make_rsrc(part, static_cast<uint32_t>(static_cast<size_t>(splits) * m_cap * D * 4));
+    const __amdgpu_buffer_rsrc_t rH = make_rsrc(h_mid, static_cast<uint32_t>(static_cast<size_t>(R) * D * 2));
+    const uint32_t stride = static_cast<uint32_t>(m_cap) * D * 4;
+    f32x4 f[MAXU];
+#pragma unroll
+    for (int k = 0; k < MAXU; ++k) {
+        const int u = tid + k * B;
+        f[k] = sum_splits<SPL>(rP, u < D4 ? (static_cast<uint32_t>(b) * D + 4 * u) * 4 : kOob, stride, splits);
     }
     __syncthreads();
     const int cnt = s_cnt;
-    for (int c4 = threadIdx.x; c4 < D4; c4 += blockDim.x) {
-        f32x4 f = {0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < splits; ++s)
-            f += *reinterpret_cast<const f32x4*>(part + (static_cast<size_t>(s) * m_cap + b) * D + 4 * c4);
-        for (int t = 0; t < cnt; ++t) {
-            const int r = s_rows[t];
-            float h[4];
-            load_bf16x4(h_mid + static_cast<size_t>(r) * D + 4 * c4, h);
-            *reinterpret_cast<uint2*>(H_out + static_cast<size_t>(r) * D + 4 * c4) =
-                make_uint2(pack_bf16x2(h[0] + f[0], h[1] + f[1]), pack_bf16x2(h[2] + f[2], h[3] + f[3]));
-        }
+    for (int t0 = 0; t0 < cnt; t0 += kBatch) {
+        uint2 hv[kBatch][MAXU];
+#pragma unroll
+        for (int t = 0; t < kBatch; ++t)
+#pragma unroll
+            for (int k = 0; k < MAXU; ++k) {
+                const int u = tid + k * B;
+                const bool valid = t0 + t < cnt && u < D4;
+                hv[t][k] = buf_load8(rH, valid ? (static_cast<uint32_t>(s_rows[valid ? t0 + t : 0]) * D + 4 * u) * 2 : kOob);
+            }
+#pragma unroll
+        for (int t = 0; t < kBatch; ++t)
+#pragma unroll
+            for (int k = 0; k < MAXU; ++k) {
+                const int u = tid + k * B;
+                if (t0 + t >= cnt || u >= D4) continue;
+                float h[4];
+                unpack4(hv[t][k], h);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) h[e] += f[k][e];
+                *reinterpret_cast<uint2*>(H_out + static_cast<size_t>(s_rows[t0 + t]) * D + 4 * u) = pack4(h);
+            }
     }
+}
+
+// split count rounded up to the compiled load batch
+template <typename F>
+hipError_t with_spl(int splits, F&& f) {
+    if (splits <= 4) return f(std::integral_constant<int, 4>{});
+    if (splits <= 8) return f(std::integral_constant<int, 8>{});
+    if (splits <= 16) return f(std::integral_constant<int, 16>{});
+    if (splits <= 32) return f(std::integral_constant<int, 32>{});
+    return hipErrorInvalidValue;
+}
+
+// threads per row: the column quads, rounded up to a wave and capped at 1024 (then 2 per thread)
+inline int quad_block(int D4) {
+    const int b = ((D4 + 63) / 64) * 64;
+    return b > 1024 ? 1024 : (b < 64 ? 64 : b);
 }
 
 }  // namespace
 
 hipError_t launch_qkv_epilogue(const QkvEpiArgs& a, hipStream_t st) {
     if (a.m_cap <= 0) return hipSuccess;
-    hipLaunchKernelGGL(qkv_epilogue_kernel, dim3(a.m_cap), dim3(256), 0, st, a);
-    return hipGetLastError();
+    const int units = (a.Hq + 2 * a.Hkv) * (a.hd >> 3);
+    if (units > 1024) return hipErrorInvalidValue;
+    const int block = ((units + 63) / 64) * 64;
+    return with_spl(a.splits, [&](auto spl) {
+        hipLaunchKernelGGL(qkv_epilogue_kernel<decltype(spl)::value>, dim3(a.m_cap), dim3(block), 0, st, a);
+        return hipGetLastError();
+    });
 }
 
 hipError_t launch_oproj_epilogue(const float* part, int splits, int R, int D, const uint16_t* H,
                                  uint16_t* h_mid, const uint16_t* ln, float eps, uint16_t* xn,
                                  hipStream_t st) {
     if (R <= 0) return hipSuccess;
-    hipLaunchKernelGGL(oproj_epilogue_kernel, dim3((R + 3) / 4), dim3(256), 0, st, part, splits, R, D, H, h_mid,
-                       ln, eps, xn);
-    return hipGetLastError();
+    const int D4 = D >> 2, block = quad_block(D4);
+    const int per = (D4 + block - 1) / block;
+    if (per > 2) return hipErrorInvalidValue;
+    return with_spl(splits, [&](auto spl) {
+        constexpr int SPL = decltype(spl)::value;
+        if (per == 1)
+            hipLaunchKernelGGL((oproj_epilogue_kernel<SPL, 1>), dim3(R), dim3(block), 0, st, part, splits, R, D, H,
+                               h_mid, ln, eps, xn);
+        else
+            hipLaunchKernelGGL((oproj_epilogue_kernel<SPL, 2>), dim3(R), dim3(block), 0, st, part, splits, R, D, H,
+                               h_mid, ln, eps, xn);
+        return hipGetLastError();
+    });
 }
 
 hipError_t launch_down_epilogue(const float* part, int splits, int m_cap, const int32_t* m_count,
@@ -172,9 +274,20 @@ hipError_t launch_down_epilogue(const float* part, int splits, int m_cap, const 
                                 const uint16_t* h_mid, uint16_t* H_out, hipStream_t st) {
     const int R = nb * N;
     if (R <= 0) return hipSuccess;
-    hipLaunchKernelGGL(down_epilogue_kernel, dim3(R > m_cap ? R : m_cap), dim3(256), 0, st, part, splits, m_cap,
-                       m_count, rec_rows, src_slot, nb, N, D, h_mid, H_out);
-    return hipGetLastError();
+    const int D4 = D >> 2, block = quad_block(D4);
+    const int per = (D4 + block - 1) / block;
+    if (per > 2) return hipErrorInvalidValue;
+    const dim3 grid(R > m_cap ? R : m_cap);
+    return with_spl(splits, [&](auto spl) {
+        constexpr int SPL = decltype(spl)::value;
+        if (per == 1)
+            hipLaunchKernelGGL((down_epilogue_kernel<SPL, 1>), grid, dim3(block), 0, st, part, splits, m_cap, m_count,
+                               rec_rows, src_slot, nb, N, D, h_mid, H_out);
+        else
+            hipLaunchKernelGGL((down_epilogue_kernel<SPL, 2>), grid, dim3(block), 0, st, part, splits, m_cap, m_count,
+                               rec_rows, src_slot, nb, N, D, h_mid, H_out);
+        return hipGetLastError();
+    });
 }
 
 }  // namespace specfold

@@ -21,7 +21,7 @@ namespace specfold {
 
 namespace {
 
-constexpr int kRowCache = 10;   // 16-byte chunks per lane kept in registers (D <= 5120)
+constexpr int kMaxChunksPerLane = 10;   // 16-byte chunks per lane of one row: D <= 5120
 
 __device__ __forceinline__ float rho_of(float a, float b) {
     if (b > 0.f) return sqrtf(a) / sqrtf(b);
@@ -45,54 +45,41 @@ __device__ __forceinline__ uint4 norm_chunk(const float* x, float s, const uint1
     return pack8(y);
 }
 
-// one wave computes rho, fold, inv_rms (and optionally the normalised row) of one row
+// One wave computes rho, fold, inv_rms (and optionally the normalised row) of one row.  Lane l
+// holds chunks l, l + 64, ... (CPL of them) of the child and the parent row; all of them are
+// requested before any is used (chunks past the row, and the parent of a main row, read zeros
+// from an out-of-range offset), so a row costs one memory round trip.
+template <int CPL>
 __device__ __forceinline__ void gate_row(const GateParams& p, int row, int lane) {
     const int i = row / p.N, n = row - i * p.N;
     const bool need_pair = (i > 0) && (p.rho_in == nullptr);
     const bool need_rows = need_pair || (p.inv_rms != nullptr) || (p.xn != nullptr);
     const int nch = p.D >> 3;
     float a = 0.f, b = 0.f, ss = 0.f;
-    uint4 cache[kRowCache];
-    const uint4* c = reinterpret_cast<const uint4*>(p.H + static_cast<size_t>(row) * p.D);
+    uint4 cv[CPL];
     if (need_rows) {
-        const uint4* q = need_pair
-            ? reinterpret_cast<const uint4*>(p.H + (static_cast<size_t>(p.par.p[i]) * p.N + n) * p.D)
-            : nullptr;
+        const __amdgpu_buffer_rsrc_t rH =
+            make_rsrc(p.H, static_cast<uint32_t>(static_cast<size_t>(p.nb) * p.N * p.D * 2));
+        const uint32_t cb = static_cast<uint32_t>(row) * p.D * 2;
+        const uint32_t pb = need_pair ? static_cast<uint32_t>(p.par.p[i] * p.N + n) * p.D * 2 : kOob;
+        uint4 pv[CPL];
 #pragma unroll
-        for (int t = 0; t < kRowCache; ++t) {
+        for (int t = 0; t < CPL; ++t) {
             const int k = lane + t * kWave;
-            if (k < nch) {
-                cache[t] = c[k];
-                float x[8];
-                unpack8(cache[t], x);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
-                if (need_pair) {
-                    float yv[8];
-                    unpack8(q[k], yv);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float d = x[e] - yv[e];
-                        a += d * d;
-                        b += yv[e] * yv[e];
-                    }
-                }
-            }
+            cv[t] = buf_load16(rH, k < nch ? cb + 16 * k : kOob);
+            pv[t] = buf_load16(rH, k < nch ? pb + 16 * k : kOob);
         }
-        for (int k = lane + kRowCache * kWave; k < nch; k += kWave) {
-            float x[8];
-            unpack8(c[k], x);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
-            if (need_pair) {
-                float yv[8];
-                unpack8(q[k], yv);
+        for (int t = 0; t < CPL; ++t) {
+            float x[8], yv[8];
+            unpack8(cv[t], x);
+            unpack8(pv[t], yv);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float d = x[e] - yv[e];
-                    a += d * d;
-                    b += yv[e] * yv[e];
-                }
+            for (int e = 0; e < 8; ++e) {
+                const float d = x[e] - yv[e];
+                ss += x[e] * x[e];
+                a += d * d;
+                b += yv[e] * yv[e];
             }
         }
         a = wave_sum(a);
@@ -115,25 +102,21 @@ __device__ __forceinline__ void gate_row(const GateParams& p, int row, int lane)
     if (p.xn) {
         uint4* o = reinterpret_cast<uint4*>(p.xn + static_cast<size_t>(row) * p.D);
 #pragma unroll
-        for (int t = 0; t < kRowCache; ++t) {
+        for (int t = 0; t < CPL; ++t) {
             const int k = lane + t * kWave;
             if (k < nch) {
                 float x[8];
-                unpack8(cache[t], x);
+                unpack8(cv[t], x);
                 o[k] = norm_chunk(x, inv, p.ln, k);
             }
-        }
-        for (int k = lane + kRowCache * kWave; k < nch; k += kWave) {
-            float x[8];
-            unpack8(c[k], x);
-            o[k] = norm_chunk(x, inv, p.ln, k);
         }
     }
 }
 
+template <int CPL>
 __global__ __launch_bounds__(256) void gate_kernel(const GateParams p) {
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row < p.nb * p.N) gate_row(p, row, threadIdx.x & (kWave - 1));
+    if (row < p.nb * p.N) gate_row<CPL>(p, row, threadIdx.x & (kWave - 1));
 }
 
 // block-wide exclusive scan of recompute flags, blockDim.x threads, rows in ascending order
@@ -215,7 +198,17 @@ __global__ __launch_bounds__(256) void row_norm_kernel(const uint16_t* __restric
 hipError_t launch_gate(const GateParams& p, hipStream_t st) {
     const int R = p.nb * p.N;
     if (R <= 0) return hipSuccess;
-    hipLaunchKernelGGL(gate_kernel, dim3((R + 3) / 4), dim3(256), 0, st, p);
+    const int cpl = ((p.D >> 3) + kWave - 1) / kWave;
+    if (cpl > kMaxChunksPerLane) return hipErrorInvalidValue;
+    const dim3 grid((R + 3) / 4), block(256);
+    switch (cpl) {
+#define SPECFOLD_GATE_CASE(C) \
+    case C: hipLaunchKernelGGL(gate_kernel<C>, grid, block, 0, st, p); break;
+        SPECFOLD_GATE_CASE(1) SPECFOLD_GATE_CASE(2) SPECFOLD_GATE_CASE(3) SPECFOLD_GATE_CASE(4)
+        SPECFOLD_GATE_CASE(5) SPECFOLD_GATE_CASE(6) SPECFOLD_GATE_CASE(7) SPECFOLD_GATE_CASE(8)
+        SPECFOLD_GATE_CASE(9) SPECFOLD_GATE_CASE(10)
+#undef SPECFOLD_GATE_CASE
+    }
     return hipGetLastError();
 }
 

@@ -34,9 +34,8 @@ namespace {
 // Out-of-range offsets: a missing row adds kOobRow, K past the matrix adds kOobK.  Buffers are
 // < 1 GB (checked by the host), so any sum involving either is out of range and the two never
 // wrap back into range together.
-constexpr uint32_t kOobRow = 0x40000000u;
+constexpr uint32_t kOobRow = kOob;
 constexpr uint32_t kOobK = 0x80000000u;
-constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr int kStageK = 64;                 // K elements per stage
 constexpr int kRowB = 128;                  // bytes of one row in one stage
 
@@ -44,10 +43,6 @@ enum { EPI_PARTIAL = 0, EPI_SWIGLU = 1 };
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
-}
 
 // 16 bytes per lane, global -> LDS: lane l's bytes land at lds + 16 l (lds is wave-uniform)
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff) {

@@ -54,7 +54,7 @@ def _shape(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(head_dim=24), -6), (dict(n_q_heads=3), -2), (dict(n_branch=0), -2), (dict(block=65), -6),
-    (dict(n_branch=65), -6), (dict(hidden=96), -6), (dict(ffn=100), -6), (dict(prefix_len=-1), -2),
+    (dict(n_branch=65), -6), (dict(hidden=96), -6), (dict(hidden=5184), -6), (dict(ffn=100), -6), (dict(prefix_len=-1), -2),
     (dict(rope_theta=0.0), -2),
 ])
 def test_workspace_bytes_rejects_bad_shapes(kw, code):
