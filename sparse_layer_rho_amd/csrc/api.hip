@@ -74,7 +74,7 @@ Layout layout_of(const Dims& d) {
     L.c_gu = pick_gemm(d.F, d.D, d.R, 1, true);
     L.c_down = pick_gemm(d.D, d.F, d.R, 1, false);
     L.s_qkv = L.c_qkv.splits; L.s_o = L.c_o.splits; L.s_down = L.c_down.splits;
-    L.chunk_len = d.P <= 1024 ? 256 : 512;
+    L.chunk_len = d.P <= 1024 ? 128 : 512;
     L.n_chunks = d.P > 0 ? (d.P + L.chunk_len - 1) / L.chunk_len : 0;
     const size_t R = static_cast<size_t>(d.R);
     size_t off = 0;
@@ -153,8 +153,11 @@ int check_layer_shape(const specfold_shape* s) {
     const int64_t nq = static_cast<int64_t>(s->n_q_heads + 2 * s->n_kv_heads) * hd;
     if (4 * static_cast<int64_t>(s->hidden) * s->ffn >= gb || 2 * nq * s->hidden >= gb ||
         2 * static_cast<int64_t>(s->hidden) * s->n_q_heads * hd >= gb || 2 * R * s->ffn >= gb ||
-        2 * R * s->hidden >= gb)
+        2 * R * s->hidden >= gb || 2 * R * nq >= gb)
         return SPECFOLD_ERR_UNSUPPORTED;
+    // prefix chunk states [n_chunks][R][Hq][hd] fp32 (chunks of 512 past 1024 prefix tokens)
+    const int64_t chunks = s->prefix_len <= 1024 ? (s->prefix_len + 127) / 128 : (s->prefix_len + 511) / 512;
+    if (4 * chunks * R * s->n_q_heads * hd >= gb) return SPECFOLD_ERR_UNSUPPORTED;
     if (static_cast<int64_t>(s->prefix_len) > (int64_t(1) << 24)) return SPECFOLD_ERR_UNSUPPORTED;
     return SPECFOLD_OK;
 }
@@ -189,6 +192,11 @@ int check_prefix(const specfold_prefix_kv* pf, const Dims& d) {
         if (x % 8 != 0) return SPECFOLD_ERR_ALIGN;
     }
     if (d.P > 1 && (pf->k_stride_tok == 0 || pf->v_stride_tok == 0)) return SPECFOLD_ERR_SHAPE;
+    // the attention kernels address each view with 32-bit offsets below 1 GB
+    const int64_t gb = int64_t(1) << 30;
+    const int64_t ek = ((d.P - 1) * pf->k_stride_tok + (d.Hkv - 1) * pf->k_stride_head + d.hd) * 2;
+    const int64_t ev = ((d.P - 1) * pf->v_stride_tok + (d.Hkv - 1) * pf->v_stride_head + d.hd) * 2;
+    if (ek >= gb || ev >= gb) return SPECFOLD_ERR_UNSUPPORTED;
     return SPECFOLD_OK;
 }
 

@@ -11,6 +11,11 @@
 // computes the N-key block part for every row of every branch and merges it with the chunk
 // states of the row's source slot by log-sum-exp, in a fixed order (deterministic).
 //
+// Keys and values move through LDS in blocks of 64: K row-major, V transposed (the PV product
+// needs 8 consecutive keys of one dimension per lane).  Every load is a bounded buffer load
+// (keys past the end and invalid slots read as zeros), so a block costs one round trip, and the
+// prefix kernel fetches block b+1 into registers while it multiplies block b.
+//
 // Both kernels are FlashAttention-style on bf16 MFMA with the transposed product S^T = K Q^T:
 // keys are the MFMA rows, the 16 queries of a wave are its columns, so each lane owns one
 // query's statistics and the P V product O^T = V^T P^T takes P straight from registers
@@ -29,33 +34,50 @@ struct AttnTile {
     static constexpr int DT = HD / 16;          // 16-row output tiles over head_dim
     static constexpr int KROW = HD * 2 + 16;    // LDS bytes per key row (padded)
     static constexpr int VROW = 64 * 2 + 8;     // LDS bytes per transposed value row (64 keys)
+    static constexpr int CH = HD / 8;           // 16-byte chunks per key row
+    static constexpr int U = (64 * CH + 255) / 256;   // staging units per thread (256 threads)
 };
 
-// Load up to 64 keys/values (rows given by key_ptr) into LDS: K row-major, V transposed.
-template <int HD, typename KeyPtr>
-__device__ __forceinline__ void stage_kv(uint8_t* sK, uint8_t* sV, int nk, KeyPtr key_ptr) {
-    using T = AttnTile<HD>;
-    constexpr int CH = HD / 8;
-    uint16_t* vt = reinterpret_cast<uint16_t*>(sV);
-    for (int idx = threadIdx.x; idx < 64 * CH; idx += blockDim.x) {
-        const int key = idx / CH, cc = idx - key * CH;
-        uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-        const uint16_t* kp = nullptr;
-        const uint16_t* vp = nullptr;
-        if (key < nk) key_ptr(key, kp, vp);
-        if (kp) {
-            kv = *reinterpret_cast<const uint4*>(kp + cc * 8);
-            vv = *reinterpret_cast<const uint4*>(vp + cc * 8);
-        }
-        *reinterpret_cast<uint4*>(sK + key * T::KROW + cc * 16) = kv;
-        const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+// Registers of one 64-key block: unit u of thread t is chunk cc of key `key`, with
+// idx = t + 256 u = cc * 64 + key (consecutive threads take consecutive keys, so the transposed
+// V stores of a wave cover 128 contiguous bytes).  off(key, cc) gives the byte offsets of the
+// K and V chunk, or kOob.
+template <int HD>
+struct KVRegs {
+    uint4 k[AttnTile<HD>::U], v[AttnTile<HD>::U];
+
+    template <typename Off>
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, Off off) {
+        using T = AttnTile<HD>;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            vt[(cc * 8 + 2 * e) * (T::VROW / 2) + key] = static_cast<uint16_t>(w[e] & 0xffffu);
-            vt[(cc * 8 + 2 * e + 1) * (T::VROW / 2) + key] = static_cast<uint16_t>(w[e] >> 16);
+        for (int u = 0; u < T::U; ++u) {
+            const int idx = threadIdx.x + 256 * u;
+            const int cc = idx >> 6, key = idx & 63;
+            uint32_t ok_ = kOob, ov = kOob;
+            if (idx < 64 * T::CH) off(key, cc, ok_, ov);
+            k[u] = buf_load16(rk, ok_);
+            v[u] = buf_load16(rv, ov);
         }
     }
-}
+
+    __device__ __forceinline__ void store(uint8_t* sK, uint8_t* sV) const {
+        using T = AttnTile<HD>;
+        uint16_t* vt = reinterpret_cast<uint16_t*>(sV);
+#pragma unroll
+        for (int u = 0; u < T::U; ++u) {
+            const int idx = threadIdx.x + 256 * u;
+            if (idx >= 64 * T::CH) continue;
+            const int cc = idx >> 6, key = idx & 63;
+            *reinterpret_cast<uint4*>(sK + key * T::KROW + cc * 16) = k[u];
+            const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                vt[(cc * 8 + 2 * e) * (T::VROW / 2) + key] = static_cast<uint16_t>(w[e] & 0xffffu);
+                vt[(cc * 8 + 2 * e + 1) * (T::VROW / 2) + key] = static_cast<uint16_t>(w[e] >> 16);
+            }
+        }
+    }
+};
 
 // One 64-key block of online softmax for the wave's 16 queries.
 // qf: B operand (query lane&15, d = 32s + 8*(lane>>4)); nk valid keys.
@@ -128,19 +150,25 @@ __device__ __forceinline__ void attend_block(const uint8_t* sK, const uint8_t* s
     }
 }
 
+// query fragments of one head row (byte offset qoff in q_c, or kOob)
 template <int HD>
-__device__ __forceinline__ void load_query(const uint16_t* qrow, bool valid, uint4 (&qf)[AttnTile<HD>::KS]) {
+__device__ __forceinline__ void load_query(__amdgpu_buffer_rsrc_t rq, uint32_t qoff, uint4 (&qf)[AttnTile<HD>::KS]) {
     const int g4 = (threadIdx.x & 63) >> 4;
 #pragma unroll
     for (int s = 0; s < AttnTile<HD>::KS; ++s) {
         const int d0 = 32 * s + 8 * g4;
-        qf[s] = (valid && d0 < HD) ? *reinterpret_cast<const uint4*>(qrow + d0) : make_uint4(0, 0, 0, 0);
+        qf[s] = buf_load16(rq, d0 < HD ? qoff + d0 * 2 : kOob);
     }
 }
 
 __device__ __forceinline__ int clamp_count(const int32_t* m_count, int cap) {
     int M = m_count[0];
     return M < 0 ? 0 : (M > cap ? cap : M);
+}
+
+// bytes spanned by a strided prefix view [P][Hkv][HD]
+__device__ __forceinline__ uint32_t view_bytes(int P, int Hkv, int64_t st, int64_t sh, int HD) {
+    return static_cast<uint32_t>(((P - 1) * st + (Hkv - 1) * sh + HD) * 2);
 }
 
 // grid: x = tiles of 64 (slot, head-in-group) queries, y = prefix chunk, z = KV group
@@ -161,8 +189,23 @@ __global__ __launch_bounds__(256) void attn_prefix_kernel(const AttnArgs a) {
     const int qi = q0 + wave * 16 + (lane & 15);
     const bool qvalid = qi < nq;
     const int m = qvalid ? qi / G : 0, h = g * G + (qvalid ? qi % G : 0);
+
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q_c, static_cast<uint32_t>(static_cast<size_t>(a.m_cap) * a.Hq * HD * 2));
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.pk, view_bytes(a.P, a.Hkv, a.pk_st, a.pk_sh, HD));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.pv, view_bytes(a.P, a.Hkv, a.pv_st, a.pv_sh, HD));
+    auto block_off = [&](int kb) {
+        const int nk = min(64, key1 - kb);
+        return [=](int key, int cc, uint32_t& ok_, uint32_t& ov) {
+            if (key < nk) {
+                ok_ = static_cast<uint32_t>(((kb + key) * a.pk_st + g * a.pk_sh + cc * 8) * 2);
+                ov = static_cast<uint32_t>(((kb + key) * a.pv_st + g * a.pv_sh + cc * 8) * 2);
+            }
+        };
+    };
+    KVRegs<HD> kv;
+    kv.load(rk, rv, block_off(key0));
     uint4 qf[T::KS];
-    load_query<HD>(a.q_c + (static_cast<size_t>(m) * a.Hq + h) * HD, qvalid, qf);
+    load_query<HD>(rq, qvalid ? static_cast<uint32_t>((m * a.Hq + h) * HD * 2) : kOob, qf);
 
     float run_m = kNegInf, run_l = 0.f;
     f32x4 o[T::DT];
@@ -170,23 +213,18 @@ __global__ __launch_bounds__(256) void attn_prefix_kernel(const AttnArgs a) {
     for (int dt = 0; dt < T::DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     for (int kb = key0; kb < key1; kb += 64) {
-        const int nk = min(64, key1 - kb);
+        __syncthreads();                           // the previous block is consumed
+        kv.store(sK, sV);
         __syncthreads();
-        stage_kv<HD>(sK, sV, nk, [&](int key, const uint16_t*& kp, const uint16_t*& vp) {
-            kp = a.pk + (kb + key) * a.pk_st + g * a.pk_sh;
-            vp = a.pv + (kb + key) * a.pv_st + g * a.pv_sh;
-        });
-        __syncthreads();
-        attend_block<HD>(sK, sV, nk, qf, a.scale_log2, run_m, run_l, o);
+        if (kb + 64 < key1) kv.load(rk, rv, block_off(kb + 64));   // in flight during the block
+        attend_block<HD>(sK, sV, min(64, key1 - kb), qf, a.scale_log2, run_m, run_l, o);
     }
     run_l += __shfl_xor(run_l, 16, kWave);
     run_l += __shfl_xor(run_l, 32, kWave);
     if (!qvalid) return;
     const size_t base = (static_cast<size_t>(chunk) * a.m_cap + m) * a.Hq + h;
-    if ((lane >> 4) == 0) {
-        a.part_ml[2 * base] = run_m;
-        a.part_ml[2 * base + 1] = run_l;
-    }
+    if ((lane >> 4) == 0)
+        *reinterpret_cast<float2*>(a.part_ml + 2 * base) = make_float2(run_m, run_l);
     float* po = a.part_o + base * HD + 4 * (lane >> 4);
 #pragma unroll
     for (int dt = 0; dt < T::DT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[dt];
@@ -196,6 +234,7 @@ __global__ __launch_bounds__(256) void attn_prefix_kernel(const AttnArgs a) {
 template <int HD>
 __global__ __launch_bounds__(256) void attn_block_kernel(const AttnArgs a) {
     using T = AttnTile<HD>;
+    constexpr int kBatch = 4;                      // prefix chunk states loaded per round trip
     __shared__ __align__(16) uint8_t sK[64 * T::KROW];
     __shared__ __align__(16) uint8_t sV[HD * T::VROW];
     __shared__ int sSlot[64];
@@ -221,23 +260,27 @@ __global__ __launch_bounds__(256) void attn_block_kernel(const AttnArgs a) {
         sSlot[threadIdx.x] = s;
     }
     __syncthreads();
-    stage_kv<HD>(sK, sV, N, [&](int key, const uint16_t*& kp, const uint16_t*& vp) {
-        const int s = sSlot[key];
-        if (s >= 0) {
-            kp = a.k_c + (static_cast<size_t>(s) * a.Hkv + g) * HD;
-            vp = a.v_c + (static_cast<size_t>(s) * a.Hkv + g) * HD;
-        }
+    const uint32_t rows_bytes = static_cast<uint32_t>(static_cast<size_t>(a.m_cap) * a.Hkv * HD * 2);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_c, rows_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_c, rows_bytes);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q_c, static_cast<uint32_t>(static_cast<size_t>(a.m_cap) * a.Hq * HD * 2));
+    KVRegs<HD> kv;
+    kv.load(rk, rv, [&](int key, int cc, uint32_t& ok_, uint32_t& ov) {
+        const int s = key < N ? sSlot[key] : -1;
+        if (s >= 0) ok_ = ov = static_cast<uint32_t>(((s * a.Hkv + g) * HD + cc * 8) * 2);
     });
-    __syncthreads();
-    if (qt >= G * nt16) return;
 
-    const int j = qt / nt16, nt = qt - j * nt16;
+    const bool active = qt < G * nt16;             // wave-uniform
+    const int j = active ? qt / nt16 : 0, nt = active ? qt - j * nt16 : 0;
     const int h = g * G + j;
     const int n = nt * 16 + (lane & 15);
-    const bool nvalid = n < N;
+    const bool nvalid = active && n < N;
     const int qslot = nvalid ? sSlot[n] : -1;
     uint4 qf[T::KS];
-    load_query<HD>(a.q_c + (static_cast<size_t>(qslot < 0 ? 0 : qslot) * a.Hq + h) * HD, qslot >= 0, qf);
+    load_query<HD>(rq, qslot >= 0 ? static_cast<uint32_t>((qslot * a.Hq + h) * HD * 2) : kOob, qf);
+    kv.store(sK, sV);
+    __syncthreads();
+    if (!active) return;
 
     float run_m = kNegInf, run_l = 0.f;
     f32x4 o[T::DT];
@@ -246,27 +289,40 @@ __global__ __launch_bounds__(256) void attn_block_kernel(const AttnArgs a) {
     attend_block<HD>(sK, sV, N, qf, a.scale_log2, run_m, run_l, o);
     run_l += __shfl_xor(run_l, 16, kWave);
     run_l += __shfl_xor(run_l, 32, kWave);
-    if (!nvalid) return;
 
-    // merge with the prefix chunk states of the source slot, chunks in ascending order
+    // merge the prefix chunk states of the source slot, in ascending chunk order, by online
+    // log-sum-exp rescaling
     const int ps = qslot < 0 ? 0 : qslot;
-    float mx = run_m;
-    for (int c = 0; c < a.n_chunks; ++c)
-        mx = fmaxf(mx, a.part_ml[2 * ((static_cast<size_t>(c) * a.m_cap + ps) * a.Hq + h)]);
-    const float wb = exp2f(run_m - mx);
-    float L = run_l * wb;
+    const __amdgpu_buffer_rsrc_t rml =
+        make_rsrc(a.part_ml, static_cast<uint32_t>(static_cast<size_t>(a.n_chunks) * a.m_cap * a.Hq * 8));
+    const __amdgpu_buffer_rsrc_t ro =
+        make_rsrc(a.part_o, static_cast<uint32_t>(static_cast<size_t>(a.n_chunks) * a.m_cap * a.Hq * HD * 4));
+    for (int c0 = 0; c0 < a.n_chunks; c0 += kBatch) {
+        float2 ml[kBatch];
+        f32x4 co[kBatch][T::DT];
 #pragma unroll
-    for (int dt = 0; dt < T::DT; ++dt) o[dt] *= wb;
-    for (int c = 0; c < a.n_chunks; ++c) {
-        const size_t base = (static_cast<size_t>(c) * a.m_cap + ps) * a.Hq + h;
-        const float wc = exp2f(a.part_ml[2 * base] - mx);
-        L += a.part_ml[2 * base + 1] * wc;
-        const float* po = a.part_o + base * HD + 4 * (lane >> 4);
+        for (int b = 0; b < kBatch; ++b) {
+            const bool ok = c0 + b < a.n_chunks;
+            const uint32_t base = static_cast<uint32_t>(((c0 + b) * a.m_cap + ps) * a.Hq + h);
+            ml[b] = __builtin_bit_cast(float2, buf_load8(rml, ok ? base * 8 : kOob));
 #pragma unroll
-        for (int dt = 0; dt < T::DT; ++dt) o[dt] += *reinterpret_cast<const f32x4*>(po + dt * 16) * wc;
+            for (int dt = 0; dt < T::DT; ++dt)
+                co[b][dt] = buf_loadf4(ro, ok ? (base * HD + dt * 16 + 4 * (lane >> 4)) * 4 : kOob);
+        }
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            if (c0 + b >= a.n_chunks) break;
+            const float nm = fmaxf(run_m, ml[b].x);
+            const float wa = exp2f(run_m - nm), wc = exp2f(ml[b].x - nm);
+            run_l = run_l * wa + ml[b].y * wc;
+#pragma unroll
+            for (int dt = 0; dt < T::DT; ++dt) o[dt] = o[dt] * wa + co[b][dt] * wc;
+            run_m = nm;
+        }
     }
+    if (!nvalid) return;
     const bool bad = (qslot < 0) || (sBad != 0);
-    const float invL = bad ? __builtin_nanf("") : 1.0f / L;
+    const float invL = bad ? __builtin_nanf("") : 1.0f / run_l;
     const int row = i * N + n;
     uint16_t* dst = a.attn + (static_cast<size_t>(row) * a.Hq + h) * HD + 4 * (lane >> 4);
 #pragma unroll
@@ -275,7 +331,7 @@ __global__ __launch_bounds__(256) void attn_block_kernel(const AttnArgs a) {
         *reinterpret_cast<uint2*>(dst + dt * 16) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     }
     if (a.lse && (lane >> 4) == 0)
-        a.lse[static_cast<size_t>(row) * a.Hq + h] = bad ? __builtin_nanf("") : (mx + log2f(L)) * 0.69314718055994531f;
+        a.lse[static_cast<size_t>(row) * a.Hq + h] = bad ? __builtin_nanf("") : (run_m + log2f(run_l)) * 0.69314718055994531f;
 }
 
 }  // namespace
