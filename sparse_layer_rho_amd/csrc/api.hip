@@ -42,22 +42,30 @@ Dims dims_of(const specfold_shape& s) {
     return d;
 }
 
-// Tile shape, column groups and K split of one projection.  A workgroup streams 64 weight
-// rows (32 output columns of SwiGLU) against 128 activation rows (64 when R <= 64) through a
-// three-slot LDS ring, so two workgroups share a CU and hide each other's waits.  Partial-sum
-// projections split K until about 384 workgroups are busy (at least 4 stages of 64 per split).
-GemmCfg pick_gemm(int n_cols, int k, int max_rows, int busy_chunks, bool swiglu) {
+// Tile shape, column groups and K split of one projection.  A workgroup streams 64 weight rows
+// (32 output columns of SwiGLU) against a chunk of activation rows through small LDS rings, so
+// two or three workgroups share a CU and hide each other's waits.  Measured on the 1.5B shapes:
+// the recompute projections run two 64-row chunks per column group (M ~ 100), the gate/up weight
+// stage spans 256 bytes of every row, and the long-K down projection keeps 128-row chunks.
+// Partial-sum projections split K until about 384 workgroups are busy.
+enum GemmKind { GEMM_QKV, GEMM_O, GEMM_GATE_UP, GEMM_DOWN };
+
+GemmCfg pick_gemm(GemmKind kind, int n_cols, int k, int max_rows, int busy_chunks) {
     GemmCfg c{};
-    c.swiglu = swiglu;
-    c.ntw = 4; c.wn = 1; c.tm = 2; c.nb = 3;
-    if (max_rows <= 64) { c.ntw = 2; c.wn = 2; c.tm = 2; c.nb = 3; }
+    c.swiglu = kind == GEMM_GATE_UP;
+    c.ntw = 4; c.wn = 1;
+    if (kind == GEMM_GATE_UP) { c.tm = 1; c.ksub = 2; c.nbw = 2; c.nba = 2; }
+    else if (kind == GEMM_DOWN) { c.tm = 2; c.ksub = 1; c.nbw = 4; c.nba = 2; }
+    else { c.tm = 1; c.ksub = 1; c.nbw = 3; c.nba = 2; }
+    if (max_rows <= 64) { c.ntw = 2; c.wn = 2; c.tm = 2; c.ksub = 2; c.nbw = 2; c.nba = 2; }
     const int cap = gemm_group_cols(c);
     c.groups = (n_cols + cap - 1) / cap;
     c.splits = 1;
-    if (!swiglu) {
-        const int busy = c.groups * (busy_chunks > 0 ? busy_chunks : 1);
+    if (!c.swiglu) {
+        const int chunks = (max_rows + gemm_chunk_rows(c) - 1) / gemm_chunk_rows(c);
+        const int busy = c.groups * (busy_chunks < chunks ? busy_chunks : chunks);
         int s = (384 + busy / 2) / busy;
-        int smax = (k + 63) / 64 / 4;
+        int smax = (k + 64 * c.ksub - 1) / (64 * c.ksub) / (c.ksub == 1 ? 4 : 2);
         if (smax > 32) smax = 32;                          // the epilogues batch up to 32 splits
         if (s > smax) s = smax;
         c.splits = s < 1 ? 1 : s;
@@ -67,12 +75,11 @@ GemmCfg pick_gemm(int n_cols, int k, int max_rows, int busy_chunks, bool swiglu)
 
 Layout layout_of(const Dims& d) {
     Layout L;
-    // the recompute projections expect one busy row chunk (folded M); o_proj has all R rows
-    L.c_qkv = pick_gemm(d.Nq, d.D, d.R, 1, false);
-    const int o_chunks = (d.R + gemm_chunk_rows(L.c_qkv) - 1) / gemm_chunk_rows(L.c_qkv);
-    L.c_o = pick_gemm(d.D, d.Do, d.R, o_chunks, false);
-    L.c_gu = pick_gemm(d.F, d.D, d.R, 1, true);
-    L.c_down = pick_gemm(d.D, d.F, d.R, 1, false);
+    // the recompute projections expect about 128 busy rows (folded M); o_proj has all R rows
+    L.c_qkv = pick_gemm(GEMM_QKV, d.Nq, d.D, d.R, 2);
+    L.c_o = pick_gemm(GEMM_O, d.D, d.Do, d.R, 1 << 20);
+    L.c_gu = pick_gemm(GEMM_GATE_UP, d.F, d.D, d.R, 2);
+    L.c_down = pick_gemm(GEMM_DOWN, d.D, d.F, d.R, 1);
     L.s_qkv = L.c_qkv.splits; L.s_o = L.c_o.splits; L.s_down = L.c_down.splits;
     L.chunk_len = d.P <= 1024 ? 128 : 512;
     L.n_chunks = d.P > 0 ? (d.P + L.chunk_len - 1) / L.chunk_len : 0;

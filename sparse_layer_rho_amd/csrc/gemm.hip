@@ -36,8 +36,8 @@ namespace {
 // wrap back into range together.
 constexpr uint32_t kOobRow = kOob;
 constexpr uint32_t kOobK = 0x80000000u;
-constexpr int kStageK = 64;                 // K elements per stage
-constexpr int kRowB = 128;                  // bytes of one row in one stage
+constexpr int kStageK = 64;                 // K elements per compute stage
+constexpr int kRowB = 128;                  // bytes of one activation row in one compute stage
 
 enum { EPI_PARTIAL = 0, EPI_SWIGLU = 1 };
 
@@ -74,11 +74,11 @@ __device__ __forceinline__ void lds_wait(u32x4 (&v)[C]) {
 }
 
 // fragments of N consecutive 16-row tiles (rows 16 apart) at addr
-template <int N, int I = 0>
+template <int N, int ROWB, int I = 0>
 __device__ __forceinline__ void read_tiles(u32x4* f, uint32_t addr) {
     if constexpr (I < N) {
-        f[I] = lds_read16<I * 16 * kRowB>(addr);
-        read_tiles<N, I + 1>(f, addr);
+        f[I] = lds_read16<I * 16 * ROWB>(addr);
+        read_tiles<N, ROWB, I + 1>(f, addr);
     }
 }
 
@@ -90,14 +90,15 @@ __device__ __forceinline__ void vm_wait() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// vm_wait<QW * n> for a runtime n in [0, MAXN]
-template <int QW, int MAXN>
-__device__ __forceinline__ void vm_wait_stages(int n) {
-    if constexpr (MAXN <= 0) {
+// wait until at most n of this wave's vector-memory operations are outstanding, for a runtime n
+// in [0, MAX] (rounded down to a multiple of STEP: waiting for more is always safe)
+template <int STEP, int MAX>
+__device__ __forceinline__ void vm_wait_le(int n) {
+    if constexpr (MAX <= 0) {
         vm_wait<0>();
     } else {
-        if (n >= MAXN) vm_wait<QW * MAXN>();
-        else vm_wait_stages<QW, MAXN - 1>(n);
+        if (n >= MAX) vm_wait<MAX>();
+        else vm_wait_le<STEP, MAX - STEP>(n);
     }
 }
 
@@ -166,27 +167,37 @@ __device__ int compact_in_lds(const GemmArgs& p, int32_t* s_rows, int* s_tot, bo
 }
 
 // Tile shape: WN x WM waves; each wave owns NTW 16-row weight tiles and TM 16-row activation
-// tiles; NB stage slots in the ring.
-template <int NTW, int WN, int TM, int NB>
+// tiles.  Weights and activations have rings of their own.  A weight stage spans KSUB compute
+// stages (KSUB * 128 contiguous bytes of every weight row: HBM serves runs of 256 bytes and
+// more far better than 128-byte pieces of many rows), NBW weight slots keep NBW-1 weight
+// stages in flight; activations (L2-resident) move per compute stage through NBA slots.
+template <int NTW, int WN, int TM, int KSUB, int NBW, int NBA>
 struct Tile {
     static constexpr int WM = 4 / WN;              // waves along the row tiles
     static constexpr int NT = NTW * WN;            // weight tiles per workgroup
     static constexpr int WROWS = 16 * NT;          // weight rows per workgroup
     static constexpr int MP = 16 * TM * WM;        // activation rows per workgroup
-    static constexpr int QWW = WROWS / 32;         // ring loads per wave per stage: weights
-    static constexpr int QW = (WROWS + MP) / 32;   //   ... weights + activations
-    static constexpr int SLOT = (WROWS + MP) * kRowB;
-    static constexpr int LDS = NB * SLOT;
+    static constexpr int WRB = KSUB * kRowB;       // bytes of a weight row in one weight stage
+    static constexpr int WLPR = WRB / 16;          // lanes per weight row in one ring load
+    static constexpr int QW = WROWS * WRB / 4096;  // ring loads per wave per weight stage
+    static constexpr int QA = MP / 32;             // ring loads per wave per compute stage
+    static constexpr int WSLOT = WROWS * WRB;
+    static constexpr int ASLOT = MP * kRowB;
+    static constexpr int LDS = NBW * WSLOT + NBA * ASLOT;
+    static constexpr int LWU = NBW - 1, LA = NBA - 1;
+    // most loads issued after an awaited activation stage (see the ring loop)
+    static constexpr int MAXN = (LA - 1) * QA + ((LA + KSUB - 1) / KSUB) * QW;
     static_assert(WN == 1 || WN == 2 || WN == 4, "wave grid");
-    static_assert(WROWS % 32 == 0 && MP % 32 == 0, "ring loads cover 8 rows per wave");
+    static_assert(KSUB == 1 || KSUB == 2 || KSUB == 4, "weight stage");
+    static_assert(WROWS * WRB % 4096 == 0 && MP % 32 == 0, "ring loads of 1 KB per wave");
     static_assert(TM >= 1 && NTW >= 1 && NTW * TM <= 16, "accumulators per wave");
-    static_assert(NB >= 2 && QW * (NB - 2) < 64, "ring depth");
+    static_assert(NBA >= 2 && NBW >= 2 && KSUB * LWU > LA && MAXN < 64, "ring depths");
 };
 
-template <int NTW, int WN, int TM, int NB, int EPI>
+template <int NTW, int WN, int TM, int KSUB, int NBW, int NBA, int EPI>
 __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
-    using T = Tile<NTW, WN, TM, NB>;
-    constexpr int WROWS = T::WROWS, MP = T::MP, QWW = T::QWW, QW = T::QW, SLOT = T::SLOT;
+    using T = Tile<NTW, WN, TM, KSUB, NBW, NBA>;
+    constexpr int WROWS = T::WROWS, MP = T::MP, QW = T::QW, QA = T::QA;
     static_assert(EPI != EPI_SWIGLU || NTW % 2 == 0, "SwiGLU tiles come in gate/up pairs");
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ int s_tot[4];
@@ -222,10 +233,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
     const int c0 = static_cast<int>(static_cast<int64_t>(g) * (ncols / 4) / p.n_groups) * 4;
     const int c1 = static_cast<int>(static_cast<int64_t>(g + 1) * (ncols / 4) / p.n_groups) * 4;
 
-    // K range of this split, in whole stages
-    const int nst_all = (p.K + kStageK - 1) / kStageK;
-    const int st_begin = static_cast<int>(static_cast<int64_t>(y) * nst_all / S);
-    const int nst = static_cast<int>(static_cast<int64_t>(y + 1) * nst_all / S) - st_begin;
+    // K range of this split: whole weight stages; compute stages inside it
+    const int nws_all = (p.K + KSUB * kStageK - 1) / (KSUB * kStageK);
+    const int ws_begin = static_cast<int>(static_cast<int64_t>(y) * nws_all / S);
+    const int nws = static_cast<int>(static_cast<int64_t>(y + 1) * nws_all / S) - ws_begin;
+    const int k_begin = ws_begin * KSUB * kStageK;
+    const int k_stop = min(p.K, (ws_begin + nws) * KSUB * kStageK);
+    const int nst = k_stop > k_begin ? (k_stop - k_begin + kStageK - 1) / kStageK : 0;
 
     // weight row of slot row r (r < WROWS), or -1 past the group.  SwiGLU slots interleave
     // [gate 16 | up 16] pairs, so a wave's tile pair holds the gate and up rows of 16 columns.
@@ -238,57 +252,81 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
         return col < c1 ? col : -1;
     };
 
-    // ---- ring loads: load q of this wave fills slot rows (q*4 + wave)*8 .. +8; lane l takes row
-    // (l >> 3) of those 8 and physical chunk l & 7, which holds logical chunk (l & 7) ^ (row & 7)
+    // ---- ring loads (1 KB per wave each).  Weight load q of this wave fills weight-slot rows
+    // (q*4 + wave) * (1024 / WRB) + lane / WLPR; the lane takes physical chunk lane % WLPR of the
+    // row, which holds logical chunk (lane % WLPR) ^ (row & 15).  Activation load q fills slot
+    // rows (q*4 + wave)*8 + lane/8, physical chunk lane & 7 = logical chunk (lane & 7) ^ (row & 7).
+    constexpr int WLPR = T::WLPR, RPL = 1024 / T::WRB;     // weight rows per load
     const __amdgpu_buffer_rsrc_t rW = make_rsrc(p.W, static_cast<uint32_t>(static_cast<size_t>(p.Nout) * p.K * 2));
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, static_cast<uint32_t>(static_cast<size_t>(p.a_row_limit) * p.lda * 2));
-    const int lchunk = (lane & 7) ^ ((lane >> 3) & 7);
-    uint32_t roff[QW];
+    uint32_t woff[QW], aoff[QA];
+    int wlk[QW];                                   // logical K offset of the lane's weight chunk
 #pragma unroll
     for (int q = 0; q < QW; ++q) {
-        const int r = (q * 4 + wave) * 8 + (lane >> 3);
-        uint32_t o = kOobRow;
-        if (q < QWW) {
-            const int gr = w_row(r);
-            if (gr >= 0) o = static_cast<uint32_t>(static_cast<size_t>(gr) * p.K * 2);
-        } else {
-            const int m = r - WROWS;
-            if (m < mrows) {
-                const int src = fused ? s_rows[m0 + m] : (p.a_rows ? p.a_rows[m0 + m] : m0 + m);
-                if (src >= 0 && src < p.a_row_limit) o = static_cast<uint32_t>(static_cast<size_t>(src) * p.lda * 2);
-            }
-        }
-        roff[q] = o + static_cast<uint32_t>(lchunk * 16);
+        const int r = (q * 4 + wave) * RPL + lane / WLPR;
+        wlk[q] = ((lane % WLPR) ^ (r & (WLPR - 1) & 15)) * 8;
+        const int gr = w_row(r);
+        woff[q] = (gr >= 0 ? static_cast<uint32_t>(static_cast<size_t>(gr) * p.K * 2) : kOobRow) +
+                  static_cast<uint32_t>(wlk[q] * 2);
     }
-    auto issue = [&](int s) {                      // stage s of this split -> slot s % NB
-        uint8_t* slot = smem + (s % NB) * SLOT;
-        const int k0 = (st_begin + s) * kStageK;
-        const uint32_t kb = k0 + lchunk * 8 < p.K ? static_cast<uint32_t>(k0 * 2) : kOobK;
+    const int alk = ((lane & 7) ^ ((lane >> 3) & 7)) * 8;
 #pragma unroll
-        for (int q = 0; q < QW; ++q) dma16(q < QWW ? rW : rA, slot + (q * 4 + wave) * 1024, roff[q] + kb);
+    for (int q = 0; q < QA; ++q) {
+        const int m = (q * 4 + wave) * 8 + (lane >> 3);
+        uint32_t o = kOobRow;
+        if (m < mrows) {
+            const int src = fused ? s_rows[m0 + m] : (p.a_rows ? p.a_rows[m0 + m] : m0 + m);
+            if (src >= 0 && src < p.a_row_limit) o = static_cast<uint32_t>(static_cast<size_t>(src) * p.lda * 2);
+        }
+        aoff[q] = o + static_cast<uint32_t>(alk * 2);
+    }
+    uint8_t* const wring = smem;
+    uint8_t* const aring = smem + NBW * T::WSLOT;
+    auto issue_w = [&](int u) {                    // weight stage u -> slot u % NBW
+        uint8_t* slot = wring + (u % NBW) * T::WSLOT;
+        const int k0 = k_begin + u * KSUB * kStageK;
+#pragma unroll
+        for (int q = 0; q < QW; ++q) {
+            const uint32_t kb = k0 + wlk[q] < k_stop ? static_cast<uint32_t>(k0 * 2) : kOobK;
+            dma16(rW, slot + (q * 4 + wave) * 1024, woff[q] + kb);
+        }
+    };
+    auto issue_a = [&](int t) {                    // activation stage t -> slot t % NBA
+        uint8_t* slot = aring + (t % NBA) * T::ASLOT;
+        const int k0 = k_begin + t * kStageK;
+        const uint32_t kb = k0 + alk < k_stop ? static_cast<uint32_t>(k0 * 2) : kOobK;
+#pragma unroll
+        for (int q = 0; q < QA; ++q) dma16(rA, slot + (q * 4 + wave) * 1024, aoff[q] + kb);
     };
 
-    // ---- fragment reads: lane reads row (lane & 15) of a 16-row tile, logical chunk
-    // 4t + (lane >> 4) in k-step t, which sits at physical chunk (that ^ (row & 7))
+    // ---- fragment reads: lane reads row fr = lane & 15 of a 16-row tile at logical chunk
+    // 8j + 4kk + (lane >> 4) of compute stage j of the weight stage, k-step kk (weights: XOR row
+    // & 15 over the stage's WLPR chunks; XOR with j << 7 moves to compute stage j), or 4kk +
+    // (lane >> 4) (activations: XOR row & 7)
     const int wn = wave % WN, wm = wave / WN;
     const int fr = lane & 15, fc = lane >> 4;
-    const uint32_t lb0 = lds_addr(smem) + fr * kRowB + ((fc ^ (fr & 7)) << 4);
-    const uint32_t lb1 = lds_addr(smem) + fr * kRowB + (((4 + fc) ^ (fr & 7)) << 4);
+    const uint32_t wl0 = fr * T::WRB + ((fc ^ (fr & (WLPR - 1))) << 4);
+    const uint32_t wl1 = fr * T::WRB + (((4 + fc) ^ (fr & (WLPR - 1))) << 4);
+    const uint32_t al0 = fr * kRowB + ((fc ^ (fr & 7)) << 4);
+    const uint32_t al1 = fr * kRowB + (((4 + fc) ^ (fr & 7)) << 4);
+    const uint32_t wbase = lds_addr(wring) + wn * NTW * 16 * T::WRB;
+    const uint32_t abase = lds_addr(aring) + wm * TM * 16 * kRowB;
     f32x4 acc[TM][NTW];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int b) {
-        const uint32_t sw = static_cast<uint32_t>(b * SLOT + wn * NTW * 16 * kRowB);
-        const uint32_t sa = static_cast<uint32_t>(b * SLOT + (WROWS + wm * TM * 16) * kRowB);
+    auto compute = [&](int t) {
+        const uint32_t j7 = static_cast<uint32_t>((t % KSUB) << 7);
+        const uint32_t sw = wbase + static_cast<uint32_t>(((t / KSUB) % NBW) * T::WSLOT);
+        const uint32_t sa = abase + static_cast<uint32_t>((t % NBA) * T::ASLOT);
         u32x4 f0[NTW + TM], f1[NTW + TM];
         // k-step 0 fragments, then k-step 1: lgkmcnt(NTW + TM) leaves only the second group pending
-        read_tiles<NTW>(f0, lb0 + sw);
-        read_tiles<TM>(f0 + NTW, lb0 + sa);
-        read_tiles<NTW>(f1, lb1 + sw);
-        read_tiles<TM>(f1 + NTW, lb1 + sa);
+        read_tiles<NTW, T::WRB>(f0, (wl0 ^ j7) + sw);
+        read_tiles<TM, kRowB>(f0 + NTW, al0 + sa);
+        read_tiles<NTW, T::WRB>(f1, (wl1 ^ j7) + sw);
+        read_tiles<TM, kRowB>(f1 + NTW, al1 + sa);
         lds_wait<NTW + TM>(f0);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -302,16 +340,30 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
             for (int j = 0; j < NTW; ++j) acc[i][j] = mma(f1[j], f1[NTW + i], acc[i][j]);
     };
 
-    // ---- the ring: NB-1 stages in flight ahead of the one being multiplied
+    // ---- the rings.  Prologue: weight stages 0 .. LWU-1, then activation stages 0 .. LA-1.
+    // Iteration t waits for activation stage t (and with it everything requested earlier),
+    // then requests activation stage t + LA and, when t starts weight stage u, weight stage
+    // u + LWU.  Weight stage t / KSUB is always requested before activation stage t
+    // (KSUB * LWU > LA), so one wait covers both; it leaves out exactly the loads this wave
+    // issued after activation stage t: activation stages t+1 .. t+LA-1 and the weight stages
+    // requested in iterations max(0, t-LA) .. t-1.
+    constexpr int LWU = T::LWU, LA = T::LA;
 #pragma unroll
-    for (int s = 0; s < NB - 1; ++s)
-        if (s < nst) issue(s);
-    for (int s = 0; s < nst; ++s) {
-        const int after = min(NB - 2, nst - 1 - s);   // stages this wave issued after s
-        vm_wait_stages<QW, NB - 2>(after);
-        block_barrier();                              // stage s landed for every wave; slot of s-1 free
-        if (s + NB - 1 < nst) issue(s + NB - 1);
-        compute(s % NB);
+    for (int u = 0; u < LWU; ++u)
+        if (u < nws) issue_w(u);
+#pragma unroll
+    for (int t = 0; t < LA; ++t)
+        if (t < nst) issue_a(t);
+    for (int t = 0; t < nst; ++t) {
+        int n_w = 0;
+        for (int i = max(0, t - LA); i < t; ++i)
+            if (i % KSUB == 0 && i / KSUB + LWU < nws) ++n_w;
+        const int n_a = max(0, min(LA - 1, nst - 1 - t));
+        vm_wait_le<(QA < QW ? QA : QW), T::MAXN>(n_a * QA + n_w * QW);
+        block_barrier();                           // stage t landed for every wave; slots of t-1 free
+        if (t + LA < nst) issue_a(t + LA);
+        if (t % KSUB == 0 && t / KSUB + LWU < nws) issue_w(t / KSUB + LWU);
+        compute(t);
     }
 
     // ---- epilogue: lane holds C[row m][cols n0 + 4*(lane>>4) + q] of tile (i, j)
@@ -344,14 +396,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
     }
 }
 
-template <int NTW, int WN, int TM, int NB, int EPI>
+template <int NTW, int WN, int TM, int KSUB, int NBW, int NBA, int EPI>
 hipError_t launch_shape(GemmArgs a, int groups, int splits, hipStream_t st) {
-    using T = Tile<NTW, WN, TM, NB>;
+    using T = Tile<NTW, WN, TM, KSUB, NBW, NBA>;
     a.n_groups = groups;
     a.m_chunks = (a.m_cap + T::MP - 1) / T::MP;
     if (a.m_chunks < 1) a.m_chunks = 1;
     const size_t lds = static_cast<size_t>(T::LDS) + (a.fc_fold ? static_cast<size_t>(a.fc_R) * 4 : 0);
-    auto kern = gemm_kernel<NTW, WN, TM, NB, EPI>;
+    auto kern = gemm_kernel<NTW, WN, TM, KSUB, NBW, NBA, EPI>;
     static size_t configured = 0;   // dynamic-LDS cap raised so far for this kernel
     if (lds > configured) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -375,14 +427,15 @@ int gemm_group_cols(const GemmCfg& c) {
 }
 
 size_t gemm_lds_bytes(const GemmCfg& c) {
-    return static_cast<size_t>(c.nb) * (16 * c.ntw * c.wn + gemm_chunk_rows(c)) * kRowB;
+    return (static_cast<size_t>(c.nbw) * 16 * c.ntw * c.wn * c.ksub + static_cast<size_t>(c.nba) * gemm_chunk_rows(c)) *
+           kRowB;
 }
 
 hipError_t launch_gemm(const GemmArgs& a, const GemmCfg& c, hipStream_t st) {
-#define SPECFOLD_GEMM_CASE(NTW_, WN_, TM_, NB_)                                                 \
-    if (c.ntw == NTW_ && c.wn == WN_ && c.tm == TM_ && c.nb == NB_)                             \
-        return c.swiglu ? launch_shape<NTW_, WN_, TM_, NB_, EPI_SWIGLU>(a, c.groups, 1, st)     \
-                        : launch_shape<NTW_, WN_, TM_, NB_, EPI_PARTIAL>(a, c.groups, c.splits, st);
+#define SPECFOLD_GEMM_CASE(NTW_, WN_, TM_, KS_, NBW_, NBA_)                                         \
+    if (c.ntw == NTW_ && c.wn == WN_ && c.tm == TM_ && c.ksub == KS_ && c.nbw == NBW_ && c.nba == NBA_)  \
+        return c.swiglu ? launch_shape<NTW_, WN_, TM_, KS_, NBW_, NBA_, EPI_SWIGLU>(a, c.groups, 1, st)   \
+                        : launch_shape<NTW_, WN_, TM_, KS_, NBW_, NBA_, EPI_PARTIAL>(a, c.groups, c.splits, st);
     SPECFOLD_GEMM_CASES(SPECFOLD_GEMM_CASE)
 #undef SPECFOLD_GEMM_CASE
     return hipErrorInvalidValue;

@@ -84,16 +84,16 @@ struct GemmArgs {
 // Tile shape of one launch: a workgroup covers the output columns of one of `groups` even
 // column groups (at most gemm_group_cols), a chunk of gemm_chunk_rows rows and one of `splits`
 // K ranges (grid.y; the partial buffer holds splits * m_cap * Nout floats).  Its 4 waves form a
-// wn x (4/wn) grid; a wave owns ntw 16-row weight tiles and tm 16-row activation tiles; nb stage
-// slots form the LDS ring.  swiglu: the gate/up GEMM (Nout = 2F, gate rows then up rows, no K
+// wn x (4/wn) grid; a wave owns ntw 16-row weight tiles and tm 16-row activation tiles; a weight
+// stage spans ksub compute stages of 64 K; nbw weight and nba activation slots form the LDS rings.  swiglu: the gate/up GEMM (Nout = 2F, gate rows then up rows, no K
 // split) writing act = silu(g) * u.
 struct GemmCfg {
-    int ntw, wn, tm, nb, groups, splits;
+    int ntw, wn, tm, ksub, nbw, nba, groups, splits;
     bool swiglu;
 };
-// the (ntw, wn, tm, nb) shapes compiled
+// the (ntw, wn, tm, ksub, nbw, nba) shapes compiled
 #define SPECFOLD_GEMM_CASES(X) \
-    X(4, 1, 2, 3) X(2, 2, 2, 3)
+    X(4, 1, 1, 2, 2, 2) X(4, 1, 1, 1, 3, 2) X(4, 1, 2, 1, 4, 2) X(2, 2, 2, 2, 2, 2)
 int gemm_chunk_rows(const GemmCfg& c);
 int gemm_group_cols(const GemmCfg& c);
 size_t gemm_lds_bytes(const GemmCfg& c);
