@@ -375,7 +375,9 @@ const char* specfold_stage_name(int stage) {
 int specfold_event_create(void** event) {
     if (!event) return SPECFOLD_ERR_NULL;
     hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) return SPECFOLD_ERR_HIP;
+    // timing only: no system-scope fence at record, so the event does not add a cache
+    // writeback/invalidate to the launch it brackets
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return SPECFOLD_ERR_HIP;
     *event = e;
     return SPECFOLD_OK;
 }
