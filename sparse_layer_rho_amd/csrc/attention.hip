@@ -278,6 +278,28 @@ __global__ __launch_bounds__(256) void attn_block_kernel(const AttnArgs a) {
     const int qslot = nvalid ? sSlot[n] : -1;
     uint4 qf[T::KS];
     load_query<HD>(rq, qslot >= 0 ? static_cast<uint32_t>((qslot * a.Hq + h) * HD * 2) : kOob, qf);
+
+    // prefix chunk states of the source slot: the first batch is requested now, so it arrives
+    // while the block part is computed
+    const int ps = qslot < 0 ? 0 : qslot;
+    const __amdgpu_buffer_rsrc_t rml =
+        make_rsrc(a.part_ml, static_cast<uint32_t>(static_cast<size_t>(a.n_chunks) * a.m_cap * a.Hq * 8));
+    const __amdgpu_buffer_rsrc_t ro =
+        make_rsrc(a.part_o, static_cast<uint32_t>(static_cast<size_t>(a.n_chunks) * a.m_cap * a.Hq * HD * 4));
+    float2 ml[kBatch];
+    f32x4 co[kBatch][T::DT];
+    auto load_states = [&](int c0) {
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const bool ok = active && c0 + b < a.n_chunks;
+            const uint32_t base = static_cast<uint32_t>(((c0 + b) * a.m_cap + ps) * a.Hq + h);
+            ml[b] = __builtin_bit_cast(float2, buf_load8(rml, ok ? base * 8 : kOob));
+#pragma unroll
+            for (int dt = 0; dt < T::DT; ++dt)
+                co[b][dt] = buf_loadf4(ro, ok ? (base * HD + dt * 16 + 4 * (lane >> 4)) * 4 : kOob);
+        }
+    };
+    load_states(0);
     kv.store(sK, sV);
     __syncthreads();
     if (!active) return;
@@ -290,25 +312,9 @@ __global__ __launch_bounds__(256) void attn_block_kernel(const AttnArgs a) {
     run_l += __shfl_xor(run_l, 16, kWave);
     run_l += __shfl_xor(run_l, 32, kWave);
 
-    // merge the prefix chunk states of the source slot, in ascending chunk order, by online
-    // log-sum-exp rescaling
-    const int ps = qslot < 0 ? 0 : qslot;
-    const __amdgpu_buffer_rsrc_t rml =
-        make_rsrc(a.part_ml, static_cast<uint32_t>(static_cast<size_t>(a.n_chunks) * a.m_cap * a.Hq * 8));
-    const __amdgpu_buffer_rsrc_t ro =
-        make_rsrc(a.part_o, static_cast<uint32_t>(static_cast<size_t>(a.n_chunks) * a.m_cap * a.Hq * HD * 4));
+    // merge the prefix chunk states in ascending chunk order by online log-sum-exp rescaling
     for (int c0 = 0; c0 < a.n_chunks; c0 += kBatch) {
-        float2 ml[kBatch];
-        f32x4 co[kBatch][T::DT];
-#pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-            const bool ok = c0 + b < a.n_chunks;
-            const uint32_t base = static_cast<uint32_t>(((c0 + b) * a.m_cap + ps) * a.Hq + h);
-            ml[b] = __builtin_bit_cast(float2, buf_load8(rml, ok ? base * 8 : kOob));
-#pragma unroll
-            for (int dt = 0; dt < T::DT; ++dt)
-                co[b][dt] = buf_loadf4(ro, ok ? (base * HD + dt * 16 + 4 * (lane >> 4)) * 4 : kOob);
-        }
+        if (c0 > 0) load_states(c0);
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
             if (c0 + b >= a.n_chunks) break;
