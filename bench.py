@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--stage-calls", type=int, default=30, help="eager calls timed per launch with events")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration runs)")
+    ap.add_argument("--layers", type=int, default=0, help="stack workloads: layers (default: the workload's)")
+    ap.add_argument("--stack-steps", type=int, default=0, help="stack workloads: steps (default: the workload's)")
+    ap.add_argument("--no-gate-flat", action="store_true", help="skip the large flat gate/compaction timing")
     return ap.parse_args()
 
 
@@ -62,6 +65,10 @@ def main():
     from synth import WORKLOADS, bf16_round, layer_weights, prefix_kv, step_inputs
 
     wl = WORKLOADS[args.workload]
+    if wl.layers > 1 or args.layers > 1:
+        return stack_bench(args, wl)
+    if wl.branch_sweep:
+        return sweep_bench(args, wl)
     sh = wl.shape
     R, D, F = sh.rows, sh.hidden, sh.ffn
     dev = torch.device("cuda:0")
@@ -224,6 +231,9 @@ def main():
         "wall_ms_per_step": round(folded["wall_ms_per_step"], 5),
     }
 
+    if not args.no_gate_flat:
+        out["gate_flat"] = gate_flat_leg(torch, sf, dev)
+
     if args.copy_probe_mb > 0:
         n = args.copy_probe_mb * (1 << 20) // 4
         a = torch.empty(n, dtype=torch.float32, device=dev).uniform_()
@@ -237,6 +247,269 @@ def main():
         out["cpu_baseline"], out["verified"] = cpu_baseline_leg(
             sh, wl, parent, H_host, w_host, pk_h, pv_h, results[wl.delta], args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def graph_time(torch, fns, reps, warmup_s=0.5):
+    """Capture fns (a list of callables launching on the current stream) in one graph; replay it,
+    untimed for warmup_s, then `reps` times between events.  Returns ms per replay."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warmup_s:
+        g.replay()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del g
+    return ms
+
+
+def gate_flat_leg(torch, sf, dev):
+    """Gate and compaction alone on a large flattened input, as bandwidth evidence: 9 branches of
+    16384 positions at D = 1536 (453 MB of H) for the gate; 64 x 262144 rows for the compaction."""
+    from synth import Shape
+    sh = Shape(9, 16384, 1536, 12, 2, 128, 8960, 0)
+    R, D = sh.rows, sh.hidden
+    parent = [-1, 0, 0, 1, 1, 2, 3, 4, 5]
+    H = torch.randn((R, D), device=dev).to(torch.bfloat16)
+    rho = torch.empty(R, device=dev)
+    fold = torch.empty(R, dtype=torch.uint8, device=dev)
+    ms = graph_time(torch, [lambda: sf.gate(sh, parent, H, 0.1, rho, fold)], reps=20)
+    # algorithmic bytes: every draft row reads itself and its parent row; rho + fold written
+    gbytes = (R - sh.block) * 2 * D * 2 + R * 5
+    del H
+    sc = Shape(64, 262144, 64, 4, 2, 16, 128, 0)
+    Rc = sc.rows
+    fold_c = (torch.rand(Rc, device=dev) < 0.7).to(torch.uint8)
+    rec_rows = torch.empty(Rc, dtype=torch.int32, device=dev)
+    rec_count = torch.empty(1, dtype=torch.int32, device=dev)
+    branch_off = torch.empty(sc.n_branch + 1, dtype=torch.int32, device=dev)
+    row_slot = torch.empty(Rc, dtype=torch.int32, device=dev)
+    ms_c = graph_time(torch, [lambda: sf.compact(sc, fold_c, rec_rows, rec_count, branch_off, row_slot)], reps=20)
+    M = int(rec_count.item())
+    # algorithmic bytes: the flags (read twice: count and scan) and the row map, list and offsets written
+    cbytes = 2 * Rc + 4 * Rc + 4 * M + 4 * (sc.n_branch + 1)
+    return {"gate": {"rows": R, "hidden": D, "us": round(ms * 1e3, 2), "bytes": gbytes,
+                     "gbs": round(gbytes / (ms * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(gbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "compact": {"rows": Rc, "us": round(ms_c * 1e3, 2), "bytes": cbytes,
+                        "gbs": round(cbytes / (ms_c * 1e-3) / 1e9, 1),
+                        "hbm_frac": round(cbytes / (ms_c * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+
+
+def _device_layer(torch, sh, seed, dev):
+    """Random-init layer weights on the device: N(0, 0.02^2) rounded to bf16, RMSNorm weights 1,
+    prefix K/V N(0, 1) -- the generator's distributions, drawn by torch for speed."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    D, F = sh.hidden, sh.ffn
+    nq = (sh.n_q_heads + 2 * sh.n_kv_heads) * sh.head_dim
+
+    def rnd(*shape, std=0.02):
+        return (torch.randn(*shape, device=dev, generator=g) * std).to(torch.bfloat16)
+    w = {"w_qkv": rnd(nq, D), "w_o": rnd(D, sh.n_q_heads * sh.head_dim), "w_gate_up": rnd(2 * F, D),
+         "w_down": rnd(D, F), "ln1": torch.ones(D, device=dev, dtype=torch.bfloat16),
+         "ln2": torch.ones(D, device=dev, dtype=torch.bfloat16)}
+    pk = rnd(sh.prefix_len, sh.n_kv_heads, sh.head_dim, std=1.0)
+    pv = rnd(sh.prefix_len, sh.n_kv_heads, sh.head_dim, std=1.0)
+    return w, pk, pv
+
+
+def stack_bench(args, wl):
+    """A full verification pass through an L-layer stack, S steps with a new draft tree each step:
+    per-branch residual streams carried across layers, every layer re-gating on its own input."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from sparse_layer_rho_amd import specfold as sf
+    from synth import bf16_round, layer_weights, prefix_kv, step_inputs
+
+    sh = wl.shape
+    R, D = sh.rows, sh.hidden
+    L = args.layers if args.layers > 1 else wl.layers
+    S = args.stack_steps if args.stack_steps > 0 else max(1, wl.steps)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev).to(torch.bfloat16)
+
+    t0 = time.time()
+    # layer 0 from the seeded generator the oracle uses (the run verifies it); the others drawn on
+    # the device with the same distributions
+    w0_host = layer_weights(sh, wl.base_seed, 0)
+    pk0_h, pv0_h = prefix_kv(sh, wl.base_seed, 0)
+    layers = [({k: to_dev(v) for k, v in w0_host.items()}, to_dev(pk0_h), to_dev(pv0_h))]
+    for l in range(1, L):
+        layers.append(_device_layer(torch, sh, 1000 * wl.base_seed + l, dev))
+    lws = [sf.layer_weights_struct(w) for w, _, _ in layers]
+    pfs = [sf.prefix_view(pk, pv) for _, pk, pv in layers]
+    steps = []
+    for s in range(S):
+        inp = step_inputs(sh, wl.base_seed, s, tree=wl.tree, child_law=wl.child_law)
+        steps.append((inp["parent"], bf16_round(inp["H"].astype(np.float32)), to_dev(
+            bf16_round(inp["H"].astype(np.float32)).reshape(R, D))))
+    torch.cuda.synchronize()
+    print(f"[bench] stack ready in {time.time() - t0:.1f}s: {args.workload}, {L} layers, {S} steps, "
+          f"{L * sh.weight_bytes_bf16() / 1e9:.2f} GB of weights", file=sys.stderr, flush=True)
+
+    ws = sf.new_workspace(sh)
+    buf = [torch.empty((R, D), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    # per-layer statistics; rows padded to 16 bytes (the library takes 16-byte aligned pointers)
+    Rp = (R + 15) // 16 * 16
+    fold = torch.zeros((L, Rp), dtype=torch.uint8, device=dev)
+    cnt = torch.zeros((L, 4), dtype=torch.int32, device=dev)
+
+    def run_step(s, delta):
+        parent, _, H0 = steps[s]
+        x = H0
+        for l in range(L):
+            y = buf[l % 2]
+            sf.verify_layer(sh, parent, lws[l], pfs[l], None, x, delta, y, ws,
+                            stats={"fold": fold[l, :R], "rec_count": cnt[l, :1]})
+            x = y
+        return x
+
+    res = {}
+    for delta in (wl.delta, 0.0):
+        out0 = None
+        Ms, ff = [], []
+        for s in range(S):
+            x = run_step(s, delta)
+            torch.cuda.synchronize()
+            if s == 0:
+                out0 = x.clone()
+            Ms.append(cnt[:, 0].cpu().numpy().copy())
+            f = fold[:, :R].cpu().numpy().reshape(L, sh.n_branch, sh.block)[:, 1:].mean(axis=(1, 2))
+            ff.append(f)
+        reps = max(1, args.steps // (S * 4))
+        ms = graph_time(torch, [lambda s=s: run_step(s, delta) for s in range(S)], reps=reps)
+        res[delta] = {"ms_per_step": ms / S, "M": np.mean(Ms, axis=0), "fold": np.mean(ff, axis=0)}
+        print(f"[bench] delta {delta}: {ms / S:.3f} ms per stack step", file=sys.stderr, flush=True)
+
+    # verification: layer 0 of step 0 against the oracle, teacher-forced on the GPU's mask
+    parent, H_host, H0 = steps[0]
+    y = torch.empty_like(H0)
+    st = {"fold": torch.zeros(R, dtype=torch.uint8, device=dev), "rec_count": torch.zeros(1, dtype=torch.int32, device=dev)}
+    sf.verify_layer(sh, parent, lws[0], pfs[0], None, H0, wl.delta, y, ws, stats=st)
+    torch.cuda.synchronize()
+    fold_g = st["fold"].cpu().numpy().reshape(sh.n_branch, sh.block).astype(bool)
+    Hd = H_host.astype(np.float64)
+    rho_o, fold_o = oracle.gate(Hd, parent, wl.delta)
+    band = np.abs(rho_o - wl.delta) < 1e-4
+    ok_mask = bool(np.array_equal(fold_g[~band], fold_o[~band]))
+    ref = oracle.verify_layer(Hd, parent, w0_host, pk0_h, pv0_h, wl.delta, sh, fold=fold_g)
+    got = y.float().cpu().numpy().astype(np.float64).reshape(Hd.shape)
+    err = float(np.linalg.norm(got - ref["H_out"]) / np.linalg.norm(ref["H_out"]))
+
+    f, d = res[wl.delta], res[0.0]
+    out = {
+        "metric": METRIC,
+        "value": round(R / (f["ms_per_step"] * 1e-3), 1),
+        "unit": "branch-tokens/s",
+        "n_gpus": 1,
+        "steps": S,
+        "ms_per_step": round(f["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random weights and prefix KV per layer, parent-linked draft hidden states per step)",
+        "config": {"workload": args.workload, "layers": L, "hidden": D, "n_q_heads": sh.n_q_heads,
+                   "n_kv_heads": sh.n_kv_heads, "ffn": sh.ffn, "block": sh.block, "drafts": sh.n_branch - 1,
+                   "prefix": sh.prefix_len, "delta": wl.delta, "rows": R, "timing": "HIP graph replay, events",
+                   "parallelism": "single GPU"},
+        "speedup_vs_dense": round(d["ms_per_step"] / f["ms_per_step"], 4),
+        "dense": {"value": round(R / (d["ms_per_step"] * 1e-3), 1), "ms_per_step": round(d["ms_per_step"], 5)},
+        "us_per_layer": {"folded": round(1e3 * f["ms_per_step"] / L, 2), "dense": round(1e3 * d["ms_per_step"] / L, 2)},
+        "rec_rows_per_layer": [round(float(v), 1) for v in f["M"]],
+        "fold_fraction_drafts_per_layer": [round(float(v), 4) for v in f["fold"]],
+        "verified": {"ok": bool(ok_mask and err <= 2e-2), "layer": 0, "step": 0, "rel_l2": round(err, 6),
+                     "mask_match_outside_band": ok_mask},
+    }
+    print(json.dumps(out), flush=True)
+
+
+def sweep_bench(args, wl):
+    """One layer swept over draft count B and delta (one tree and one set of hidden states per B,
+    reused across delta, so the folded fraction is monotone in delta)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from sparse_layer_rho_amd import specfold as sf
+    from synth import bf16_round, layer_weights, prefix_kv, step_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    base = wl.shape
+
+    def to_dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev).to(torch.bfloat16)
+
+    t0 = time.time()
+    w_host = layer_weights(base, wl.base_seed, 0)
+    pk_h, pv_h = prefix_kv(base, wl.base_seed, 0)
+    w0 = {k: to_dev(v) for k, v in w_host.items()}
+    n_copies = max(2, int(np.ceil(600e6 / base.weight_bytes_bf16())))
+    lws = [sf.layer_weights_struct(w0)] + [sf.layer_weights_struct({k: v.clone() for k, v in w0.items()})
+                                          for _ in range(n_copies - 1)]
+    pk, pv = to_dev(pk_h), to_dev(pv_h)
+    pf = sf.prefix_view(pk, pv)
+    print(f"[bench] sweep ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    points = []
+    for B in wl.branch_sweep:
+        sh = base.with_branches(B + 1)
+        R, D = sh.rows, sh.hidden
+        inp = step_inputs(sh, wl.base_seed, 0, tree=wl.tree, child_law=wl.child_law)
+        parent, H_host = inp["parent"], bf16_round(inp["H"].astype(np.float32))
+        H = to_dev(H_host.reshape(R, D))
+        ws = sf.new_workspace(sh)
+        y = torch.empty((R, D), dtype=torch.bfloat16, device=dev)
+        st = {"fold": torch.zeros(R, dtype=torch.uint8, device=dev), "rec_count": torch.zeros(1, dtype=torch.int32, device=dev)}
+        per = {}
+        for delta in wl.delta_sweep:
+            sf.verify_layer(sh, parent, lws[0], pf, None, H, delta, y, ws, stats=st)
+            torch.cuda.synchronize()
+            M = int(st["rec_count"].item())
+            ff = float(st["fold"].cpu().numpy().reshape(sh.n_branch, sh.block)[1:].mean())
+            reps = max(1, args.steps // (4 * n_copies))
+            ms = graph_time(torch, [lambda k=k, delta=delta: sf.verify_layer(sh, parent, lws[k], pf, None, H, delta, y, ws)
+                                    for k in range(n_copies)], reps=reps) / n_copies
+            per[delta] = (ms, M, ff)
+        # verification at the workload's delta, teacher-forced on the GPU's mask
+        sf.verify_layer(sh, parent, lws[0], pf, None, H, wl.delta, y, ws, stats=st)
+        torch.cuda.synchronize()
+        fold_g = st["fold"].cpu().numpy().reshape(sh.n_branch, sh.block).astype(bool)
+        Hd = H_host.astype(np.float64)
+        ref = oracle.verify_layer(Hd, parent, w_host, pk_h, pv_h, wl.delta, sh, fold=fold_g)
+        got = y.float().cpu().numpy().astype(np.float64).reshape(Hd.shape)
+        err = float(np.linalg.norm(got - ref["H_out"]) / np.linalg.norm(ref["H_out"]))
+        ms0 = per[0.0][0] if 0.0 in per else None
+        for delta, (ms, M, ff) in per.items():
+            points.append({"drafts": B, "delta": delta, "rec_rows": M, "fold_fraction_drafts": round(ff, 4),
+                           "us": round(ms * 1e3, 2), "branch_tokens_per_s": round(R / (ms * 1e-3), 1),
+                           "speedup_vs_dense": round(ms0 / ms, 4) if ms0 else None})
+        points.append({"drafts": B, "verified_delta": wl.delta, "rel_l2": round(err, 6), "ok": err <= 2e-2})
+        print(f"[bench] B={B} done", file=sys.stderr, flush=True)
+    print(json.dumps({"metric": METRIC, "unit": "branch-tokens/s", "workload": args.workload, "n_gpus": 1,
+                      "dtype": "bf16", "data": "synthetic", "regime": f"cold ({n_copies} weight copies)",
+                      "points": points}), flush=True)
 
 
 def cpu_baseline_leg(sh, wl, parent, H_host, w_host, pk_h, pv_h, gpu_res, seconds):

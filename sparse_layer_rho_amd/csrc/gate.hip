@@ -10,7 +10,8 @@
 //
 // Compaction [SpecFold summary, App. B]: an exclusive scan of the recompute flags in row order
 // (wave ballots + a cross-wave scan in LDS) writes the global list, the per-branch offsets and
-// the inverse map row -> slot.
+// the inverse map row -> slot.  Past 8192 rows the scan runs over tiles in three passes (count,
+// tile offsets, scan from the offset), so large inputs use the whole GPU.
 //
 // Sources [SpecFold summary, App. B and §A.3]: every row walks its fold chain up the parent map
 // (at most n_branch steps; branch 0 always terminates) -- rows are independent, so one
@@ -119,15 +120,17 @@ __global__ __launch_bounds__(256) void gate_kernel(const GateParams p) {
     if (row < p.nb * p.N) gate_row<CPL>(p, row, threadIdx.x & (kWave - 1));
 }
 
-// block-wide exclusive scan of recompute flags, blockDim.x threads, rows in ascending order
-__global__ __launch_bounds__(1024) void compact_kernel(const CompactParams p) {
+// Exclusive scan of the recompute flags of rows [r_begin, r_end) in ascending order, starting
+// at slot `base`, by one workgroup (ballots per wave, a cross-wave scan in LDS).  Writes the
+// list, row -> slot and the per-branch offsets of the rows it covers; returns the count.
+__device__ int scan_rows(const CompactParams& p, int r_begin, int r_end, int base) {
     __shared__ int s_wave_tot[16];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const int nw = blockDim.x >> 6;
-    int base = 0;
-    for (int r0 = 0; r0 < p.R; r0 += blockDim.x) {
+    const int start = base;
+    for (int r0 = r_begin; r0 < r_end; r0 += blockDim.x) {
         const int r = r0 + tid;
-        const bool rec = (r < p.R) && (p.fold[r] == 0);
+        const bool rec = (r < r_end) && (p.fold[r] == 0);
         const uint64_t m = __ballot(rec);
         const int excl = __popcll(m & ((1ull << lane) - 1ull));
         if (lane == 0) s_wave_tot[wave] = __popcll(m);
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(1024) void compact_kernel(const CompactParams p) {
             tot += t;
         }
         const int slot = base + woff + excl;
-        if (r < p.R) {
+        if (r < r_end) {
             p.row_slot[r] = rec ? slot : -1;
             if (rec) p.rec_rows[slot] = r;
             if (r % p.N == 0) p.branch_off[r / p.N] = slot;
@@ -147,10 +150,79 @@ __global__ __launch_bounds__(1024) void compact_kernel(const CompactParams p) {
         base += tot;
         __syncthreads();
     }
-    if (tid == 0) {
-        p.rec_count[0] = base;
-        p.branch_off[p.nb] = base;
+    return base - start;
+}
+
+// all rows in one workgroup (R up to a few tiles: the layer's own sizes)
+__global__ __launch_bounds__(1024) void compact_kernel(const CompactParams p) {
+    const int total = scan_rows(p, 0, p.R, 0);
+    if (threadIdx.x == 0) {
+        p.rec_count[0] = total;
+        p.branch_off[p.nb] = total;
     }
+}
+
+// Large inputs: tiles of kCompactTile rows.  Pass 1 counts each tile's recompute rows into the
+// first row_slot entry of the tile (scratch that pass 3 overwrites), pass 2 turns the counts
+// into exclusive offsets, pass 3 scans every tile from its offset.
+constexpr int kCompactTile = 8192;
+
+__global__ __launch_bounds__(256) void compact_count_kernel(const CompactParams p) {
+    __shared__ int s_tot[4];
+    const int tile = blockIdx.x, tid = threadIdx.x;
+    const int r0 = tile * kCompactTile;
+    // thread t counts rows r0 + 32t .. +32: two 16-byte loads, or byte loads where the array ends
+    // inside them (the flags are bytes; nothing past R is read)
+    const int rt = r0 + 32 * tid;
+    int cnt = 0;
+    if (rt + 32 <= p.R) {
+        const uint4 v0 = *reinterpret_cast<const uint4*>(p.fold + rt);
+        const uint4 v1 = *reinterpret_cast<const uint4*>(p.fold + rt + 16);
+        const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) cnt += ((w[q] >> (8 * b)) & 0xffu) == 0 ? 1 : 0;
+    } else {
+        for (int r = rt; r < p.R && r < rt + 32; ++r) cnt += p.fold[r] == 0 ? 1 : 0;
+    }
+    cnt = static_cast<int>(wave_sum(static_cast<float>(cnt)));
+    if ((tid & 63) == 0) s_tot[tid >> 6] = cnt;
+    __syncthreads();
+    if (tid == 0) p.row_slot[r0] = s_tot[0] + s_tot[1] + s_tot[2] + s_tot[3];
+}
+
+__global__ __launch_bounds__(1024) void compact_offsets_kernel(const CompactParams p, int ntiles) {
+    __shared__ int s_part[1024];
+    const int tid = threadIdx.x;
+    // thread t owns tiles 2t, 2t+1 (ntiles <= 2048)
+    const int a = 2 * tid < ntiles ? p.row_slot[2 * tid * kCompactTile] : 0;
+    const int b = 2 * tid + 1 < ntiles ? p.row_slot[(2 * tid + 1) * kCompactTile] : 0;
+    s_part[tid] = a + b;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {               // inclusive Hillis-Steele scan
+        const int v = tid >= d ? s_part[tid - d] : 0;
+        __syncthreads();
+        s_part[tid] += v;
+        __syncthreads();
+    }
+    const int excl = s_part[tid] - (a + b);
+    if (2 * tid < ntiles) p.row_slot[2 * tid * kCompactTile] = excl;
+    if (2 * tid + 1 < ntiles) p.row_slot[(2 * tid + 1) * kCompactTile] = excl + a;
+    if (tid == 1023) {
+        p.rec_count[0] = s_part[1023];
+        p.branch_off[p.nb] = s_part[1023];
+    }
+}
+
+__global__ __launch_bounds__(1024) void compact_scatter_kernel(const CompactParams p) {
+    __shared__ int s_base;
+    const int r0 = blockIdx.x * kCompactTile;
+    if (threadIdx.x == 0) s_base = p.row_slot[r0];
+    __syncthreads();
+    const int base = s_base;
+    __syncthreads();                               // everyone has the offset before row r0 is rewritten
+    scan_rows(p, r0, min(p.R, r0 + kCompactTile), base);
 }
 
 __global__ __launch_bounds__(256) void resolve_kernel(const ResolveParams p) {
@@ -213,7 +285,15 @@ hipError_t launch_gate(const GateParams& p, hipStream_t st) {
 }
 
 hipError_t launch_compact(const CompactParams& p, hipStream_t st) {
-    hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, st, p);
+    if (p.R <= kCompactTile) {
+        hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, st, p);
+        return hipGetLastError();
+    }
+    const int ntiles = (p.R + kCompactTile - 1) / kCompactTile;
+    if (ntiles > 2048) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(compact_count_kernel, dim3(ntiles), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(compact_offsets_kernel, dim3(1), dim3(1024), 0, st, p, ntiles);
+    hipLaunchKernelGGL(compact_scatter_kernel, dim3(ntiles), dim3(1024), 0, st, p);
     return hipGetLastError();
 }
 

@@ -88,7 +88,10 @@ def test_gate_threshold_bit_exact_when_fed_rho():
 
 @pytest.mark.parametrize("B1,N,kind,p", [(3, 8, "chain", 0.7), (9, 32, "random", 0.72), (6, 20, "star", 0.5),
                                          (64, 64, "random", 0.8), (9, 32, "random", 1.0), (9, 32, "random", 0.0),
-                                         (1, 17, "random", 0.5), (33, 40, "chain", 0.9)])
+                                         (1, 17, "random", 0.5), (33, 40, "chain", 0.9),
+                                         # past one 8192-row tile: the three-pass compaction
+                                         (37, 1000, "random", 0.7), (3, 8193, "random", 0.3),
+                                         (5, 8192, "random", 1.0), (64, 4096, "chain", 0.5)])
 def test_compact_and_resolve_bit_exact(B1, N, kind, p):
     sh = Shape(B1, N, 64, 4, 2, 16, 128, 0)
     rng = np.random.default_rng(B1 * 100 + N)
