@@ -187,7 +187,7 @@ def main():
     achieved = gu_bytes / (gu_us * 1e-6) / 1e9
     roofline = {"kernel": "gate_up_swiglu_gemm", "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None, "avg_us": round(gu_us, 2), "bytes_per_launch": gu_bytes,
+                "traffic": measured_traffic(), "avg_us": round(gu_us, 2), "bytes_per_launch": gu_bytes,
                 "tflops": round(2 * M * 2 * F * D / (gu_us * 1e-6) / 1e12, 1)}
 
     # whole-layer roofline at the vendor peaks: sum over kernels of max(bytes/BW, flops/MFMA)
@@ -247,6 +247,26 @@ def main():
         out["cpu_baseline"], out["verified"] = cpu_baseline_leg(
             sh, wl, parent, H_host, w_host, pk_h, pv_h, results[wl.delta], args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gate_up_swiglu_gemm_layer-1.5b_traffic.md")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the gate/up GEMM from the committed counter record (FETCH_SIZE +
+    WRITE_SIZE, calibrated by a copy of known size), or None when the record is missing or was
+    taken for a different version of the GEMM sources."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_RECORD).read()
+        rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (OSError, IndexError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "kernels.h", "common.h"):
+        with open(os.path.join(ROOT, "sparse_layer_rho_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return rec.get("traffic_bytes") if rec.get("source_sha256") == h.hexdigest() else None
 
 
 def graph_time(torch, fns, reps, warmup_s=0.5):
