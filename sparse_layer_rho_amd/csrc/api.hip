@@ -56,7 +56,7 @@ GemmCfg pick_gemm(GemmKind kind, int n_cols, int k, int max_rows, int busy_chunk
     c.ntw = 4; c.wn = 1;
     if (kind == GEMM_GATE_UP) { c.tm = 1; c.ksub = 2; c.nbw = 2; c.nba = 2; }
     else if (kind == GEMM_DOWN) { c.tm = 2; c.ksub = 1; c.nbw = 4; c.nba = 2; }
-    else { c.tm = 1; c.ksub = 1; c.nbw = 3; c.nba = 2; }
+    else { c.ntw = 2; c.tm = 1; c.ksub = 1; c.nbw = 3; c.nba = 2; }
     if (max_rows <= 64) { c.ntw = 2; c.wn = 2; c.tm = 2; c.ksub = 2; c.nbw = 2; c.nba = 2; }
     const int cap = gemm_group_cols(c);
     c.groups = (n_cols + cap - 1) / cap;
@@ -64,7 +64,9 @@ GemmCfg pick_gemm(GemmKind kind, int n_cols, int k, int max_rows, int busy_chunk
     if (!c.swiglu) {
         const int chunks = (max_rows + gemm_chunk_rows(c) - 1) / gemm_chunk_rows(c);
         const int busy = c.groups * (busy_chunks < chunks ? busy_chunks : chunks);
-        int s = (384 + busy / 2) / busy;
+        // workgroups aimed at per launch (measured best on the 1.5B layer shapes)
+        const int target = kind == GEMM_DOWN ? 384 : kind == GEMM_O ? 768 : 512;
+        int s = (target + busy / 2) / busy;
         int smax = (k + 64 * c.ksub - 1) / (64 * c.ksub) / (c.ksub == 1 ? 4 : 2);
         if (smax > 32) smax = 32;                          // the epilogues batch up to 32 splits
         if (s > smax) s = smax;

@@ -11,10 +11,17 @@
 // computes the N-key block part for every row of every branch and merges it with the chunk
 // states of the row's source slot by log-sum-exp, in a fixed order (deterministic).
 //
-// Keys and values move through LDS in blocks of 64: K row-major, V transposed (the PV product
-// needs 8 consecutive keys of one dimension per lane).  Every load is a bounded buffer load
-// (keys past the end and invalid slots read as zeros), so a block costs one round trip, and the
-// prefix kernel fetches block b+1 into registers while it multiplies block b.
+// Keys and values move HBM -> LDS with buffer_load ... lds (no register staging), both
+// row-major: one such load fills 1 KB of LDS, i.e. whole key rows, so every 4-lane quad reads
+// one 64-byte segment.  Row r keeps its 16-byte chunk c at position c ^ fk(r) in K and
+// c ^ fv(r) in V, which makes the K fragment reads (16 rows x one chunk) and the transposed V
+// reads conflict-free.  The P V product needs 8 keys of one dimension per lane; gfx950's
+// ds_read_b64_tr_b16 delivers them from the row-major layout: in each 16-lane group, lane p
+// names the 4 elements at (row p/4, columns 4(p%4)..+3) of a 4 x 16 tile, and lane L receives
+// column L of that tile (one element per row).  Every load is bounded (keys past the end and
+// invalid slots read as zeros).  The prefix kernel requests a whole stage of 128 keys at once,
+// so a stage costs one round trip, and the next stage is in flight while one is multiplied;
+// two waves share each query tile, one per 64-key half of the stage.
 //
 // Both kernels are FlashAttention-style on bf16 MFMA with the transposed product S^T = K Q^T:
 // keys are the MFMA rows, the 16 queries of a wave are its columns, so each lane owns one
@@ -27,59 +34,57 @@ namespace specfold {
 namespace {
 
 constexpr float kNegInf = -__builtin_inff();
+constexpr int kStageKeys = 128;                 // prefix keys per LDS stage
+constexpr int kPrefixQT = 2;                    // 16-query tiles per prefix workgroup
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 template <int HD>
 struct AttnTile {
     static constexpr int KS = (HD + 31) / 32;   // 32-wide k-steps over head_dim
     static constexpr int DT = HD / 16;          // 16-row output tiles over head_dim
-    static constexpr int KROW = HD * 2 + 16;    // LDS bytes per key row (padded)
-    static constexpr int VROW = 64 * 2 + 8;     // LDS bytes per transposed value row (64 keys)
     static constexpr int CH = HD / 8;           // 16-byte chunks per key row
-    static constexpr int U = (64 * CH + 255) / 256;   // staging units per thread (256 threads)
+    static constexpr int RB = HD * 2;           // LDS bytes per key row
+    static __device__ __forceinline__ int fk(int r) { return r & (CH - 1); }
+    static __device__ __forceinline__ int fv(int r) { return (2 * r) & (CH - 1); }
 };
 
-// Registers of one 64-key block: unit u of thread t is chunk cc of key `key`, with
-// idx = t + 256 u = cc * 64 + key (consecutive threads take consecutive keys, so the transposed
-// V stores of a wave cover 128 contiguous bytes).  off(key, cc) gives the byte offsets of the
-// K and V chunk, or kOob.
-template <int HD>
-struct KVRegs {
-    uint4 k[AttnTile<HD>::U], v[AttnTile<HD>::U];
+// 16 bytes per lane, global -> LDS: lane l's bytes land at lds + 16 l (lds is wave-uniform)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds), 16, voff, 0, 0, 0);
+}
 
-    template <typename Off>
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, Off off) {
-        using T = AttnTile<HD>;
+// this wave's buffer loads (register and LDS) are complete
+__device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Request NKEYS rows of K and V into sK / sV (swizzled as above).  row_off(row, k_or_v) gives
+// the element offset of a key row's first dimension, or -1 for a missing key (the host keeps
+// every view under 1 GB, so offsets fit in 32 bits).  Load i of the
+// NKEYS*CH/64 per tensor is issued by wave i % NW (NW waves in the workgroup).
+template <int HD, int NKEYS, int NW, typename RowOff>
+__device__ __forceinline__ void request_rows(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                             uint8_t* sK, uint8_t* sV, RowOff row_off) {
+    using T = AttnTile<HD>;
+    constexpr int kLoads = NKEYS * T::CH / 64;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
-        for (int u = 0; u < T::U; ++u) {
-            const int idx = threadIdx.x + 256 * u;
-            const int cc = idx >> 6, key = idx & 63;
-            uint32_t ok_ = kOob, ov = kOob;
-            if (idx < 64 * T::CH) off(key, cc, ok_, ov);
-            k[u] = buf_load16(rk, ok_);
-            v[u] = buf_load16(rv, ov);
-        }
+    for (int t = 0; t < (kLoads + NW - 1) / NW; ++t) {
+        const int i = wave + NW * t;
+        if (i >= kLoads) break;                    // wave-uniform
+        const int q = i * 64 + lane;
+        const int row = q / T::CH, pos = q % T::CH;
+        const int ek = row_off(row, 0), ev = row_off(row, 1);
+        const uint32_t ok_ = ek < 0 ? kOob : static_cast<uint32_t>((ek + 8 * (pos ^ T::fk(row))) * 2);
+        const uint32_t ov = ev < 0 ? kOob : static_cast<uint32_t>((ev + 8 * (pos ^ T::fv(row))) * 2);
+        dma16(rk, sK + i * 1024, ok_);
+        dma16(rv, sV + i * 1024, ov);
     }
+}
 
-    __device__ __forceinline__ void store(uint8_t* sK, uint8_t* sV) const {
-        using T = AttnTile<HD>;
-        uint16_t* vt = reinterpret_cast<uint16_t*>(sV);
-#pragma unroll
-        for (int u = 0; u < T::U; ++u) {
-            const int idx = threadIdx.x + 256 * u;
-            if (idx >= 64 * T::CH) continue;
-            const int cc = idx >> 6, key = idx & 63;
-            *reinterpret_cast<uint4*>(sK + key * T::KROW + cc * 16) = k[u];
-            const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                vt[(cc * 8 + 2 * e) * (T::VROW / 2) + key] = static_cast<uint16_t>(w[e] & 0xffffu);
-                vt[(cc * 8 + 2 * e + 1) * (T::VROW / 2) + key] = static_cast<uint16_t>(w[e] >> 16);
-            }
-        }
-    }
-};
-
-// One 64-key block of online softmax for the wave's 16 queries.
+// One 64-key block of online softmax for the wave's 16 queries; sK / sV point at the block's
+// first row (a multiple of 16 rows into the stage, so the swizzles line up).
 // qf: B operand (query lane&15, d = 32s + 8*(lane>>4)); nk valid keys.
 template <int HD>
 __device__ __forceinline__ void attend_block(const uint8_t* sK, const uint8_t* sV, int nk,
@@ -88,21 +93,26 @@ __device__ __forceinline__ void attend_block(const uint8_t* sK, const uint8_t* s
     using T = AttnTile<HD>;
     const int lane = threadIdx.x & 63;
     const int g4 = lane >> 4, l16 = lane & 15;
-    const int ntiles = (nk + 15) >> 4;
-    f32x4 sc[4];
+    // Branch-free: rows past nk hold zeros (their loads were out of range), their scores are
+    // masked below and their P entries are zero, so all fragment reads can be issued at once.
+    uint4 kf[4][T::KS];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-        sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (kt < ntiles) {
+        const int r = kt * 16 + l16;
 #pragma unroll
-            for (int s = 0; s < T::KS; ++s) {
-                const int d0 = 32 * s + 8 * g4;
-                const uint4 kf = (d0 < HD) ? *reinterpret_cast<const uint4*>(sK + (kt * 16 + l16) * T::KROW + d0 * 2)
-                                           : make_uint4(0, 0, 0, 0);
-                sc[kt] = mfma16x16x32(kf, qf[s], sc[kt]);
-            }
+        for (int s = 0; s < T::KS; ++s) {
+            const int c = 4 * s + g4;
+            kf[kt][s] = (8 * c < HD) ? *reinterpret_cast<const uint4*>(sK + r * T::RB + ((c ^ T::fk(r)) << 4))
+                                     : make_uint4(0, 0, 0, 0);
         }
     }
+    f32x4 sc[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < T::KS; ++s)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) sc[kt] = mfma16x16x32(kf[kt][s], qf[s], sc[kt]);
     // lane holds S^T[key = 16kt + 4*g4 + i][query l16]
     float bmax = kNegInf;
 #pragma unroll
@@ -132,21 +142,28 @@ __device__ __forceinline__ void attend_block(const uint8_t* sK, const uint8_t* s
 #pragma unroll
     for (int dt = 0; dt < T::DT; ++dt) o[dt] *= alpha;
     // O^T += V^T P^T over two 32-key steps; slot 8*g4 + i <-> key 32u + 4*g4 + i and
-    // slot 8*g4 + 4 + i <-> key 32u + 16 + 4*g4 + i on both operands
+    // slot 8*g4 + 4 + i <-> key 32u + 16 + 4*g4 + i on both operands.  The A operand (V^T,
+    // rows = dimensions) comes from two transposed reads of 4 keys each: lane p of the group
+    // names key row 4*g4 + p/4 (+16), dimensions 16dt + 4(p%4)..+3.
+    const int pr = l16 >> 2, pc = l16 & 3;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        if (32 * u < nk) {
-            const float pf[8] = {sc[2 * u][0], sc[2 * u][1], sc[2 * u][2], sc[2 * u][3],
-                                 sc[2 * u + 1][0], sc[2 * u + 1][1], sc[2 * u + 1][2], sc[2 * u + 1][3]};
-            const uint4 pb = pack8(pf);
+        const float pf[8] = {sc[2 * u][0], sc[2 * u][1], sc[2 * u][2], sc[2 * u][3],
+                             sc[2 * u + 1][0], sc[2 * u + 1][1], sc[2 * u + 1][2], sc[2 * u + 1][3]};
+        const uint4 pb = pack8(pf);
+        const int r0 = 32 * u + 4 * g4 + pr, r1 = r0 + 16;
+        uint2 lo[T::DT], hi[T::DT];
 #pragma unroll
-            for (int dt = 0; dt < T::DT; ++dt) {
-                const uint16_t* vrow = reinterpret_cast<const uint16_t*>(sV + (dt * 16 + l16) * T::VROW);
-                const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 32 * u + 4 * g4);
-                const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 32 * u + 16 + 4 * g4);
-                o[dt] = mfma16x16x32(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, o[dt]);
-            }
+        for (int dt = 0; dt < T::DT; ++dt) {
+            const int c = 2 * dt + (pc >> 1);
+            const uint8_t* a0 = sV + r0 * T::RB + ((c ^ T::fv(r0)) << 4) + 8 * (pc & 1);
+            const uint8_t* a1 = sV + r1 * T::RB + ((c ^ T::fv(r1)) << 4) + 8 * (pc & 1);
+            lo[dt] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0)));
+            hi[dt] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a1)));
         }
+#pragma unroll
+        for (int dt = 0; dt < T::DT; ++dt)
+            o[dt] = mfma16x16x32(make_uint4(lo[dt].x, lo[dt].y, hi[dt].x, hi[dt].y), pb, o[dt]);
     }
 }
 
@@ -171,39 +188,44 @@ __device__ __forceinline__ uint32_t view_bytes(int P, int Hkv, int64_t st, int64
     return static_cast<uint32_t>(((P - 1) * st + (Hkv - 1) * sh + HD) * 2);
 }
 
-// grid: x = tiles of 64 (slot, head-in-group) queries, y = prefix chunk, z = KV group
+// grid: x = prefix chunk * Hkv + KV group, y = group of kPrefixQT 16-query tiles of (slot,
+// head-in-group) queries, so the groups below the recompute count are dispatched first.
+// 2 kPrefixQT waves: wave w takes query tile w % kPrefixQT and, of every stage, the 64-key half
+// w / kPrefixQT; the two halves' states are merged through LDS at the end.  (Every wave reads
+// a whole 64-key block from LDS, so few waves per CU keep the LDS port from saturating.)  Dynamic LDS: one stage of kStageKeys rows of K and V, or two when
+// a chunk spans several stages.
 template <int HD>
-__global__ __launch_bounds__(256) void attn_prefix_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(128 * kPrefixQT) void attn_prefix_kernel(const AttnArgs a) {
     using T = AttnTile<HD>;
-    __shared__ __align__(16) uint8_t sK[64 * T::KROW];
-    __shared__ __align__(16) uint8_t sV[HD * T::VROW];
+    constexpr int kStageBytes = kStageKeys * T::RB;
+    extern __shared__ __align__(16) uint8_t smem[];
     const int G = a.Hq / a.Hkv;
-    const int g = blockIdx.z, chunk = blockIdx.y;
+    const int g = blockIdx.x % a.Hkv, chunk = blockIdx.x / a.Hkv;
     const int M = clamp_count(a.m_count, a.m_cap);
     const int nq = M * G;
-    const int q0 = blockIdx.x * 64;
+    const int q0 = blockIdx.y * 16 * kPrefixQT;
     if (q0 >= nq) return;
     const int key0 = chunk * a.chunk_len;
     const int key1 = min(a.P, key0 + a.chunk_len);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int qi = q0 + wave * 16 + (lane & 15);
+    const int qw = wave % kPrefixQT, half = wave / kPrefixQT;
+    const int qi = q0 + qw * 16 + (lane & 15);
     const bool qvalid = qi < nq;
     const int m = qvalid ? qi / G : 0, h = g * G + (qvalid ? qi % G : 0);
 
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q_c, static_cast<uint32_t>(static_cast<size_t>(a.m_cap) * a.Hq * HD * 2));
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.pk, view_bytes(a.P, a.Hkv, a.pk_st, a.pk_sh, HD));
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.pv, view_bytes(a.P, a.Hkv, a.pv_st, a.pv_sh, HD));
-    auto block_off = [&](int kb) {
-        const int nk = min(64, key1 - kb);
-        return [=](int key, int cc, uint32_t& ok_, uint32_t& ov) {
-            if (key < nk) {
-                ok_ = static_cast<uint32_t>(((kb + key) * a.pk_st + g * a.pk_sh + cc * 8) * 2);
-                ov = static_cast<uint32_t>(((kb + key) * a.pv_st + g * a.pv_sh + cc * 8) * 2);
-            }
-        };
+    const int kst = static_cast<int>(a.pk_st), kbase = g * static_cast<int>(a.pk_sh);
+    const int vst = static_cast<int>(a.pv_st), vbase = g * static_cast<int>(a.pv_sh);
+    auto request_stage = [&](int kb, int buf) {
+        uint8_t* sK = smem + buf * 2 * kStageBytes;
+        request_rows<HD, kStageKeys, 2 * kPrefixQT>(rk, rv, sK, sK + kStageBytes, [&](int row, int which) -> int {
+            const int key = kb + row;
+            return key >= key1 ? -1 : (which == 0 ? key * kst + kbase : key * vst + vbase);
+        });
     };
-    KVRegs<HD> kv;
-    kv.load(rk, rv, block_off(key0));
+    request_stage(key0, 0);
     uint4 qf[T::KS];
     load_query<HD>(rq, qvalid ? static_cast<uint32_t>((m * a.Hq + h) * HD * 2) : kOob, qf);
 
@@ -212,12 +234,43 @@ __global__ __launch_bounds__(256) void attn_prefix_kernel(const AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < T::DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int kb = key0; kb < key1; kb += 64) {
-        __syncthreads();                           // the previous block is consumed
-        kv.store(sK, sV);
-        __syncthreads();
-        if (kb + 64 < key1) kv.load(rk, rv, block_off(kb + 64));   // in flight during the block
-        attend_block<HD>(sK, sV, min(64, key1 - kb), qf, a.scale_log2, run_m, run_l, o);
+    int buf = 0;
+    for (int kb = key0; kb < key1; kb += kStageKeys) {
+        vm_drain();
+        __syncthreads();                           // stage kb is in LDS; the other buffer is free
+        if (kb + kStageKeys < key1) request_stage(kb + kStageKeys, buf ^ 1);
+        const uint8_t* sK = smem + buf * 2 * kStageBytes;
+        const int sb = 64 * half, nst = min(kStageKeys, key1 - kb);
+        if (sb < nst)                              // wave-uniform
+            attend_block<HD>(sK + sb * T::RB, sK + kStageBytes + sb * T::RB, min(64, nst - sb), qf,
+                             a.scale_log2, run_m, run_l, o);
+        __syncthreads();                           // this buffer is consumed
+        buf ^= 1;
+    }
+    // merge the second half's state into the first (per-lane partial denominators are
+    // rescaled like the outputs; the rescale factor is uniform over a query's four lanes)
+    float* xs = reinterpret_cast<float*>(smem) + qw * (T::DT * 4 + 2) * 64 + lane;
+    if (half == 1) {
+#pragma unroll
+        for (int dt = 0; dt < T::DT; ++dt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xs[(dt * 4 + e) * 64] = o[dt][e];
+        xs[T::DT * 4 * 64] = run_m;
+        xs[(T::DT * 4 + 1) * 64] = run_l;
+    }
+    __syncthreads();
+    if (half == 1) return;
+    {
+        const float m1 = xs[T::DT * 4 * 64], l1 = xs[(T::DT * 4 + 1) * 64];
+        const float nm = fmaxf(run_m, m1);
+        const float w0 = run_m == kNegInf ? 0.f : exp2f(run_m - nm);
+        const float w1 = m1 == kNegInf ? 0.f : exp2f(m1 - nm);
+        run_l = run_l * w0 + l1 * w1;
+#pragma unroll
+        for (int dt = 0; dt < T::DT; ++dt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[dt][e] = o[dt][e] * w0 + xs[(dt * 4 + e) * 64] * w1;
+        run_m = nm;
     }
     run_l += __shfl_xor(run_l, 16, kWave);
     run_l += __shfl_xor(run_l, 32, kWave);
@@ -230,44 +283,38 @@ __global__ __launch_bounds__(256) void attn_prefix_kernel(const AttnArgs a) {
     for (int dt = 0; dt < T::DT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[dt];
 }
 
-// grid: x = branch, y = KV group, z = group of 4 query tiles (16 positions x 1 head each)
+// grid: x = branch, y = KV group, z = query tile (16 positions x 1 head).  One wave per
+// workgroup: the chunk states a tile merges are its largest input, and single-wave workgroups
+// spread them over as many CUs as there are tiles.
 template <int HD>
-__global__ __launch_bounds__(256) void attn_block_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(64) void attn_block_kernel(const AttnArgs a) {
     using T = AttnTile<HD>;
     constexpr int kBatch = 4;                      // prefix chunk states loaded per round trip
-    __shared__ __align__(16) uint8_t sK[64 * T::KROW];
-    __shared__ __align__(16) uint8_t sV[HD * T::VROW];
+    __shared__ __align__(16) uint8_t sK[64 * T::RB];
+    __shared__ __align__(16) uint8_t sV[64 * T::RB];
     __shared__ int sSlot[64];
-    __shared__ int sBad;
     const int G = a.Hq / a.Hkv, N = a.N;
     const int i = blockIdx.x, g = blockIdx.y;
     const int M = clamp_count(a.m_count, a.m_cap);
     const int nt16 = (N + 15) >> 4;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int qt = blockIdx.z * 4 + wave;
+    const int lane = threadIdx.x;
+    const int qt = blockIdx.z;
 
-    if (threadIdx.x == 0) sBad = 0;
-    __syncthreads();
-    if (threadIdx.x < 64) {
-        int s = -1;
-        if (threadIdx.x < N) {
-            s = a.src_slot[i * N + threadIdx.x];
-            if (s < 0 || s >= M) {
-                s = -1;
-                atomicOr(&sBad, 1);
-            }
-        }
-        sSlot[threadIdx.x] = s;
+    int s_own = -1;
+    if (lane < N) {
+        s_own = a.src_slot[i * N + lane];
+        if (s_own < 0 || s_own >= M) s_own = -2;
     }
+    const bool any_bad = __ballot(s_own == -2) != 0;   // some position has no valid source
+    sSlot[lane] = s_own < 0 ? -1 : s_own;
     __syncthreads();
     const uint32_t rows_bytes = static_cast<uint32_t>(static_cast<size_t>(a.m_cap) * a.Hkv * HD * 2);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_c, rows_bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_c, rows_bytes);
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q_c, static_cast<uint32_t>(static_cast<size_t>(a.m_cap) * a.Hq * HD * 2));
-    KVRegs<HD> kv;
-    kv.load(rk, rv, [&](int key, int cc, uint32_t& ok_, uint32_t& ov) {
-        const int s = key < N ? sSlot[key] : -1;
-        if (s >= 0) ok_ = ov = static_cast<uint32_t>(((s * a.Hkv + g) * HD + cc * 8) * 2);
+    request_rows<HD, 64, 1>(rk, rv, sK, sV, [&](int row, int) -> int {
+        const int s = row < N ? sSlot[row] : -1;
+        return s < 0 ? -1 : (s * a.Hkv + g) * HD;
     });
 
     const bool active = qt < G * nt16;             // wave-uniform
@@ -280,7 +327,7 @@ __global__ __launch_bounds__(256) void attn_block_kernel(const AttnArgs a) {
     load_query<HD>(rq, qslot >= 0 ? static_cast<uint32_t>((qslot * a.Hq + h) * HD * 2) : kOob, qf);
 
     // prefix chunk states of the source slot: the first batch is requested now, so it arrives
-    // while the block part is computed
+    // with the block's keys
     const int ps = qslot < 0 ? 0 : qslot;
     const __amdgpu_buffer_rsrc_t rml =
         make_rsrc(a.part_ml, static_cast<uint32_t>(static_cast<size_t>(a.n_chunks) * a.m_cap * a.Hq * 8));
@@ -300,7 +347,7 @@ __global__ __launch_bounds__(256) void attn_block_kernel(const AttnArgs a) {
         }
     };
     load_states(0);
-    kv.store(sK, sV);
+    vm_drain();
     __syncthreads();
     if (!active) return;
 
@@ -327,7 +374,7 @@ __global__ __launch_bounds__(256) void attn_block_kernel(const AttnArgs a) {
         }
     }
     if (!nvalid) return;
-    const bool bad = (qslot < 0) || (sBad != 0);
+    const bool bad = (qslot < 0) || any_bad;
     const float invL = bad ? __builtin_nanf("") : 1.0f / run_l;
     const int row = i * N + n;
     uint16_t* dst = a.attn + (static_cast<size_t>(row) * a.Hq + h) * HD + 4 * (lane >> 4);
@@ -340,31 +387,42 @@ __global__ __launch_bounds__(256) void attn_block_kernel(const AttnArgs a) {
         a.lse[static_cast<size_t>(row) * a.Hq + h] = bad ? __builtin_nanf("") : (run_m + log2f(run_l)) * 0.69314718055994531f;
 }
 
+template <int HD>
+hipError_t launch_prefix_hd(const AttnArgs& a, dim3 grid, hipStream_t st) {
+    // one LDS stage holds the whole chunk, else two alternate
+    const size_t stage = static_cast<size_t>(2) * kStageKeys * AttnTile<HD>::RB;
+    const size_t lds = (a.chunk_len > kStageKeys ? 2 : 1) * stage;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_prefix_kernel<HD>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_prefix_kernel<HD>, grid, dim3(128 * kPrefixQT), lds, st, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_attn_prefix(const AttnArgs& a, hipStream_t st) {
     if (a.n_chunks <= 0) return hipSuccess;
+    if (a.chunk_len <= 0 || a.chunk_len % 64 != 0) return hipErrorInvalidValue;
     const int G = a.Hq / a.Hkv;
-    const dim3 grid((a.m_cap * G + 63) / 64, a.n_chunks, a.Hkv);
+    const dim3 grid(a.n_chunks * a.Hkv, (a.m_cap * G + 16 * kPrefixQT - 1) / (16 * kPrefixQT));
     switch (a.hd) {
-        case 16: hipLaunchKernelGGL(attn_prefix_kernel<16>, grid, dim3(256), 0, st, a); break;
-        case 32: hipLaunchKernelGGL(attn_prefix_kernel<32>, grid, dim3(256), 0, st, a); break;
-        case 64: hipLaunchKernelGGL(attn_prefix_kernel<64>, grid, dim3(256), 0, st, a); break;
-        case 128: hipLaunchKernelGGL(attn_prefix_kernel<128>, grid, dim3(256), 0, st, a); break;
+        case 16: return launch_prefix_hd<16>(a, grid, st);
+        case 32: return launch_prefix_hd<32>(a, grid, st);
+        case 64: return launch_prefix_hd<64>(a, grid, st);
+        case 128: return launch_prefix_hd<128>(a, grid, st);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_attn_block(const AttnArgs& a, hipStream_t st) {
     const int G = a.Hq / a.Hkv;
-    const int tiles = G * ((a.N + 15) / 16);
-    const dim3 grid(a.nb, a.Hkv, (tiles + 3) / 4);
+    const dim3 grid(a.nb, a.Hkv, G * ((a.N + 15) / 16));
     switch (a.hd) {
-        case 16: hipLaunchKernelGGL(attn_block_kernel<16>, grid, dim3(256), 0, st, a); break;
-        case 32: hipLaunchKernelGGL(attn_block_kernel<32>, grid, dim3(256), 0, st, a); break;
-        case 64: hipLaunchKernelGGL(attn_block_kernel<64>, grid, dim3(256), 0, st, a); break;
-        case 128: hipLaunchKernelGGL(attn_block_kernel<128>, grid, dim3(256), 0, st, a); break;
+        case 16: hipLaunchKernelGGL(attn_block_kernel<16>, grid, dim3(64), 0, st, a); break;
+        case 32: hipLaunchKernelGGL(attn_block_kernel<32>, grid, dim3(64), 0, st, a); break;
+        case 64: hipLaunchKernelGGL(attn_block_kernel<64>, grid, dim3(64), 0, st, a); break;
+        case 128: hipLaunchKernelGGL(attn_block_kernel<128>, grid, dim3(64), 0, st, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
