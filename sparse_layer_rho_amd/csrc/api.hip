@@ -56,10 +56,19 @@ GemmCfg pick_gemm(GemmKind kind, int n_cols, int k, int max_rows, int busy_chunk
     c.ntw = 4; c.wn = 1;
     if (kind == GEMM_GATE_UP) { c.tm = 1; c.ksub = 2; c.nbw = 2; c.nba = 2; }
     else if (kind == GEMM_DOWN) { c.tm = 2; c.ksub = 1; c.nbw = 4; c.nba = 2; }
-    else { c.ntw = 2; c.tm = 1; c.ksub = 1; c.nbw = 3; c.nba = 2; }
+    else {
+        // 64-column groups unless that leaves few workgroups: narrower groups re-read the
+        // activations more often, which only pays while it buys parallelism
+        const int chunks = (max_rows + 63) / 64;
+        const int busy = ((n_cols + 63) / 64) * (busy_chunks < chunks ? busy_chunks : chunks);
+        c.ntw = busy >= 128 ? 4 : 2; c.tm = 1; c.ksub = 1; c.nbw = 3; c.nba = 2;
+    }
     if (max_rows <= 64) { c.ntw = 2; c.wn = 2; c.tm = 2; c.ksub = 2; c.nbw = 2; c.nba = 2; }
     const int cap = gemm_group_cols(c);
     c.groups = (n_cols + cap - 1) / cap;
+    // the recompute-row projections keep two row workgroups per column group however small M
+    // is (the split count below assumes them)
+    c.min_chunks = (kind == GEMM_QKV || kind == GEMM_GATE_UP) ? 2 : 1;
     c.splits = 1;
     if (!c.swiglu) {
         const int chunks = (max_rows + gemm_chunk_rows(c) - 1) / gemm_chunk_rows(c);

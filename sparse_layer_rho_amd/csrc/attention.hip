@@ -35,7 +35,6 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kStageKeys = 128;                 // prefix keys per LDS stage
-constexpr int kPrefixQT = 2;                    // 16-query tiles per prefix workgroup
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -188,14 +187,14 @@ __device__ __forceinline__ uint32_t view_bytes(int P, int Hkv, int64_t st, int64
     return static_cast<uint32_t>(((P - 1) * st + (Hkv - 1) * sh + HD) * 2);
 }
 
-// grid: x = prefix chunk * Hkv + KV group, y = group of kPrefixQT 16-query tiles of (slot,
+// grid: x = prefix chunk * Hkv + KV group, y = group of QT 16-query tiles of (slot,
 // head-in-group) queries, so the groups below the recompute count are dispatched first.
-// 2 kPrefixQT waves: wave w takes query tile w % kPrefixQT and, of every stage, the 64-key half
-// w / kPrefixQT; the two halves' states are merged through LDS at the end.  (Every wave reads
+// 2 QT waves: wave w takes query tile w % QT and, of every stage, the 64-key half w / QT; the
+// two halves' states are merged through LDS at the end.  (Every wave reads
 // a whole 64-key block from LDS, so few waves per CU keep the LDS port from saturating.)  Dynamic LDS: one stage of kStageKeys rows of K and V, or two when
 // a chunk spans several stages.
-template <int HD>
-__global__ __launch_bounds__(128 * kPrefixQT) void attn_prefix_kernel(const AttnArgs a) {
+template <int HD, int QT>
+__global__ __launch_bounds__(128 * QT) void attn_prefix_kernel(const AttnArgs a) {
     using T = AttnTile<HD>;
     constexpr int kStageBytes = kStageKeys * T::RB;
     extern __shared__ __align__(16) uint8_t smem[];
@@ -203,12 +202,12 @@ __global__ __launch_bounds__(128 * kPrefixQT) void attn_prefix_kernel(const Attn
     const int g = blockIdx.x % a.Hkv, chunk = blockIdx.x / a.Hkv;
     const int M = clamp_count(a.m_count, a.m_cap);
     const int nq = M * G;
-    const int q0 = blockIdx.y * 16 * kPrefixQT;
+    const int q0 = blockIdx.y * 16 * QT;
     if (q0 >= nq) return;
     const int key0 = chunk * a.chunk_len;
     const int key1 = min(a.P, key0 + a.chunk_len);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int qw = wave % kPrefixQT, half = wave / kPrefixQT;
+    const int qw = wave % QT, half = wave / QT;
     const int qi = q0 + qw * 16 + (lane & 15);
     const bool qvalid = qi < nq;
     const int m = qvalid ? qi / G : 0, h = g * G + (qvalid ? qi % G : 0);
@@ -220,7 +219,7 @@ __global__ __launch_bounds__(128 * kPrefixQT) void attn_prefix_kernel(const Attn
     const int vst = static_cast<int>(a.pv_st), vbase = g * static_cast<int>(a.pv_sh);
     auto request_stage = [&](int kb, int buf) {
         uint8_t* sK = smem + buf * 2 * kStageBytes;
-        request_rows<HD, kStageKeys, 2 * kPrefixQT>(rk, rv, sK, sK + kStageBytes, [&](int row, int which) -> int {
+        request_rows<HD, kStageKeys, 2 * QT>(rk, rv, sK, sK + kStageBytes, [&](int row, int which) -> int {
             const int key = kb + row;
             return key >= key1 ? -1 : (which == 0 ? key * kst + kbase : key * vst + vbase);
         });
@@ -387,16 +386,30 @@ __global__ __launch_bounds__(64) void attn_block_kernel(const AttnArgs a) {
         a.lse[static_cast<size_t>(row) * a.Hq + h] = bad ? __builtin_nanf("") : (run_m + log2f(run_l)) * 0.69314718055994531f;
 }
 
-template <int HD>
-hipError_t launch_prefix_hd(const AttnArgs& a, dim3 grid, hipStream_t st) {
+template <int HD, int QT>
+hipError_t launch_prefix_qt(const AttnArgs& a, hipStream_t st) {
     // one LDS stage holds the whole chunk, else two alternate
     const size_t stage = static_cast<size_t>(2) * kStageKeys * AttnTile<HD>::RB;
     const size_t lds = (a.chunk_len > kStageKeys ? 2 : 1) * stage;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_prefix_kernel<HD>),
+    static_assert(QT * (AttnTile<HD>::DT * 4 + 2) * 64 * 4 <= 2 * kStageKeys * AttnTile<HD>::RB,
+                  "the merge exchange fits in one stage");
+    const int G = a.Hq / a.Hkv;
+    const dim3 grid(a.n_chunks * a.Hkv, (a.m_cap * G + 16 * QT - 1) / (16 * QT));
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_prefix_kernel<HD, QT>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_prefix_kernel<HD>, grid, dim3(128 * kPrefixQT), lds, st, a);
+    hipLaunchKernelGGL((attn_prefix_kernel<HD, QT>), grid, dim3(128 * QT), lds, st, a);
     return hipGetLastError();
+}
+
+// Two query tiles per workgroup while that keeps the grid small (fewer waves per CU read each
+// block from LDS); four once the grid is large, where every workgroup's K/V stages cost L2
+// bandwidth and sharing them over more queries pays.
+template <int HD>
+hipError_t launch_prefix_hd(const AttnArgs& a, hipStream_t st) {
+    const int G = a.Hq / a.Hkv;
+    const long wgs2 = static_cast<long>(a.n_chunks) * a.Hkv * ((a.m_cap * G + 31) / 32);
+    return wgs2 <= 1024 ? launch_prefix_qt<HD, 2>(a, st) : launch_prefix_qt<HD, 4>(a, st);
 }
 
 }  // namespace
@@ -404,13 +417,11 @@ hipError_t launch_prefix_hd(const AttnArgs& a, dim3 grid, hipStream_t st) {
 hipError_t launch_attn_prefix(const AttnArgs& a, hipStream_t st) {
     if (a.n_chunks <= 0) return hipSuccess;
     if (a.chunk_len <= 0 || a.chunk_len % 64 != 0) return hipErrorInvalidValue;
-    const int G = a.Hq / a.Hkv;
-    const dim3 grid(a.n_chunks * a.Hkv, (a.m_cap * G + 16 * kPrefixQT - 1) / (16 * kPrefixQT));
     switch (a.hd) {
-        case 16: return launch_prefix_hd<16>(a, grid, st);
-        case 32: return launch_prefix_hd<32>(a, grid, st);
-        case 64: return launch_prefix_hd<64>(a, grid, st);
-        case 128: return launch_prefix_hd<128>(a, grid, st);
+        case 16: return launch_prefix_hd<16>(a, st);
+        case 32: return launch_prefix_hd<32>(a, st);
+        case 64: return launch_prefix_hd<64>(a, st);
+        case 128: return launch_prefix_hd<128>(a, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -223,9 +223,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
     }
     M = M < 0 ? 0 : (M > p.m_cap ? p.m_cap : M);
     M = __builtin_amdgcn_readfirstlane(M);
-    const int m0 = chunk * MP;
-    if (g >= p.n_groups || m0 >= M) return;       // uniform: nothing for this workgroup
-    const int mrows = min(MP, M - m0);
+    // rows [0, M) split evenly over c_use of the C row workgroups of each group: as many as M
+    // needs, but at least min_chunks (two workgroups streaming the same weight tile, the
+    // second from L2, run faster than one), decided here because M is only known on the device
+    const int c_need = (M + MP - 1) / MP;
+    const int c_use = min(C, max(c_need, p.min_chunks));
+    const int per = c_use > 0 ? (M + c_use - 1) / c_use : 0;   // <= MP
+    const int m0 = chunk * per;
+    if (g >= p.n_groups || chunk >= c_use || m0 >= M) return;   // uniform: nothing to do here
+    const int mrows = min(per, M - m0);
 
     // output columns [c0, c1) of this group: the columns spread evenly over the groups, in
     // multiples of 4 (a lane stores 4 consecutive columns)
@@ -397,9 +403,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
 }
 
 template <int NTW, int WN, int TM, int KSUB, int NBW, int NBA, int EPI>
-hipError_t launch_shape(GemmArgs a, int groups, int splits, hipStream_t st) {
+hipError_t launch_shape(GemmArgs a, const GemmCfg& c, int splits, hipStream_t st) {
     using T = Tile<NTW, WN, TM, KSUB, NBW, NBA>;
+    const int groups = c.groups;
     a.n_groups = groups;
+    a.min_chunks = c.min_chunks;
     a.m_chunks = (a.m_cap + T::MP - 1) / T::MP;
     if (a.m_chunks < 1) a.m_chunks = 1;
     const size_t lds = static_cast<size_t>(T::LDS) + (a.fc_fold ? static_cast<size_t>(a.fc_R) * 4 : 0);
@@ -434,8 +442,8 @@ size_t gemm_lds_bytes(const GemmCfg& c) {
 hipError_t launch_gemm(const GemmArgs& a, const GemmCfg& c, hipStream_t st) {
 #define SPECFOLD_GEMM_CASE(NTW_, WN_, TM_, KS_, NBW_, NBA_)                                         \
     if (c.ntw == NTW_ && c.wn == WN_ && c.tm == TM_ && c.ksub == KS_ && c.nbw == NBW_ && c.nba == NBA_)  \
-        return c.swiglu ? launch_shape<NTW_, WN_, TM_, KS_, NBW_, NBA_, EPI_SWIGLU>(a, c.groups, 1, st)   \
-                        : launch_shape<NTW_, WN_, TM_, KS_, NBW_, NBA_, EPI_PARTIAL>(a, c.groups, c.splits, st);
+        return c.swiglu ? launch_shape<NTW_, WN_, TM_, KS_, NBW_, NBA_, EPI_SWIGLU>(a, c, 1, st)           \
+                        : launch_shape<NTW_, WN_, TM_, KS_, NBW_, NBA_, EPI_PARTIAL>(a, c, c.splits, st);
     SPECFOLD_GEMM_CASES(SPECFOLD_GEMM_CASE)
 #undef SPECFOLD_GEMM_CASE
     return hipErrorInvalidValue;

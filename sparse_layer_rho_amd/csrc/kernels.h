@@ -63,6 +63,7 @@ struct GemmArgs {
     const uint16_t* W;       // [Nout][K]
     int K, Nout;
     int n_groups, m_chunks;  // set by the launcher
+    int min_chunks;          // set by the launcher: rows split over at least this many workgroups
     float* partial;          // [splits][m_cap][Nout]   (partial-sum epilogue)
     uint16_t* act;           // [m_cap][F]              (SwiGLU epilogue)
     int F;
@@ -90,6 +91,7 @@ struct GemmArgs {
 struct GemmCfg {
     int ntw, wn, tm, ksub, nbw, nba, groups, splits;
     bool swiglu;
+    int min_chunks;          // row workgroups per column group used at least (when there are that many)
 };
 // the (ntw, wn, tm, ksub, nbw, nba) shapes compiled
 #define SPECFOLD_GEMM_CASES(X) \
