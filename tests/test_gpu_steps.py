@@ -140,13 +140,23 @@ def test_sparse_qkv_matches_oracle(name):
         assert rel_l2(g, exp) < 1e-2
 
 
-@pytest.mark.parametrize("name", ["tiny", "layer-1.5b", "sweep-14b"])
+# large grids: R = 2112 (N = 64, head_dim 64) and R = 1056 (head_dim 32, prefix 600 = 4 full
+# 128-key chunks + 88) take the prefix kernel's four-query-tile form
+ATTN_SHAPES = {"R2112-d64": (Shape(33, 64, 256, 8, 2, 64, 320, 300), "random", 0.1),
+               "R1056-d32-P600": (Shape(33, 32, 128, 8, 2, 32, 192, 600), "chain", 0.1)}
+
+
+@pytest.mark.parametrize("name", ["tiny", "layer-1.5b", "sweep-14b"] + list(ATTN_SHAPES))
 def test_folded_attention_matches_oracle(name):
-    wl = WORKLOADS[name]
-    case = LayerCase.workload(name)
+    if name in ATTN_SHAPES:
+        shape, tree, delta = ATTN_SHAPES[name]
+        case = LayerCase(shape, 21, tree=tree)
+    else:
+        case = LayerCase.workload(name)
+        delta = WORKLOADS[name].delta
     sh = case.shape
     R = sh.n_branch * sh.block
-    ref = _oracle_steps(case, wl.delta)
+    ref = _oracle_steps(case, delta)
     M = ref["rec_rows"].size
     # bf16-rounded projections feed both sides
     qc, kc, vc = (np.asarray(torch.from_numpy(ref[k].astype(np.float32)).to(torch.bfloat16).float(), np.float64)
