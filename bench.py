@@ -69,6 +69,8 @@ def main():
         return stack_bench(args, wl)
     if wl.branch_sweep:
         return sweep_bench(args, wl)
+    if wl.tree_sweep:
+        return tree_bench(args, wl)
     sh = wl.shape
     R, D, F = sh.rows, sh.hidden, sh.ffn
     dev = torch.device("cuda:0")
@@ -190,6 +192,28 @@ def main():
                 "traffic": measured_traffic(), "avg_us": round(gu_us, 2), "bytes_per_launch": gu_bytes,
                 "tflops": round(2 * M * 2 * F * D / (gu_us * 1e-6) / 1e12, 1)}
 
+    # per-kernel fractions of the vendor peaks (folded step, event-timed launches): MFMA for the
+    # GEMMs and attention, HBM for every kernel; bytes are what each step must read and write
+    # (weights, activations, outputs), not split-K partials or chunk states
+    def kernel_pct(st, m):
+        d, Hq, Hkv, P, N = sh.head_dim, sh.n_q_heads, sh.n_kv_heads, sh.prefix_len, sh.block
+        Nq, Do = (Hq + 2 * Hkv) * d, Hq * d
+        rows = {
+            "gate_rmsnorm": (st["gate_rmsnorm"], 0, 2 * R * D + 2 * R * D + 9 * R),
+            "qkv_gemm_compact_resolve": (st["qkv_gemm_compact_resolve"], 2 * m * Nq * D, 2 * Nq * D + 2 * m * D + 2 * m * Nq),
+            "attention": (st["attn_prefix"] + st["attn_block_merge"], 4 * d * Hq * (P * m + N * R),
+                          4 * P * Hkv * d + 2 * m * Nq + 2 * R * Do),
+            "oproj_gemm": (st["oproj_gemm"], 2 * R * Do * D, 2 * Do * D + 2 * R * Do + 2 * R * D),
+            "gate_up_swiglu_gemm": (st["gate_up_swiglu_gemm"], 2 * m * 2 * F * D, gu_bytes),
+            "down_gemm": (st["down_gemm"], 2 * m * F * D, 2 * F * D + 2 * m * F + 2 * m * D),
+        }
+        out_ = {}
+        for k, (us, flops, byts) in rows.items():
+            sec = us * 1e-6
+            out_[k] = {"us": round(us, 2), "mfma_frac": round(flops / sec / (BF16_PEAK_TFLOPS * 1e12), 4) if flops else None,
+                       "hbm_frac": round(byts / sec / (HBM_PEAK_GBS * 1e9), 4)}
+        return out_
+
     # whole-layer roofline at the vendor peaks: sum over kernels of max(bytes/BW, flops/MFMA)
     def layer_roof_us(m):
         Nq, Do = (sh.n_q_heads + 2 * sh.n_kv_heads) * sh.head_dim, sh.n_q_heads * sh.head_dim
@@ -226,6 +250,7 @@ def main():
         "layer_roofline_frac": {"folded": round(layer_roof_us(M) / (folded["ms_per_step"] * 1e3), 4),
                                 "dense": round(layer_roof_us(R) / (dense["ms_per_step"] * 1e3), 4)},
         "roofline": roofline,
+        "kernel_frac_of_peak": kernel_pct(st_f, M),
         "stages_us": {"folded": {k: round(v, 2) for k, v in st_f.items()},
                       "dense": {k: round(v, 2) for k, v in st_d.items()}},
         "wall_ms_per_step": round(folded["wall_ms_per_step"], 5),
@@ -487,8 +512,10 @@ def sweep_bench(args, wl):
     pk_h, pv_h = prefix_kv(base, wl.base_seed, 0)
     w0 = {k: to_dev(v) for k, v in w_host.items()}
     n_copies = max(2, int(np.ceil(600e6 / base.weight_bytes_bf16())))
-    lws = [sf.layer_weights_struct(w0)] + [sf.layer_weights_struct({k: v.clone() for k, v in w0.items()})
-                                          for _ in range(n_copies - 1)]
+    # the copies must outlive every launch that reads them: the structs hold raw pointers, and
+    # graph capture empties the allocator's cache, returning freed blocks to the runtime
+    copies = [w0] + [{k: v.clone() for k, v in w0.items()} for _ in range(n_copies - 1)]
+    lws = [sf.layer_weights_struct(c) for c in copies]
     pk, pv = to_dev(pk_h), to_dev(pv_h)
     pf = sf.prefix_view(pk, pv)
     print(f"[bench] sweep ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -530,6 +557,77 @@ def sweep_bench(args, wl):
     print(json.dumps({"metric": METRIC, "unit": "branch-tokens/s", "workload": args.workload, "n_gpus": 1,
                       "dtype": "bf16", "data": "synthetic", "regime": f"cold ({n_copies} weight copies)",
                       "points": points}), flush=True)
+
+
+def tree_bench(args, wl):
+    """One layer at fixed B swept over the draft tree's shape (siblings of main, random trees of
+    bounded depth, a chain), folded at the workload's delta against dense (delta 0); each tree
+    is verified against the oracle, teacher-forced on the GPU's mask."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from sparse_layer_rho_amd import specfold as sf
+    from synth import bf16_round, layer_weights, prefix_kv, step_inputs, tree_of
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sh = wl.shape
+    R, D = sh.rows, sh.hidden
+
+    def to_dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev).to(torch.bfloat16)
+
+    t0 = time.time()
+    w_host = layer_weights(sh, wl.base_seed, 0)
+    pk_h, pv_h = prefix_kv(sh, wl.base_seed, 0)
+    w0 = {k: to_dev(v) for k, v in w_host.items()}
+    n_copies = max(2, int(np.ceil(600e6 / sh.weight_bytes_bf16())))
+    # the copies must outlive every launch that reads them: the structs hold raw pointers, and
+    # graph capture empties the allocator's cache, returning freed blocks to the runtime
+    copies = [w0] + [{k: v.clone() for k, v in w0.items()} for _ in range(n_copies - 1)]
+    lws = [sf.layer_weights_struct(c) for c in copies]
+    pk, pv = to_dev(pk_h), to_dev(pv_h)
+    pf = sf.prefix_view(pk, pv)
+    ws = sf.new_workspace(sh)
+    y = torch.empty((R, D), dtype=torch.bfloat16, device=dev)
+    st = {"fold": torch.zeros(R, dtype=torch.uint8, device=dev), "rec_count": torch.zeros(1, dtype=torch.int32, device=dev)}
+    print(f"[bench] tree sweep ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    points = []
+    for kind in wl.tree_sweep:
+        parent = tree_of(kind, sh.n_branch, wl.base_seed, 0)
+        depth = np.zeros(sh.n_branch, dtype=np.int64)
+        for i in range(1, sh.n_branch):
+            depth[i] = depth[parent[i]] + 1
+        inp = step_inputs(sh, wl.base_seed, 0, child_law=wl.child_law, parent=parent)
+        H_host = bf16_round(inp["H"].astype(np.float32))
+        H = to_dev(H_host.reshape(R, D))
+        res = {}
+        for delta in (wl.delta, 0.0):
+            sf.verify_layer(sh, parent, lws[0], pf, None, H, delta, y, ws, stats=st)
+            torch.cuda.synchronize()
+            M = int(st["rec_count"].item())
+            ff = float(st["fold"].cpu().numpy().reshape(sh.n_branch, sh.block)[1:].mean())
+            reps = max(1, args.steps // (4 * n_copies))
+            ms = graph_time(torch, [lambda k=k, delta=delta: sf.verify_layer(sh, parent, lws[k], pf, None, H, delta, y, ws)
+                                    for k in range(n_copies)], reps=reps) / n_copies
+            res[delta] = (ms, M, ff)
+        sf.verify_layer(sh, parent, lws[0], pf, None, H, wl.delta, y, ws, stats=st)
+        torch.cuda.synchronize()
+        fold_g = st["fold"].cpu().numpy().reshape(sh.n_branch, sh.block).astype(bool)
+        Hd = H_host.astype(np.float64)
+        ref = oracle.verify_layer(Hd, parent, w_host, pk_h, pv_h, wl.delta, sh, fold=fold_g)
+        got = y.float().cpu().numpy().astype(np.float64).reshape(Hd.shape)
+        err = float(np.linalg.norm(got - ref["H_out"]) / np.linalg.norm(ref["H_out"]))
+        (msf, M, ff), (msd, _, _) = res[wl.delta], res[0.0]
+        points.append({"tree": kind, "parent": parent.tolist(), "max_depth": int(depth.max()),
+                       "rec_rows": M, "fold_fraction_drafts": round(ff, 4), "us": round(msf * 1e3, 2),
+                       "dense_us": round(msd * 1e3, 2), "branch_tokens_per_s": round(R / (msf * 1e-3), 1),
+                       "speedup_vs_dense": round(msd / msf, 4), "rel_l2": round(err, 6), "ok": err <= 2e-2})
+        print(f"[bench] tree {kind} done", file=sys.stderr, flush=True)
+    print(json.dumps({"metric": METRIC, "unit": "branch-tokens/s", "workload": args.workload, "n_gpus": 1,
+                      "dtype": "bf16", "data": "synthetic", "delta": wl.delta, "drafts": sh.n_branch - 1,
+                      "regime": f"cold ({n_copies} weight copies)", "points": points}), flush=True)
 
 
 def cpu_baseline_leg(sh, wl, parent, H_host, w_host, pk_h, pv_h, gpu_res, seconds):

@@ -206,13 +206,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
     const int y = blockIdx.y, S = gridDim.y;
-    // blockIdx.x -> (column group, row chunk).  Consecutive workgroup ids go round-robin over
-    // the 8 XCDs, so the chunks of one group get ids that share id % 8 and sit within 8*C of
-    // each other: they run on one XCD at about the same time and the group's weights come from
-    // that XCD's L2 after the first chunk fetched them.
     const int C = p.m_chunks;
-    const int id = blockIdx.x, grp = id / (8 * C), rem = id - grp * 8 * C;
-    const int chunk = rem >> 3, g = grp * 8 + (rem & 7);
 
     int M;
     const bool fused = p.fc_fold != nullptr;
@@ -227,10 +221,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
     // needs, but at least min_chunks (two workgroups streaming the same weight tile, the
     // second from L2, run faster than one), decided here because M is only known on the device
     const int c_need = (M + MP - 1) / MP;
-    const int c_use = min(C, max(c_need, p.min_chunks));
-    const int per = c_use > 0 ? (M + c_use - 1) / c_use : 0;   // <= MP
+    const int c_use = max(1, min(C, max(c_need, p.min_chunks)));
+    // blockIdx.x -> (column group, row workgroup) over the c_use row workgroups in use: the
+    // workgroups with work take the lowest ids (the grid is sized for C), so consecutive ids
+    // -- which the dispatcher deals round-robin to the XCDs and, within an XCD, to its CUs --
+    // spread them evenly over the CUs whatever C and c_use are (interleaving idle ids with a
+    // period that shares a factor with the CU count would load some CUs twice and leave others
+    // idle).  The row workgroups of one group share id % 8 and sit within 8 c_use ids of each
+    // other: they run on one XCD at about the same time and the group's weights come from that
+    // XCD's L2 after the first fetched them.
+    const int id = blockIdx.x, grp = id / (8 * c_use), rem = id - grp * 8 * c_use;
+    const int chunk = rem >> 3, g = grp * 8 + (rem & 7);
+    const int per = (M + c_use - 1) / c_use;   // <= MP
     const int m0 = chunk * per;
-    if (g >= p.n_groups || chunk >= c_use || m0 >= M) return;   // uniform: nothing to do here
+    if (g >= p.n_groups || m0 >= M) return;    // uniform: nothing to do here
     const int mrows = min(per, M - m0);
 
     // output columns [c0, c1) of this group: the columns spread evenly over the groups, in

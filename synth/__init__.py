@@ -21,4 +21,5 @@ from .inputs import (  # noqa: F401
     parent_tree,
     prefix_kv,
     step_inputs,
+    tree_of,
 )

@@ -81,6 +81,7 @@ class Workload:
     child_law: str = "lognormal"    # "lognormal" (with unmasked rows) or "tiny"
     branch_sweep: tuple = ()
     delta_sweep: tuple = ()
+    tree_sweep: tuple = ()          # tree shapes: "star", "depthK" (random, depth <= K), "chain"
     note: str = ""
 
 
@@ -101,7 +102,18 @@ WORKLOADS: dict[str, Workload] = {
     "sweep-14b": Workload("sweep-14b", Shape(9, 32, 5120, 40, 8, 128, 13824, 4096), 4, 0.1,
                           branch_sweep=(2, 4, 6, 8),
                           delta_sweep=(0.0, 0.01, 0.1, 0.2, 0.3, 0.5, 0.7)),
+    # one layer at 1.5B-class shape with B = 7 drafts, swept over the draft tree's shape: seven
+    # siblings of main (depth 1), random trees of depth <= 2, 3, 4, and a 7-deep chain
+    "draft-shapes-1.5b": Workload("draft-shapes-1.5b", Shape(8, 32, 1536, 12, 2, 128, 8960, 512), 5, 0.1,
+                                  tree_sweep=("star", "depth2", "depth3", "depth4", "chain")),
 }
+
+
+def tree_of(kind: str, n_branch: int, base_seed: int, step: int) -> np.ndarray:
+    """Parent map for a tree-shape name: "star", "chain", or "depthK" (random, depth <= K)."""
+    if kind.startswith("depth"):
+        return parent_tree(n_branch, base_seed, step, "random", max_depth=int(kind[5:]))
+    return parent_tree(n_branch, base_seed, step, kind)
 
 
 # ---------------------------------------------------------------- bfloat16 rounding
