@@ -205,7 +205,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
-    const int y = blockIdx.y, S = gridDim.y;
+    const int S = gridDim.y;
     const int C = p.m_chunks;
 
     int M;
@@ -222,15 +222,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
     // second from L2, run faster than one), decided here because M is only known on the device
     const int c_need = (M + MP - 1) / MP;
     const int c_use = max(1, min(C, max(c_need, p.min_chunks)));
-    // blockIdx.x -> (column group, row workgroup) over the c_use row workgroups in use: the
-    // workgroups with work take the lowest ids (the grid is sized for C), so consecutive ids
-    // -- which the dispatcher deals round-robin to the XCDs and, within an XCD, to its CUs --
-    // spread them evenly over the CUs whatever C and c_use are (interleaving idle ids with a
-    // period that shares a factor with the CU count would load some CUs twice and leave others
-    // idle).  The row workgroups of one group share id % 8 and sit within 8 c_use ids of each
-    // other: they run on one XCD at about the same time and the group's weights come from that
-    // XCD's L2 after the first fetched them.
-    const int id = blockIdx.x, grp = id / (8 * c_use), rem = id - grp * 8 * c_use;
+    // linear workgroup id -> (split, column group, row workgroup) over the c_use row
+    // workgroups in use: the busy workgroups of all splits take the lowest ids (the grid is
+    // sized for C), so consecutive ids -- which the dispatcher deals round-robin to the XCDs
+    // and, within an XCD, to its CUs -- spread them evenly over the CUs whatever C, c_use and
+    // S are (interleaving idle ids with a period that shares a factor with the CU count would
+    // load some CUs twice and leave others idle).  The row workgroups of one group share
+    // id % 8 and sit within 8 c_use ids of each other: they run on one XCD at about the same
+    // time and the group's weights come from that XCD's L2 after the first fetched them.
+    const int A = ((p.n_groups + 7) / 8) * 8 * c_use;          // busy workgroups per split
+    const int lin = blockIdx.x + gridDim.x * blockIdx.y;
+    if (lin >= S * A) return;
+    const int y = lin / A, id = lin - y * A;
+    const int grp = id / (8 * c_use), rem = id - grp * 8 * c_use;
     const int chunk = rem >> 3, g = grp * 8 + (rem & 7);
     const int per = (M + c_use - 1) / c_use;   // <= MP
     const int m0 = chunk * per;
