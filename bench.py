@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="stack workloads: layers (default: the workload's)")
     ap.add_argument("--stack-steps", type=int, default=0, help="stack workloads: steps (default: the workload's)")
     ap.add_argument("--no-gate-flat", action="store_true", help="skip the large flat gate/compaction timing")
+    ap.add_argument("--serialized", action="store_true",
+                    help="also time serialized verification (each branch alone, delta 0) and compare it "
+                         "with the batched dense layer")
     return ap.parse_args()
 
 
@@ -259,6 +262,10 @@ def main():
     if not args.no_gate_flat:
         out["gate_flat"] = gate_flat_leg(torch, sf, dev)
 
+    if args.serialized:
+        out["serialized"] = serialized_leg(torch, sf, sh, lws, pf, H_in, results[0.0]["H_out"], dense, args,
+                                           H_host, w_host, pk_h, pv_h)
+
     if args.copy_probe_mb > 0:
         n = args.copy_probe_mb * (1 << 20) // 4
         a = torch.empty(n, dtype=torch.float32, device=dev).uniform_()
@@ -272,6 +279,48 @@ def main():
         out["cpu_baseline"], out["verified"] = cpu_baseline_leg(
             sh, wl, parent, H_host, w_host, pk_h, pv_h, results[wl.delta], args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def serialized_leg(torch, sf, sh, lws, pf, H_in, H_dense, dense, args, H_host, w_host, pk_h, pv_h):
+    """Serialized verification [SpecFold summary, App. C]: every branch verified alone (one
+    branch, parent map [-1], delta 0), as a vanilla verifier would, B+1 layer calls per step.
+    Reports its throughput against the batched dense layer (delta 0, same kernels) and how its
+    outputs compare with the batched layer's: the split-K decomposition depends on the row
+    count, so the fp32 sums may be ordered differently and round to different bf16 values."""
+    import numpy as np
+
+    import oracle
+
+    N, D = sh.block, sh.hidden
+    sh1 = sh.with_branches(1)
+    ws1 = sf.new_workspace(sh1)
+    y = torch.empty_like(H_dense)
+    par1 = [-1]
+    n_copies = len(lws)
+
+    def run_all(k):
+        for i in range(sh.n_branch):
+            sf.verify_layer(sh1, par1, lws[k], pf, None, H_in[i * N:(i + 1) * N], 0.0, y[i * N:(i + 1) * N], ws1)
+
+    run_all(0)
+    torch.cuda.synchronize()
+    same = (y.view(torch.int16) == H_dense.view(torch.int16)).all(dim=1)
+    diff = (y.float() - H_dense.float()).abs()
+    reps = max(1, args.steps // (4 * n_copies))
+    ms = graph_time(torch, [lambda k=k: run_all(k) for k in range(n_copies)], reps=reps) / n_copies
+    # oracle: the plain layer on the first and the last branch alone
+    errs = []
+    for i in (0, sh.n_branch - 1):
+        ref = oracle.dense_branch_layer(H_host[i].astype(np.float64), w_host, pk_h, pv_h, sh)
+        got = y[i * N:(i + 1) * N].float().cpu().numpy().astype(np.float64)
+        errs.append(float(np.linalg.norm(got - ref) / np.linalg.norm(ref)))
+    R = sh.rows
+    return {"ms_per_step": round(ms, 5), "branch_tokens_per_s": round(R / (ms * 1e-3), 1),
+            "batched_dense_speedup": round(ms / dense["ms_per_step"], 4),
+            "rows_bitwise_equal_to_batched": round(float(same.float().mean().item()), 4),
+            "max_abs_diff_vs_batched": round(float(diff.max().item()), 6),
+            "oracle_rel_l2": [round(e, 6) for e in errs], "ok": max(errs) <= 2e-2,
+            "note": "each of the B+1 branches alone (n_branch 1, delta 0), graph-replayed"}
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gate_up_swiglu_gemm_layer-1.5b_traffic.md")

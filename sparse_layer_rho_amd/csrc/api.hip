@@ -47,8 +47,30 @@ Dims dims_of(const specfold_shape& s) {
 // two or three workgroups share a CU and hide each other's waits.  Measured on the 1.5B shapes:
 // the recompute projections run two 64-row chunks per column group (M ~ 100), the gate/up weight
 // stage spans 256 bytes of every row, and the long-K down projection keeps 128-row chunks.
-// Partial-sum projections split K until about 384 workgroups are busy.
+// The projections: tile shape from the row count (performance only), K-splits from the
+// projection's shape alone.
 enum GemmKind { GEMM_QKV, GEMM_O, GEMM_GATE_UP, GEMM_DOWN };
+
+// K-splits of a partial-sum projection as a function of (kind, output columns, K) only -- not
+// of the row count -- so every output's sum is formed in the same order whatever the batch:
+// a batched verification pass matches serialized verification (each branch alone) bit for bit
+// [SpecFold summary, App. C: the drift of batched matmuls comes from shape-dependent
+// accumulation order].  The counts aim at about 512 (QKV), 768 (o_proj) and 384 (down) busy
+// workgroups with the row workgroups a 288-row layer has (2, 5 and 1 per column group), as
+// measured best on the 1.5B layer.
+int splits_for(GemmKind kind, int n_cols, int k) {
+    if (kind == GEMM_GATE_UP) return 1;             // SwiGLU needs the whole sum
+    const int rows = kind == GEMM_QKV ? 2 : kind == GEMM_O ? 5 : 1;
+    int cols = 64;
+    if (kind != GEMM_DOWN && ((n_cols + 63) / 64) * rows < 128) cols = 32;
+    const int busy = ((n_cols + cols - 1) / cols) * rows;
+    const int target = kind == GEMM_DOWN ? 384 : kind == GEMM_O ? 768 : 512;
+    int s = (target + busy / 2) / busy;
+    int smax = (k + 127) / 128 / 2;                  // two 128-element units per split at least
+    if (smax > 32) smax = 32;                        // the epilogues batch up to 32 splits
+    if (s > smax) s = smax;
+    return s < 1 ? 1 : s;
+}
 
 GemmCfg pick_gemm(GemmKind kind, int n_cols, int k, int max_rows, int busy_chunks) {
     GemmCfg c{};
@@ -67,20 +89,9 @@ GemmCfg pick_gemm(GemmKind kind, int n_cols, int k, int max_rows, int busy_chunk
     const int cap = gemm_group_cols(c);
     c.groups = (n_cols + cap - 1) / cap;
     // the recompute-row projections keep two row workgroups per column group however small M
-    // is (the split count below assumes them)
+    // is (the split counts assume them)
     c.min_chunks = (kind == GEMM_QKV || kind == GEMM_GATE_UP) ? 2 : 1;
-    c.splits = 1;
-    if (!c.swiglu) {
-        const int chunks = (max_rows + gemm_chunk_rows(c) - 1) / gemm_chunk_rows(c);
-        const int busy = c.groups * (busy_chunks < chunks ? busy_chunks : chunks);
-        // workgroups aimed at per launch (measured best on the 1.5B layer shapes)
-        const int target = kind == GEMM_DOWN ? 384 : kind == GEMM_O ? 768 : 512;
-        int s = (target + busy / 2) / busy;
-        int smax = (k + 64 * c.ksub - 1) / (64 * c.ksub) / (c.ksub == 1 ? 4 : 2);
-        if (smax > 32) smax = 32;                          // the epilogues batch up to 32 splits
-        if (s > smax) s = smax;
-        c.splits = s < 1 ? 1 : s;
-    }
+    c.splits = splits_for(kind, n_cols, k);
     return c;
 }
 

@@ -37,6 +37,7 @@ namespace {
 constexpr uint32_t kOobRow = kOob;
 constexpr uint32_t kOobK = 0x80000000u;
 constexpr int kStageK = 64;                 // K elements per compute stage
+constexpr int kSplitUnit = 128;             // K-splits cut K at multiples of this
 constexpr int kRowB = 128;                  // bytes of one activation row in one compute stage
 
 enum { EPI_PARTIAL = 0, EPI_SWIGLU = 1 };
@@ -247,12 +248,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
     const int c0 = static_cast<int>(static_cast<int64_t>(g) * (ncols / 4) / p.n_groups) * 4;
     const int c1 = static_cast<int>(static_cast<int64_t>(g + 1) * (ncols / 4) / p.n_groups) * 4;
 
-    // K range of this split: whole weight stages; compute stages inside it
-    const int nws_all = (p.K + KSUB * kStageK - 1) / (KSUB * kStageK);
-    const int ws_begin = static_cast<int>(static_cast<int64_t>(y) * nws_all / S);
-    const int nws = static_cast<int>(static_cast<int64_t>(y + 1) * nws_all / S) - ws_begin;
-    const int k_begin = ws_begin * KSUB * kStageK;
-    const int k_stop = min(p.K, (ws_begin + nws) * KSUB * kStageK);
+    // K range of this split: whole units of kSplitUnit elements (a multiple of every weight
+    // stage), so the split boundaries -- and with them the order in which every output's sum
+    // is formed -- depend on K and the split count only, not on the tile shape or the rows
+    static_assert(kSplitUnit % (KSUB * kStageK) == 0, "weight stages tile the split unit");
+    const int nun = (p.K + kSplitUnit - 1) / kSplitUnit;
+    const int u0 = static_cast<int>(static_cast<int64_t>(y) * nun / S);
+    const int u1 = static_cast<int>(static_cast<int64_t>(y + 1) * nun / S);
+    const int k_begin = u0 * kSplitUnit;
+    const int k_stop = min(p.K, u1 * kSplitUnit);
+    const int nws = k_stop > k_begin ? (k_stop - k_begin + KSUB * kStageK - 1) / (KSUB * kStageK) : 0;
     const int nst = k_stop > k_begin ? (k_stop - k_begin + kStageK - 1) / kStageK : 0;
 
     // weight row of slot row r (r < WROWS), or -1 past the group.  SwiGLU slots interleave

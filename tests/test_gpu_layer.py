@@ -128,3 +128,35 @@ def test_layer_14b_shape_sweep_points(B):
         res = case.run(delta)
         _, err = case.check(delta, res)
         print(f"14b B={B} delta={delta}: fold {res['fold'][1:].mean():.3f} rel L2 {err:.2e}")
+
+
+@pytest.mark.parametrize("shape", [
+    Shape(5, 24, 1024, 8, 2, 128, 2816, 200),     # R = 120 batched, 24 alone: different tile shapes
+    Shape(9, 32, 1536, 12, 2, 128, 8960, 512),    # the 1.5B layer
+])
+def test_batched_matches_serialized_bitwise(shape):
+    """The K-split of every projection depends on its shape only, not on the row count, so the
+    batched dense layer (delta 0) gives every branch the bits it gets when verified alone --
+    the serialized verification of [SpecFold summary, App. C] -- and the main branch, which
+    never folds and attends only to its own keys, gets the same bits folded or not."""
+    from gpu_case import DEV, dev_bf16
+    from sparse_layer_rho_amd import specfold as sf
+    case = LayerCase(shape, 31)
+    B1, N, D = shape.n_branch, shape.block, shape.hidden
+    R = B1 * N
+    w, pk, pv = case.device()
+    H = dev_bf16(case.H.reshape(R, D))
+    ws = sf.new_workspace(shape)
+    dense = torch.empty((R, D), dtype=torch.bfloat16, device=DEV)
+    sf.verify_layer(shape, case.parent, w, pk, pv, H, 0.0, dense, ws)
+    folded = torch.empty_like(dense)
+    sf.verify_layer(shape, case.parent, w, pk, pv, H, 0.1, folded, ws)
+    sh1 = shape.with_branches(1)
+    ws1 = sf.new_workspace(sh1)
+    alone = torch.empty_like(dense)
+    for i in range(B1):
+        sf.verify_layer(sh1, [-1], w, pk, pv, H[i * N:(i + 1) * N], 0.0, alone[i * N:(i + 1) * N], ws1)
+    torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int16).cpu().numpy()
+    assert np.array_equal(bits(dense), bits(alone))
+    assert np.array_equal(bits(folded)[:N], bits(dense)[:N])
