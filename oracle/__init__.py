@@ -37,3 +37,4 @@ from .layer import (  # noqa: F401
 )
 from .tables import verify_layer_tables  # noqa: F401
 from .correction import folded_attention_by_correction  # noqa: F401
+from .head import embed, final_norm, greedy_tokens, lm_head_logits, verify_head  # noqa: F401,E402
