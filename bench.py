@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="stack workloads: layers (default: the workload's)")
     ap.add_argument("--stack-steps", type=int, default=0, help="stack workloads: steps (default: the workload's)")
     ap.add_argument("--no-gate-flat", action="store_true", help="skip the large flat gate/compaction timing")
+    ap.add_argument("--with-head", action="store_true",
+                    help="stack workloads: also time whole verification passes from token ids: embedding "
+                         "gather, the layer stack and the final RMSNorm + LM head + greedy token")
+    ap.add_argument("--vocab", type=int, default=151936, help="vocabulary of the --with-head passes")
     ap.add_argument("--serialized", action="store_true",
                     help="also time serialized verification (each branch alone, delta 0) and compare it "
                          "with the batched dense layer")
@@ -536,7 +540,82 @@ def stack_bench(args, wl):
         "verified": {"ok": bool(ok_mask and err <= 2e-2), "layer": 0, "step": 0, "rel_l2": round(err, 6),
                      "mask_match_outside_band": ok_mask},
     }
+    if args.with_head:
+        out["pass_with_head"] = pass_leg(torch, sf, sh, wl, args, steps, lws, pfs, ws, buf, fold, cnt, L, S, dev)
     print(json.dumps(out), flush=True)
+
+
+def pass_leg(torch, sf, sh, wl, args, steps, lws, pfs, ws, buf, fold, cnt, L, S, dev):
+    """Whole verification passes from token ids [SpecFold summary, App. B]: embedding gather,
+    the L-layer stack (folded at the workload's delta, or dense), final RMSNorm + LM head +
+    greedy token of every row.  The drafts' tokens copy their parent's block with 1-4 newly
+    unmasked positions, so the first layer's gate sees identical rows wherever a draft agrees
+    with its parent.  The head is checked against the oracle on sampled rows of the last
+    layer's output."""
+    import numpy as np
+
+    import oracle
+    from synth import step_tokens
+
+    R, D, V = sh.rows, sh.hidden, args.vocab
+    g = torch.Generator(device=dev)
+    g.manual_seed(7919 * wl.base_seed + 17)
+    E = torch.randn(V, D, device=dev, generator=g).to(torch.bfloat16)
+    W_lm = (0.02 * torch.randn(V, D, device=dev, generator=g)).to(torch.bfloat16)
+    ln_f = torch.ones(D, dtype=torch.bfloat16, device=dev)
+    toks = [torch.from_numpy(step_tokens(sh, V, wl.base_seed, s, steps[s][0]).reshape(R)).to(dev) for s in range(S)]
+    hws = sf.head_workspace(sh, V)
+    H0 = torch.empty((R, D), dtype=torch.bfloat16, device=dev)
+    tok_out = torch.empty(R, dtype=torch.int32, device=dev)
+    logit_out = torch.empty(R, dtype=torch.float32, device=dev)
+
+    def run_pass(s, delta, stats=False):
+        sf.embed(sh, toks[s], E, H0)
+        x = H0
+        for l in range(L):
+            y = buf[l % 2]
+            sf.verify_layer(sh, steps[s][0], lws[l], pfs[l], None, x, delta, y, ws,
+                            stats={"fold": fold[l, :R], "rec_count": cnt[l, :1]} if stats else None)
+            x = y
+        sf.lm_head(sh, x, ln_f, W_lm, tok_out, logit_out, hws)
+        return x
+
+    res = {}
+    for delta in (wl.delta, 0.0):
+        ff = []
+        for s in range(S):
+            run_pass(s, delta, stats=True)
+            torch.cuda.synchronize()
+            ff.append(fold[:, :R].cpu().numpy().reshape(L, sh.n_branch, sh.block)[:, 1:].mean(axis=(1, 2)))
+        reps = max(1, args.steps // (S * 4))
+        ms = graph_time(torch, [lambda s=s: run_pass(s, delta) for s in range(S)], reps=reps) / S
+        res[delta] = (ms, np.mean(ff, axis=0))
+        print(f"[bench] pass with head, delta {delta}: {ms:.3f} ms", file=sys.stderr, flush=True)
+    reps = max(1, args.steps)
+    embed_ms = graph_time(torch, [lambda: sf.embed(sh, toks[0], E, H0)], reps=reps)
+    head_ms = graph_time(torch, [lambda: sf.lm_head(sh, buf[0], ln_f, W_lm, tok_out, logit_out, hws)], reps=reps)
+    # the head on the last layer's output of step 0, folded, against the oracle (sampled rows)
+    x = run_pass(0, wl.delta)
+    torch.cuda.synchronize()
+    rows = np.array([0, R // 3, R // 2, R - 1])
+    Xh = x.float().cpu().numpy().astype(np.float64)[rows]
+    xn = oracle.final_norm(Xh, np.ones(D), sh.rms_eps)
+    Wh = W_lm.float().cpu().numpy().astype(np.float64)
+    logits = oracle.lm_head_logits(xn, Wh)
+    tok_o, mx = oracle.greedy_tokens(logits)
+    tg = tok_out.cpu().numpy()[rows]
+    bound = (2.0 ** -8 + D * 2.0 ** -24) * (np.abs(xn) @ np.abs(Wh).T).max(axis=1)
+    ok = bool((logits[np.arange(rows.size), tg] >= mx - 2 * bound).all())
+    (fms, ffold), (dms, _) = res[wl.delta], res[0.0]
+    head_bytes = 2 * V * D + 2 * R * D
+    return {"vocab": V, "ms_per_pass": round(fms, 5), "dense_ms_per_pass": round(dms, 5),
+            "speedup_vs_dense": round(dms / fms, 4), "branch_tokens_per_s": round(R / (fms * 1e-3), 1),
+            "embed_us": round(1e3 * embed_ms, 2), "lm_head_us": round(1e3 * head_ms, 2),
+            "lm_head_hbm_frac": round(head_bytes / (head_ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+            "fold_fraction_drafts_per_layer": [round(float(v), 4) for v in ffold],
+            "head_tokens_match_oracle": bool(np.array_equal(tg, tok_o)), "head_within_bound": ok,
+            "data": "token ids: main uniform, drafts copy the parent's block with 1-4 new tokens; "
+                    "E ~ N(0,1), W_lm ~ N(0, 0.02^2), final norm weight 1 (seeded, on the device)"}
 
 
 def sweep_bench(args, wl):

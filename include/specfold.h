@@ -263,6 +263,35 @@ int specfold_verify_layer(const specfold_shape* shape, const int32_t* parent_hos
                           const specfold_trace* trace, void* ws, size_t ws_bytes,
                           void* stream);
 
+/* ---------------------------------------------------------------- either side of the stack
+ * [SpecFold summary, App. B]: the folded kernels cover the transformer layers; the token
+ * embedding before the first layer and the language-model head after the last one stay
+ * outside them and are not folded -- every row of every branch gets its logits.
+ * R = n_branch * block rows, D = hidden; vocab V >= 1.
+ *
+ * specfold_embed: H[r] = E[tokens[r]] for every row; a token id outside [0, V) gives a row of
+ * NaN.  tokens [R] int32 device, E [V][D] bf16 device, H [R][D] bf16 out.
+ */
+int specfold_embed(const specfold_shape* shape, const int32_t* tokens, const specfold_bf16* E,
+                   int32_t vocab, specfold_bf16* H, void* stream);
+
+/* Bytes of workspace specfold_lm_head needs for this shape and vocabulary (0 if invalid). */
+size_t specfold_head_workspace_bytes(const specfold_shape* shape, int32_t vocab);
+
+/* specfold_lm_head: final RMSNorm, LM head and greedy token of every row:
+ *   xn = RMSNorm(H[r]) * ln_f (rms_eps of the shape);  logits[r][v] = xn . W_lm[v] (fp32
+ *   accumulation, no bias);  token[r] = the lowest index among the maximal logits, logit[r]
+ *   that maximum.  The logits are never stored: each workgroup keeps its columns' best per
+ *   row and a second launch merges them in column order.  NaN logits are never chosen; a
+ *   row without a finite or infinite candidate gets token -1 and logit NaN.
+ *   H [R][D] bf16, ln_f [D] bf16, W_lm [V][D] bf16 (torch Linear layout; any size -- the
+ *   vocabulary is streamed in pieces under 1 GB); token [R] int32 out, logit [R] fp32 out;
+ *   ws: specfold_head_workspace_bytes(shape, vocab) bytes, any contents.
+ */
+int specfold_lm_head(const specfold_shape* shape, const specfold_bf16* H, const specfold_bf16* ln_f,
+                     const specfold_bf16* w_lm, int32_t vocab, int32_t* token, float* logit,
+                     void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

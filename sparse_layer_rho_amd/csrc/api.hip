@@ -362,6 +362,51 @@ hipError_t run_ffn(const Dims& d, const Layout& L, const uint16_t* xn2, const ui
 
 }  // namespace
 
+// ---------------------------------------------------------------- LM head layout
+// Vocabulary pieces: the GEMM addresses its weights with 32-bit buffer offsets below 1 GB, so
+// W_lm streams in pieces of at most this many rows (a multiple of the 64-column groups).
+struct HeadLayout {
+    GemmCfg cfg;
+    int piece;                   // vocabulary rows per launch
+    int groups;                  // column groups over all pieces
+    size_t xn, val, idx, total;
+};
+
+int head_piece_rows(int D) {
+    const int64_t rows = ((int64_t(1) << 30) - 1) / (2 * static_cast<int64_t>(D));
+    return static_cast<int>(rows / 64 * 64);
+}
+
+HeadLayout head_layout(const specfold_shape& s, int V) {
+    HeadLayout h{};
+    const int R = s.n_branch * s.block, D = s.hidden;
+    // one workgroup row covers 128 rows (64 for small R); 64 columns per group; no K split
+    h.cfg = R > 64 ? GemmCfg{4, 1, 2, 1, 4, 2, 0, 1, false, 1, true} : GemmCfg{4, 1, 1, 1, 3, 2, 0, 1, false, 1, true};
+    h.piece = head_piece_rows(D);
+    const int cap = gemm_group_cols(h.cfg);
+    h.groups = 0;
+    for (int v0 = 0; v0 < V; v0 += h.piece) {
+        const int n = V - v0 < h.piece ? V - v0 : h.piece;
+        h.groups += (n + cap - 1) / cap;
+    }
+    size_t off = 0;
+    auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+    h.xn = take(static_cast<size_t>(R) * D * 2);
+    h.val = take(static_cast<size_t>(h.groups) * R * 4);
+    h.idx = take(static_cast<size_t>(h.groups) * R * 4);
+    h.total = off;
+    return h;
+}
+
+int check_head_shape(const specfold_shape* s, int32_t vocab) {
+    int e = check_rows_shape(s, SPECFOLD_MAX_BLOCK);
+    if (e) return e;
+    if (vocab < 1) return SPECFOLD_ERR_SHAPE;
+    if (2 * static_cast<int64_t>(s->n_branch) * s->block * s->hidden >= (int64_t(1) << 30))
+        return SPECFOLD_ERR_UNSUPPORTED;
+    return SPECFOLD_OK;
+}
+
 extern "C" {
 
 int specfold_version(void) { return SPECFOLD_VERSION; }
@@ -631,4 +676,58 @@ int specfold_verify_layer(const specfold_shape* shape, const int32_t* parent_hos
     return SPECFOLD_OK;
 }
 
+
+size_t specfold_head_workspace_bytes(const specfold_shape* shape, int32_t vocab) {
+    if (check_head_shape(shape, vocab)) return 0;
+    return head_layout(*shape, vocab).total;
+}
+
+int specfold_embed(const specfold_shape* shape, const int32_t* tokens, const specfold_bf16* E, int32_t vocab,
+                   specfold_bf16* H, void* stream) {
+    int e = check_rows_shape(shape, SPECFOLD_MAX_BLOCK);
+    if (e) return e;
+    if (vocab < 1) return SPECFOLD_ERR_SHAPE;
+    if ((e = dev(tokens)) || (e = dev(E)) || (e = dev(H))) return e;
+    const int R = shape->n_branch * shape->block, D = shape->hidden;
+    if (overlaps(H, static_cast<size_t>(R) * D * 2, E, static_cast<size_t>(vocab) * D * 2) ||
+        overlaps(H, static_cast<size_t>(R) * D * 2, tokens, static_cast<size_t>(R) * 4))
+        return SPECFOLD_ERR_ALIAS;
+    return hip_status(launch_embed(tokens, R, E, vocab, D, H, static_cast<hipStream_t>(stream)));
+}
+
+int specfold_lm_head(const specfold_shape* shape, const specfold_bf16* H, const specfold_bf16* ln_f,
+                     const specfold_bf16* w_lm, int32_t vocab, int32_t* token, float* logit, void* ws,
+                     size_t ws_bytes, void* stream) {
+    int e = check_head_shape(shape, vocab);
+    if (e) return e;
+    if ((e = dev(H)) || (e = dev(ln_f)) || (e = dev(w_lm)) || (e = dev(token)) || (e = dev(logit))) return e;
+    const HeadLayout L = head_layout(*shape, vocab);
+    if (!ws) return SPECFOLD_ERR_NULL;
+    if (ws_bytes < L.total) return SPECFOLD_ERR_WORKSPACE;
+    if ((e = dev(ws))) return e;
+    const int R = shape->n_branch * shape->block, D = shape->hidden;
+    if (overlaps(ws, ws_bytes, H, static_cast<size_t>(R) * D * 2) || overlaps(token, static_cast<size_t>(R) * 4, logit,
+                                                                              static_cast<size_t>(R) * 4))
+        return SPECFOLD_ERR_ALIAS;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint16_t* xn = at<uint16_t>(ws, L.xn);
+    float* val = at<float>(ws, L.val);
+    int32_t* idx = at<int32_t>(ws, L.idx);
+    hipError_t he = launch_rmsnorm_rows(H, R, D, ln_f, shape->rms_eps, xn, st);
+    if (he != hipSuccess) return hip_status(he);
+    const int cap = gemm_group_cols(L.cfg);
+    int gbase = 0;
+    for (int v0 = 0; v0 < vocab; v0 += L.piece) {
+        const int n = vocab - v0 < L.piece ? vocab - v0 : L.piece;
+        GemmCfg c = L.cfg;
+        c.groups = (n + cap - 1) / cap;
+        GemmArgs g{};
+        g.A = xn; g.lda = D; g.a_rows = nullptr; g.a_row_limit = R; g.m_count = nullptr; g.m_fixed = R;
+        g.m_cap = R; g.W = w_lm + static_cast<size_t>(v0) * D; g.K = D; g.Nout = n;
+        g.arg_val = val; g.arg_idx = idx; g.col_base = v0; g.group_base = gbase;
+        if ((he = launch_gemm(g, c, st)) != hipSuccess) return hip_status(he);
+        gbase += c.groups;
+    }
+    return hip_status(launch_argmax_merge(val, idx, L.groups, R, token, logit, st));
+}
 }  // extern "C"

@@ -267,6 +267,65 @@ __global__ __launch_bounds__(256) void row_norm_kernel(const uint16_t* __restric
 
 }  // namespace
 
+namespace {
+
+// RMSNorm of whole rows (the final norm before the LM head): one wave per row, every chunk of
+// the row requested before any is used, as in the gate.
+template <int CPL>
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const uint16_t* H, int R, int D, const uint16_t* ln,
+                                                           float eps, uint16_t* xn) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & (kWave - 1);
+    if (row >= R) return;
+    const int nch = D >> 3;
+    const __amdgpu_buffer_rsrc_t rH = make_rsrc(H, static_cast<uint32_t>(static_cast<size_t>(R) * D * 2));
+    const uint32_t base = static_cast<uint32_t>(row) * D * 2;
+    uint4 cv[CPL];
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+        const int k = lane + t * kWave;
+        cv[t] = buf_load16(rH, k < nch ? base + 16 * k : kOob);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+        float x[8];
+        unpack8(cv[t], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+    }
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / static_cast<float>(D) + eps);
+    uint4* o = reinterpret_cast<uint4*>(xn + static_cast<size_t>(row) * D);
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+        const int k = lane + t * kWave;
+        if (k < nch) {
+            float x[8];
+            unpack8(cv[t], x);
+            o[k] = norm_chunk(x, inv, ln, k);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm_rows(const uint16_t* H, int R, int D, const uint16_t* ln, float eps, uint16_t* xn,
+                               hipStream_t st) {
+    if (R <= 0) return hipSuccess;
+    const int cpl = ((D >> 3) + kWave - 1) / kWave;
+    if (cpl > kMaxChunksPerLane) return hipErrorInvalidValue;
+    const dim3 grid((R + 3) / 4), block(256);
+    switch (cpl) {
+#define SPECFOLD_NORM_CASE(C) \
+    case C: hipLaunchKernelGGL(rmsnorm_rows_kernel<C>, grid, block, 0, st, H, R, D, ln, eps, xn); break;
+        SPECFOLD_NORM_CASE(1) SPECFOLD_NORM_CASE(2) SPECFOLD_NORM_CASE(3) SPECFOLD_NORM_CASE(4)
+        SPECFOLD_NORM_CASE(5) SPECFOLD_NORM_CASE(6) SPECFOLD_NORM_CASE(7) SPECFOLD_NORM_CASE(8)
+        SPECFOLD_NORM_CASE(9) SPECFOLD_NORM_CASE(10)
+#undef SPECFOLD_NORM_CASE
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_gate(const GateParams& p, hipStream_t st) {
     const int R = p.nb * p.N;
     if (R <= 0) return hipSuccess;

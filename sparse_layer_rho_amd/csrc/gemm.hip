@@ -40,7 +40,7 @@ constexpr int kStageK = 64;                 // K elements per compute stage
 constexpr int kSplitUnit = 128;             // K-splits cut K at multiples of this
 constexpr int kRowB = 128;                  // bytes of one activation row in one compute stage
 
-enum { EPI_PARTIAL = 0, EPI_SWIGLU = 1 };
+enum { EPI_PARTIAL = 0, EPI_SWIGLU = 1, EPI_ARGMAX = 2 };
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -404,6 +404,31 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
                 *reinterpret_cast<uint2*>(p.act + static_cast<size_t>(m0 + m) * p.F + col) =
                     make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
             }
+        } else if constexpr (EPI == EPI_ARGMAX && WN == 1) {
+            // the wave holds every column of the group for its rows: the lane's best over its
+            // columns in ascending order (first maximum kept; NaN never taken), then the best of
+            // the 4 lanes sharing the row (ties to the lower column)
+            float best = 0.f;
+            int bi = -1;
+#pragma unroll
+            for (int j = 0; j < NTW; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int col = c0 + j * 16 + 4 * (lane >> 4) + q;
+                    const float v = acc[i][j][q];
+                    if (col < c1 && v == v && (bi < 0 || v > best)) { best = v; bi = col; }
+                }
+#pragma unroll
+            for (int off = 16; off <= 32; off <<= 1) {
+                const float ob = __shfl_xor(best, off, kWave);
+                const int oi = __shfl_xor(bi, off, kWave);
+                if (oi >= 0 && (bi < 0 || ob > best || (ob == best && oi < bi))) { best = ob; bi = oi; }
+            }
+            if ((lane >> 4) == 0) {
+                const size_t o = static_cast<size_t>(p.group_base + g) * p.m_cap + m0 + m;
+                p.arg_val[o] = bi < 0 ? __builtin_nanf("") : best;
+                p.arg_idx[o] = bi < 0 ? -1 : p.col_base + bi;
+            }
         } else {
             float* dst = p.partial + (static_cast<size_t>(y) * p.m_cap + m0 + m) * p.Nout + 4 * (lane >> 4);
 #pragma unroll
@@ -455,7 +480,9 @@ size_t gemm_lds_bytes(const GemmCfg& c) {
 hipError_t launch_gemm(const GemmArgs& a, const GemmCfg& c, hipStream_t st) {
 #define SPECFOLD_GEMM_CASE(NTW_, WN_, TM_, KS_, NBW_, NBA_)                                         \
     if (c.ntw == NTW_ && c.wn == WN_ && c.tm == TM_ && c.ksub == KS_ && c.nbw == NBW_ && c.nba == NBA_)  \
-        return c.swiglu ? launch_shape<NTW_, WN_, TM_, KS_, NBW_, NBA_, EPI_SWIGLU>(a, c, 1, st)           \
+        return c.argmax ? (WN_ == 1 ? launch_shape<NTW_, WN_, TM_, KS_, NBW_, NBA_, EPI_ARGMAX>(a, c, 1, st)  \
+                                    : hipErrorInvalidValue)                                            \
+             : c.swiglu ? launch_shape<NTW_, WN_, TM_, KS_, NBW_, NBA_, EPI_SWIGLU>(a, c, 1, st)          \
                         : launch_shape<NTW_, WN_, TM_, KS_, NBW_, NBA_, EPI_PARTIAL>(a, c, c.splits, st);
     SPECFOLD_GEMM_CASES(SPECFOLD_GEMM_CASE)
 #undef SPECFOLD_GEMM_CASE

@@ -80,6 +80,10 @@ struct GemmArgs {
     int32_t* fc_src_slot;
     int32_t* fc_count_copy;      // nullable extra copies (per-call statistics)
     int32_t* fc_src_slot_copy;
+    // greedy-token epilogue: per (column group, row) the best output and its column
+    float* arg_val;              // [group_base + n_groups][m_cap]
+    int32_t* arg_idx;            // column + col_base, or -1 when the group has no candidate
+    int col_base, group_base;
 };
 
 // Tile shape of one launch: a workgroup covers the output columns of one of `groups` even
@@ -92,6 +96,7 @@ struct GemmCfg {
     int ntw, wn, tm, ksub, nbw, nba, groups, splits;
     bool swiglu;
     int min_chunks;          // row workgroups per column group used at least (when there are that many)
+    bool argmax;             // greedy-token epilogue (wn must be 1, no K split)
 };
 // the (ntw, wn, tm, ksub, nbw, nba) shapes compiled
 #define SPECFOLD_GEMM_CASES(X) \
@@ -139,6 +144,12 @@ struct AttnArgs {
     float scale_log2;        // log2(e) / sqrt(hd)
 };
 hipError_t launch_attn_prefix(const AttnArgs& a, hipStream_t st);
+// rows kernels either side of the stack
+hipError_t launch_rmsnorm_rows(const uint16_t* H, int R, int D, const uint16_t* ln, float eps, uint16_t* xn,
+                               hipStream_t st);
+hipError_t launch_embed(const int32_t* tokens, int R, const uint16_t* E, int V, int D, uint16_t* H, hipStream_t st);
+hipError_t launch_argmax_merge(const float* arg_val, const int32_t* arg_idx, int groups, int R, int32_t* token,
+                               float* logit, hipStream_t st);
 hipError_t launch_attn_block(const AttnArgs& a, hipStream_t st);
 
 }  // namespace specfold

@@ -34,7 +34,7 @@ EXPORTS = (
     "specfold_stage_name", "specfold_event_create", "specfold_event_destroy",
     "specfold_event_elapsed_ms", "specfold_gate", "specfold_compact", "specfold_resolve_sources",
     "specfold_sparse_qkv", "specfold_folded_attention", "specfold_out_proj", "specfold_sparse_ffn",
-    "specfold_verify_layer",
+    "specfold_verify_layer", "specfold_embed", "specfold_head_workspace_bytes", "specfold_lm_head",
 )
 
 
@@ -97,6 +97,9 @@ def _load():
                                       ctypes.c_int),
         "specfold_out_proj": ([pS, P, P, P, P, P, SZ, P], ctypes.c_int),
         "specfold_sparse_ffn": ([pS, P, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
+        "specfold_embed": ([pS, P, P, ctypes.c_int32, P, P], ctypes.c_int),
+        "specfold_head_workspace_bytes": ([pS, ctypes.c_int32], SZ),
+        "specfold_lm_head": ([pS, P, P, P, ctypes.c_int32, P, P, P, SZ, P], ctypes.c_int),
         "specfold_verify_layer": ([pS, P, ctypes.POINTER(LayerWeights), ctypes.POINTER(PrefixKV), P, F32, P,
                                    ctypes.POINTER(LayerStats), ctypes.POINTER(Trace), P, SZ, P], ctypes.c_int),
     }
@@ -294,6 +297,37 @@ def verify_layer(shape, parent, weights, prefix_k, prefix_v, H_in, delta, H_out,
         st_ptr, ctypes.byref(trace) if trace is not None else None,
         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream())
     _check(status, "specfold_verify_layer")
+
+
+# ------------------------------------------------------------------ either side of the stack
+
+def embed(shape, tokens, E, H):
+    """H[r] = E[tokens[r]] (NaN rows for ids outside [0, V)); tokens int32 [R], E bf16 [V, D]."""
+    sh = make_shape(shape)
+    R, D = shape.n_branch * shape.block, shape.hidden
+    V = E.shape[0]
+    st = _lib.specfold_embed(ctypes.byref(sh), _ptr(tokens, torch.int32, R, "tokens"),
+                             _ptr(E, torch.bfloat16, V * D, "E"), V, _ptr(H, torch.bfloat16, R * D, "H"), _stream())
+    _check(st, "specfold_embed")
+
+
+def head_workspace(shape, vocab, device="cuda") -> torch.Tensor:
+    n = int(_lib.specfold_head_workspace_bytes(ctypes.byref(make_shape(shape)), int(vocab)))
+    if n == 0:
+        raise ValueError("shape or vocabulary not supported by the library")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def lm_head(shape, H, ln_f, w_lm, token, logit, ws):
+    """Final RMSNorm, LM head and greedy token of every row: token int32 [R], logit f32 [R]."""
+    sh = make_shape(shape)
+    R, D = shape.n_branch * shape.block, shape.hidden
+    V = w_lm.shape[0]
+    st = _lib.specfold_lm_head(ctypes.byref(sh), _ptr(H, torch.bfloat16, R * D, "H"),
+                               _ptr(ln_f, torch.bfloat16, D, "ln_f"), _ptr(w_lm, torch.bfloat16, V * D, "w_lm"), V,
+                               _ptr(token, torch.int32, R, "token"), _ptr(logit, torch.float32, R, "logit"),
+                               _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream())
+    _check(st, "specfold_lm_head")
 
 
 # ------------------------------------------------------------------ per-launch timing

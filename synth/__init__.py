@@ -21,5 +21,6 @@ from .inputs import (  # noqa: F401
     parent_tree,
     prefix_kv,
     step_inputs,
+    step_tokens,
     tree_of,
 )

@@ -24,6 +24,7 @@ import numpy as np
 # tensor ids inside a seed tuple
 _T_LN1, _T_WQKV, _T_WO, _T_LN2, _T_WGU, _T_WDOWN, _T_PK, _T_PV = range(8)
 _T_TREE, _T_MAIN, _T_CHILD = 10, 11, 12
+_T_TOKENS = 13
 
 # Log-normal law of a draft row's relative distance r (non-unmasked rows) chosen so
 # that, with E[#unmasked]/N = 2.5/32, P(r <= 0.1) = 0.72 and P(r <= 0.3) = 0.88 over
@@ -208,6 +209,23 @@ def parent_tree(n_branch: int, base_seed: int, step: int, kind: str = "random",
         par[i] = p
         depth[i] = depth[p] + 1
     return par
+
+
+def step_tokens(shape: Shape, vocab: int, base_seed: int, step: int, parent) -> np.ndarray:
+    """Token ids [B+1, N] of one verification step: main's block is uniform over the
+    vocabulary; each draft copies its parent's block and newly unmasks 1-4 positions with
+    fresh uniform tokens (the drafts' structure of the hidden-state generator, at token level)."""
+    parent = np.asarray(parent, dtype=np.int64)
+    B1, N = shape.n_branch, shape.block
+    rng = _rng(base_seed, step, 0, _T_TOKENS)
+    tok = np.empty((B1, N), dtype=np.int32)
+    tok[0] = rng.integers(0, vocab, N)
+    for i in range(1, B1):
+        tok[i] = tok[parent[i]]
+        u = int(rng.integers(1, 5))
+        pos = rng.choice(N, size=min(u, N), replace=False)
+        tok[i, pos] = rng.integers(0, vocab, pos.size)
+    return tok
 
 
 def main_hidden(shape: Shape, base_seed: int, step: int) -> np.ndarray:

@@ -131,3 +131,28 @@ def test_verify_layer_validation():
     assert call(w=sf.LayerWeights(FAKE, None, FAKE, FAKE, FAKE, FAKE)) == -1
     assert call(pf=sf.PrefixKV(FAKE * 8, FAKE * 9, 33, 16, 32, 16)) == -4
     assert call(sh=_shape(block=80)) == -6
+
+
+def test_head_entry_points_validation():
+    sh = _shape()
+    V = 1000
+    need = L.specfold_head_workspace_bytes(ctypes.byref(sh), V)
+    R, D = sh.n_branch * sh.block, sh.hidden
+    groups = (V + 63) // 64
+    assert need >= R * D * 2 + 2 * groups * R * 4
+    assert L.specfold_head_workspace_bytes(ctypes.byref(sh), 0) == 0
+    assert L.specfold_head_workspace_bytes(ctypes.byref(_shape(hidden=96)), V) == 0
+    ws = 0x40000000
+    # (H, ln_f, w_lm, vocab, token, logit, ws, ws_bytes)
+    assert L.specfold_lm_head(ctypes.byref(sh), None, FAKE * 2, FAKE * 3, V, FAKE * 4, FAKE * 5, ws, need, None) == -1
+    assert L.specfold_lm_head(ctypes.byref(sh), MISALIGNED, FAKE * 2, FAKE * 3, V, FAKE * 4, FAKE * 5, ws, need,
+                              None) == -4
+    assert L.specfold_lm_head(ctypes.byref(sh), FAKE, FAKE * 2, FAKE * 3, V, FAKE * 4, FAKE * 5, ws, need - 1,
+                              None) == -5
+    assert L.specfold_lm_head(ctypes.byref(sh), FAKE, FAKE * 2, FAKE * 3, 0, FAKE * 4, FAKE * 5, ws, need, None) == -2
+    # token and logit overlap
+    assert L.specfold_lm_head(ctypes.byref(sh), FAKE, FAKE * 2, FAKE * 3, V, FAKE * 4, FAKE * 4, ws, need, None) == -7
+    # embedding: NULL table, bad vocabulary, output overlapping the table
+    assert L.specfold_embed(ctypes.byref(sh), FAKE, None, V, FAKE * 2, None) == -1
+    assert L.specfold_embed(ctypes.byref(sh), FAKE, FAKE * 2, 0, FAKE * 3, None) == -2
+    assert L.specfold_embed(ctypes.byref(sh), FAKE, FAKE * 2, V, FAKE * 2, None) == -7
