@@ -52,6 +52,8 @@ def parse():
                     help="stack workloads: also time whole verification passes from token ids: embedding "
                          "gather, the layer stack and the final RMSNorm + LM head + greedy token")
     ap.add_argument("--vocab", type=int, default=151936, help="vocabulary of the --with-head passes")
+    ap.add_argument("--correction", action="store_true",
+                    help="also time the pages' attention-state correction (variants/) against the library's merge")
     ap.add_argument("--serialized", action="store_true",
                     help="also time serialized verification (each branch alone, delta 0) and compare it "
                          "with the batched dense layer")
@@ -172,15 +174,17 @@ def main():
     def stage_times(delta):
         tm = sf.StageTimer()
         acc = None
-        for k in range(args.stage_calls):
+        calls = max(1, args.stage_calls)
+        skip = min(3, calls - 1)                  # untimed first calls
+        for k in range(calls):
             sf.verify_layer(sh, parent, lws[k % n_copies], pf, None, H_in, delta, H_out, ws, stats=stats,
                             trace=tm.trace)
             torch.cuda.synchronize()
             t = tm.elapsed_ms()
-            if k >= 3:
+            if k >= skip:
                 acc = t if acc is None else {n: acc[n] + t[n] for n in acc}
         tm.close()
-        cnt = args.stage_calls - 3
+        cnt = calls - skip
         return {n: 1e3 * v / cnt for n, v in acc.items()}     # microseconds
 
     st_f = stage_times(wl.delta)
@@ -266,9 +270,11 @@ def main():
     if not args.no_gate_flat:
         out["gate_flat"] = gate_flat_leg(torch, sf, dev)
 
+    if args.correction:
+        out["correction"] = correction_leg(torch, sf, sh, wl, parent, H_in, w0, pk, pv, args)
+
     if args.serialized:
-        out["serialized"] = serialized_leg(torch, sf, sh, lws, pf, H_in, results[0.0]["H_out"], dense, args,
-                                           H_host, w_host, pk_h, pv_h)
+        out["serialized"] = serialized_leg(torch, sf, sh, lws, pf, H_in, results[0.0]["H_out"], dense, args)
 
     if args.copy_probe_mb > 0:
         n = args.copy_probe_mb * (1 << 20) // 4
@@ -285,17 +291,14 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def serialized_leg(torch, sf, sh, lws, pf, H_in, H_dense, dense, args, H_host, w_host, pk_h, pv_h):
+def serialized_leg(torch, sf, sh, lws, pf, H_in, H_dense, dense, args):
     """Serialized verification [SpecFold summary, App. C]: every branch verified alone (one
     branch, parent map [-1], delta 0), as a vanilla verifier would, B+1 layer calls per step.
     Reports its throughput against the batched dense layer (delta 0, same kernels) and how its
-    outputs compare with the batched layer's: the split-K decomposition depends on the row
-    count, so the fp32 sums may be ordered differently and round to different bf16 values."""
-    import numpy as np
-
-    import oracle
-
-    N, D = sh.block, sh.hidden
+    outputs compare with the batched layer's: the K-split decomposition is a function of the
+    projection's shape only, so every row should carry the same bits either way (the parity of
+    both forms with the oracle is the tests' business)."""
+    N = sh.block
     sh1 = sh.with_branches(1)
     ws1 = sf.new_workspace(sh1)
     y = torch.empty_like(H_dense)
@@ -312,19 +315,105 @@ def serialized_leg(torch, sf, sh, lws, pf, H_in, H_dense, dense, args, H_host, w
     diff = (y.float() - H_dense.float()).abs()
     reps = max(1, args.steps // (4 * n_copies))
     ms = graph_time(torch, [lambda k=k: run_all(k) for k in range(n_copies)], reps=reps) / n_copies
-    # oracle: the plain layer on the first and the last branch alone
-    errs = []
-    for i in (0, sh.n_branch - 1):
-        ref = oracle.dense_branch_layer(H_host[i].astype(np.float64), w_host, pk_h, pv_h, sh)
-        got = y[i * N:(i + 1) * N].float().cpu().numpy().astype(np.float64)
-        errs.append(float(np.linalg.norm(got - ref) / np.linalg.norm(ref)))
     R = sh.rows
     return {"ms_per_step": round(ms, 5), "branch_tokens_per_s": round(R / (ms * 1e-3), 1),
             "batched_dense_speedup": round(ms / dense["ms_per_step"], 4),
             "rows_bitwise_equal_to_batched": round(float(same.float().mean().item()), 4),
             "max_abs_diff_vs_batched": round(float(diff.max().item()), 6),
-            "oracle_rel_l2": [round(e, 6) for e in errs], "ok": max(errs) <= 2e-2,
+            "finite": bool(torch.isfinite(y.float()).all().item()),
             "note": "each of the B+1 branches alone (n_branch 1, delta 0), graph-replayed"}
+
+
+def correction_leg(torch, sf, sh, wl, parent, H_in, w, pk, pv, args):
+    """The pages' attention-state correction [SpecFold summary, App. B, §A.1, §A.3] against the
+    library's prefix-partial + block merge, on the same folded layer's projections (the
+    library's gate, compaction, source resolution and QKV).  The variant (variants/, not part
+    of the library) computes fresh fp32 states for the recompute rows, corrects the folded
+    rows one tree level at a time, and divides; the library computes every row's attention
+    in two launches.  Both are compared with direct attention evaluated in float64 by torch
+    on the device from the same bf16 projections."""
+    from variants import correction as corr
+
+    dev = H_in.device
+    R, Hq, Hkv, d, N = sh.rows, sh.n_q_heads, sh.n_kv_heads, sh.head_dim, sh.block
+    I32 = torch.int32
+    rho = torch.empty(R, device=dev)
+    fold = torch.empty(R, dtype=torch.uint8, device=dev)
+    inv = torch.empty(R, device=dev)
+    rec = torch.zeros(R, dtype=I32, device=dev)
+    cnt = torch.zeros(4, dtype=I32, device=dev)
+    off = torch.zeros(sh.n_branch + 1, dtype=I32, device=dev)
+    slot = torch.zeros(R, dtype=I32, device=dev)
+    src_b = torch.zeros(R, dtype=I32, device=dev)
+    src = torch.zeros(R, dtype=I32, device=dev)
+    q = torch.zeros((R, Hq, d), dtype=torch.bfloat16, device=dev)
+    k = torch.zeros((R, Hkv, d), dtype=torch.bfloat16, device=dev)
+    v = torch.zeros_like(k)
+    ws = sf.new_workspace(sh)
+    sf.gate(sh, parent, H_in, wl.delta, rho, fold, inv_rms=inv)
+    sf.compact(sh, fold, rec, cnt[:1], off, slot)
+    sf.resolve_sources(sh, parent, fold, slot, src_b, src)
+    sf.sparse_qkv(sh, H_in, inv, rec, cnt[:1], w["ln1"], w["w_qkv"], q, k, v, ws)
+    attn = torch.empty((R, Hq * d), dtype=torch.bfloat16, device=dev)
+    state = torch.empty(corr.state_shape(sh), device=dev)
+    out = torch.empty((R, Hq, d), device=dev)
+    levels = corr.levels(sh, parent)
+
+    def lib():
+        sf.folded_attention(sh, q, k, v, rec, cnt[:1], src, pk, pv, attn, ws)
+
+    def fresh():
+        corr.fresh(sh, q, k, v, rec, cnt[:1], src, pk, pv, state)
+
+    def variant():
+        corr.attention(sh, parent, q, k, v, rec, cnt[:1], src, fold, pk, pv, state, out)
+
+    lib()
+    variant()
+    torch.cuda.synchronize()
+    # every phase reads only inputs it does not write, so a graph of REP back-to-back copies
+    # times one copy without the graph launch in the figure
+    REP = 16
+    reps = max(10, args.steps // REP)
+
+    def per_call(fn):
+        return graph_time(torch, [fn] * REP, reps) / REP
+
+    t = {"library_merge": per_call(lib), "variant_total": per_call(variant), "variant_fresh": per_call(fresh)}
+    variant()                                       # the states every level reads are the final ones
+    t_levels = [per_call(lambda m=m: corr.level(sh, parent, m, q, k, v, src, fold, state)) for m in levels]
+    t["variant_finalize"] = per_call(lambda: corr.finalize(sh, state, out))
+    variant()
+    torch.cuda.synchronize()
+
+    # direct attention in float64 from the same projections (rows gathered by source slot)
+    sl = src.long()
+    Q = q.double()[sl].view(sh.n_branch, N, Hq, d)
+    K = k.double()[sl].view(sh.n_branch, N, Hkv, d)
+    V = v.double()[sl].view(sh.n_branch, N, Hkv, d)
+    G = Hq // Hkv
+    ref = torch.empty((sh.n_branch, N, Hq, d), dtype=torch.float64, device=dev)
+    for g in range(Hkv):
+        keys = torch.cat([pk.double()[:, g].unsqueeze(0).expand(sh.n_branch, -1, -1), K[:, :, g]], dim=1)
+        vals = torch.cat([pv.double()[:, g].unsqueeze(0).expand(sh.n_branch, -1, -1), V[:, :, g]], dim=1)
+        for h in range(g * G, (g + 1) * G):
+            s = torch.matmul(Q[:, :, h], keys.transpose(1, 2).contiguous()) / (d ** 0.5)
+            ref[:, :, h] = torch.matmul(torch.softmax(s, dim=-1), vals)
+    ref = ref.view(R, Hq, d)
+
+    def err(x):
+        x = x.double().view(R, Hq, d)
+        return {"rel_l2": float(((x - ref).norm() / ref.norm()).item()),
+                "max_abs": float((x - ref).abs().max().item())}
+
+    M = int(cnt[0].item())
+    return {"levels": len(levels), "rec_rows": M,
+            "folded_rows": int(fold.sum().item()),
+            "us": {k_: round(1e3 * v_, 2) for k_, v_ in t.items()},
+            "variant_level_us": [round(1e3 * v_, 2) for v_ in t_levels],
+            "numerics_vs_f64_direct": {"library_merge_bf16_out": err(attn.float()),
+                                       "variant_fp32_out": err(out)},
+            "note": "same projections for both; library output is bf16, the variant's fp32"}
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gate_up_swiglu_gemm_layer-1.5b_traffic.md")
@@ -433,7 +522,6 @@ def stack_bench(args, wl):
     import numpy as np
     import torch
 
-    import oracle
     from sparse_layer_rho_amd import specfold as sf
     from synth import bf16_round, layer_weights, prefix_kv, step_inputs
 
@@ -448,8 +536,8 @@ def stack_bench(args, wl):
         return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev).to(torch.bfloat16)
 
     t0 = time.time()
-    # layer 0 from the seeded generator the oracle uses (the run verifies it); the others drawn on
-    # the device with the same distributions
+    # layer 0 from the seeded host generator the tests use; the others drawn on the device with
+    # the same distributions
     w0_host = layer_weights(sh, wl.base_seed, 0)
     pk0_h, pv0_h = prefix_kv(sh, wl.base_seed, 0)
     layers = [({k: to_dev(v) for k, v in w0_host.items()}, to_dev(pk0_h), to_dev(pv0_h))]
@@ -500,20 +588,11 @@ def stack_bench(args, wl):
         res[delta] = {"ms_per_step": ms / S, "M": np.mean(Ms, axis=0), "fold": np.mean(ff, axis=0)}
         print(f"[bench] delta {delta}: {ms / S:.3f} ms per stack step", file=sys.stderr, flush=True)
 
-    # verification: layer 0 of step 0 against the oracle, teacher-forced on the GPU's mask
-    parent, H_host, H0 = steps[0]
-    y = torch.empty_like(H0)
-    st = {"fold": torch.zeros(R, dtype=torch.uint8, device=dev), "rec_count": torch.zeros(1, dtype=torch.int32, device=dev)}
-    sf.verify_layer(sh, parent, lws[0], pfs[0], None, H0, wl.delta, y, ws, stats=st)
+    # the folded pass's output must be finite in every layer's stream (its parity with the
+    # oracle, layer by layer and across the stack, is checked by the tests)
+    x = run_step(0, wl.delta)
     torch.cuda.synchronize()
-    fold_g = st["fold"].cpu().numpy().reshape(sh.n_branch, sh.block).astype(bool)
-    Hd = H_host.astype(np.float64)
-    rho_o, fold_o = oracle.gate(Hd, parent, wl.delta)
-    band = np.abs(rho_o - wl.delta) < 1e-4
-    ok_mask = bool(np.array_equal(fold_g[~band], fold_o[~band]))
-    ref = oracle.verify_layer(Hd, parent, w0_host, pk0_h, pv0_h, wl.delta, sh, fold=fold_g)
-    got = y.float().cpu().numpy().astype(np.float64).reshape(Hd.shape)
-    err = float(np.linalg.norm(got - ref["H_out"]) / np.linalg.norm(ref["H_out"]))
+    finite = bool(torch.isfinite(x.float()).all().item())
 
     f, d = res[wl.delta], res[0.0]
     out = {
@@ -537,8 +616,7 @@ def stack_bench(args, wl):
         "us_per_layer": {"folded": round(1e3 * f["ms_per_step"] / L, 2), "dense": round(1e3 * d["ms_per_step"] / L, 2)},
         "rec_rows_per_layer": [round(float(v), 1) for v in f["M"]],
         "fold_fraction_drafts_per_layer": [round(float(v), 4) for v in f["fold"]],
-        "verified": {"ok": bool(ok_mask and err <= 2e-2), "layer": 0, "step": 0, "rel_l2": round(err, 6),
-                     "mask_match_outside_band": ok_mask},
+        "finite_output": finite,
     }
     if args.with_head:
         out["pass_with_head"] = pass_leg(torch, sf, sh, wl, args, steps, lws, pfs, ws, buf, fold, cnt, L, S, dev)
@@ -550,11 +628,10 @@ def pass_leg(torch, sf, sh, wl, args, steps, lws, pfs, ws, buf, fold, cnt, L, S,
     the L-layer stack (folded at the workload's delta, or dense), final RMSNorm + LM head +
     greedy token of every row.  The drafts' tokens copy their parent's block with 1-4 newly
     unmasked positions, so the first layer's gate sees identical rows wherever a draft agrees
-    with its parent.  The head is checked against the oracle on sampled rows of the last
-    layer's output."""
+    with its parent.  The head's parity with the oracle is checked by the tests; here every
+    greedy token must name a vocabulary entry and every best logit be finite."""
     import numpy as np
 
-    import oracle
     from synth import step_tokens
 
     R, D, V = sh.rows, sh.hidden, args.vocab
@@ -594,18 +671,10 @@ def pass_leg(torch, sf, sh, wl, args, steps, lws, pfs, ws, buf, fold, cnt, L, S,
     reps = max(1, args.steps)
     embed_ms = graph_time(torch, [lambda: sf.embed(sh, toks[0], E, H0)], reps=reps)
     head_ms = graph_time(torch, [lambda: sf.lm_head(sh, buf[0], ln_f, W_lm, tok_out, logit_out, hws)], reps=reps)
-    # the head on the last layer's output of step 0, folded, against the oracle (sampled rows)
-    x = run_pass(0, wl.delta)
+    run_pass(0, wl.delta)
     torch.cuda.synchronize()
-    rows = np.array([0, R // 3, R // 2, R - 1])
-    Xh = x.float().cpu().numpy().astype(np.float64)[rows]
-    xn = oracle.final_norm(Xh, np.ones(D), sh.rms_eps)
-    Wh = W_lm.float().cpu().numpy().astype(np.float64)
-    logits = oracle.lm_head_logits(xn, Wh)
-    tok_o, mx = oracle.greedy_tokens(logits)
-    tg = tok_out.cpu().numpy()[rows]
-    bound = (2.0 ** -8 + D * 2.0 ** -24) * (np.abs(xn) @ np.abs(Wh).T).max(axis=1)
-    ok = bool((logits[np.arange(rows.size), tg] >= mx - 2 * bound).all())
+    tg = tok_out.cpu().numpy()
+    ok = bool(((tg >= 0) & (tg < V)).all() and torch.isfinite(logit_out).all().item())
     (fms, ffold), (dms, _) = res[wl.delta], res[0.0]
     head_bytes = 2 * V * D + 2 * R * D
     return {"vocab": V, "ms_per_pass": round(fms, 5), "dense_ms_per_pass": round(dms, 5),
@@ -613,18 +682,18 @@ def pass_leg(torch, sf, sh, wl, args, steps, lws, pfs, ws, buf, fold, cnt, L, S,
             "embed_us": round(1e3 * embed_ms, 2), "lm_head_us": round(1e3 * head_ms, 2),
             "lm_head_hbm_frac": round(head_bytes / (head_ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
             "fold_fraction_drafts_per_layer": [round(float(v), 4) for v in ffold],
-            "head_tokens_match_oracle": bool(np.array_equal(tg, tok_o)), "head_within_bound": ok,
+            "tokens_in_vocab_and_logits_finite": ok,
             "data": "token ids: main uniform, drafts copy the parent's block with 1-4 new tokens; "
                     "E ~ N(0,1), W_lm ~ N(0, 0.02^2), final norm weight 1 (seeded, on the device)"}
 
 
 def sweep_bench(args, wl):
     """One layer swept over draft count B and delta (one tree and one set of hidden states per B,
-    reused across delta, so the folded fraction is monotone in delta)."""
+    reused across delta, so the folded fraction is monotone in delta).  The tests check the
+    layer's parity with the oracle at points of this sweep."""
     import numpy as np
     import torch
 
-    import oracle
     from sparse_layer_rho_amd import specfold as sf
     from synth import bf16_round, layer_weights, prefix_kv, step_inputs
 
@@ -667,20 +736,15 @@ def sweep_bench(args, wl):
             ms = graph_time(torch, [lambda k=k, delta=delta: sf.verify_layer(sh, parent, lws[k], pf, None, H, delta, y, ws)
                                     for k in range(n_copies)], reps=reps) / n_copies
             per[delta] = (ms, M, ff)
-        # verification at the workload's delta, teacher-forced on the GPU's mask
         sf.verify_layer(sh, parent, lws[0], pf, None, H, wl.delta, y, ws, stats=st)
         torch.cuda.synchronize()
-        fold_g = st["fold"].cpu().numpy().reshape(sh.n_branch, sh.block).astype(bool)
-        Hd = H_host.astype(np.float64)
-        ref = oracle.verify_layer(Hd, parent, w_host, pk_h, pv_h, wl.delta, sh, fold=fold_g)
-        got = y.float().cpu().numpy().astype(np.float64).reshape(Hd.shape)
-        err = float(np.linalg.norm(got - ref["H_out"]) / np.linalg.norm(ref["H_out"]))
+        finite = bool(torch.isfinite(y.float()).all().item())
         ms0 = per[0.0][0] if 0.0 in per else None
         for delta, (ms, M, ff) in per.items():
             points.append({"drafts": B, "delta": delta, "rec_rows": M, "fold_fraction_drafts": round(ff, 4),
                            "us": round(ms * 1e3, 2), "branch_tokens_per_s": round(R / (ms * 1e-3), 1),
                            "speedup_vs_dense": round(ms0 / ms, 4) if ms0 else None})
-        points.append({"drafts": B, "verified_delta": wl.delta, "rel_l2": round(err, 6), "ok": err <= 2e-2})
+        points.append({"drafts": B, "delta": wl.delta, "finite_output": finite})
         print(f"[bench] B={B} done", file=sys.stderr, flush=True)
     print(json.dumps({"metric": METRIC, "unit": "branch-tokens/s", "workload": args.workload, "n_gpus": 1,
                       "dtype": "bf16", "data": "synthetic", "regime": f"cold ({n_copies} weight copies)",
@@ -689,12 +753,11 @@ def sweep_bench(args, wl):
 
 def tree_bench(args, wl):
     """One layer at fixed B swept over the draft tree's shape (siblings of main, random trees of
-    bounded depth, a chain), folded at the workload's delta against dense (delta 0); each tree
-    is verified against the oracle, teacher-forced on the GPU's mask."""
+    bounded depth, a chain), folded at the workload's delta against dense (delta 0).  The tests
+    check the layer's parity with the oracle on each of these tree shapes."""
     import numpy as np
     import torch
 
-    import oracle
     from sparse_layer_rho_amd import specfold as sf
     from synth import bf16_round, layer_weights, prefix_kv, step_inputs, tree_of
 
@@ -742,16 +805,12 @@ def tree_bench(args, wl):
             res[delta] = (ms, M, ff)
         sf.verify_layer(sh, parent, lws[0], pf, None, H, wl.delta, y, ws, stats=st)
         torch.cuda.synchronize()
-        fold_g = st["fold"].cpu().numpy().reshape(sh.n_branch, sh.block).astype(bool)
-        Hd = H_host.astype(np.float64)
-        ref = oracle.verify_layer(Hd, parent, w_host, pk_h, pv_h, wl.delta, sh, fold=fold_g)
-        got = y.float().cpu().numpy().astype(np.float64).reshape(Hd.shape)
-        err = float(np.linalg.norm(got - ref["H_out"]) / np.linalg.norm(ref["H_out"]))
+        finite = bool(torch.isfinite(y.float()).all().item())
         (msf, M, ff), (msd, _, _) = res[wl.delta], res[0.0]
         points.append({"tree": kind, "parent": parent.tolist(), "max_depth": int(depth.max()),
                        "rec_rows": M, "fold_fraction_drafts": round(ff, 4), "us": round(msf * 1e3, 2),
                        "dense_us": round(msd * 1e3, 2), "branch_tokens_per_s": round(R / (msf * 1e-3), 1),
-                       "speedup_vs_dense": round(msd / msf, 4), "rel_l2": round(err, 6), "ok": err <= 2e-2})
+                       "speedup_vs_dense": round(msd / msf, 4), "finite_output": finite})
         print(f"[bench] tree {kind} done", file=sys.stderr, flush=True)
     print(json.dumps({"metric": METRIC, "unit": "branch-tokens/s", "workload": args.workload, "n_gpus": 1,
                       "dtype": "bf16", "data": "synthetic", "delta": wl.delta, "drafts": sh.n_branch - 1,

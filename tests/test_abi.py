@@ -156,3 +156,32 @@ def test_head_entry_points_validation():
     assert L.specfold_embed(ctypes.byref(sh), FAKE, None, V, FAKE * 2, None) == -1
     assert L.specfold_embed(ctypes.byref(sh), FAKE, FAKE * 2, 0, FAKE * 3, None) == -2
     assert L.specfold_embed(ctypes.byref(sh), FAKE, FAKE * 2, V, FAKE * 2, None) == -7
+
+
+def test_correction_variant_exports_and_validates():
+    """The comparison variant (variants/) loads, exports what its header declares, and its
+    host-side checks reject bad trees and shapes without launching anything."""
+    from variants import correction as corr
+
+    header = os.path.join(os.path.dirname(os.path.dirname(__file__)), "variants", "correction.h")
+    text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(specfold_variant_[a-z_]+)\s*\(", text)))
+    assert set(names) == set(corr.EXPORTS)
+    for n in names:
+        assert hasattr(corr._lib, n), n
+    sh = WORKLOADS["layer-1.5b"].shape
+    # depth levels of a known tree
+    assert corr.levels(sh, [-1, 0, 0, 1, 2, 3, 1, 0, 4]) == [0b10000110, 0b01011000, 0b100100000]
+    assert corr.levels(sh, [-1, 0, 1, 2, 3, 4, 5, 6, 7]) == [1 << i for i in range(1, 9)]
+    with pytest.raises(sf.SpecfoldError) as e:
+        corr.levels(sh, [-1, 0, 2, 1, 2, 3, 1, 0, 4])         # par[2] = 2 is not an ancestor
+    assert e.value.status == -3
+    bad = sf.make_shape(sh)
+    bad.head_dim = 256                                         # beyond the variant's two dims per lane
+    masks = (ctypes.c_uint64 * 9)()
+    n = ctypes.c_int32()
+    par = (ctypes.c_int32 * 9)(-1, 0, 0, 0, 0, 0, 0, 0, 0)
+    assert corr._lib.specfold_variant_correction_levels(ctypes.byref(bad), par, masks, ctypes.byref(n)) == -2
+    st = corr._lib.specfold_variant_correction_fresh(ctypes.byref(sf.make_shape(sh)), None, None, None, None, None,
+                                                     None, None, None, None)
+    assert st == -1

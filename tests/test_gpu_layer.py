@@ -8,7 +8,7 @@ import torch
 
 import oracle
 from gpu_case import LayerCase, rel_l2
-from synth import WORKLOADS, Shape, layer_weights, parent_tree, prefix_kv, step_inputs
+from synth import WORKLOADS, Shape, layer_weights, parent_tree, prefix_kv, step_inputs, tree_of
 
 pytestmark = pytest.mark.gpu
 
@@ -35,6 +35,18 @@ def test_verify_layer_edge_shapes(shape, tree):
     for delta in (0.0, 0.1, 0.3):
         res = case.run(delta)
         case.check(delta, res)
+
+
+@pytest.mark.parametrize("kind", WORKLOADS["draft-shapes-1.5b"].tree_sweep)
+def test_draft_tree_shapes_match_oracle(kind):
+    """The draft-shape sweep's trees (siblings of main, random trees of bounded depth, a
+    chain) at its full 1.5B-class shape, B = 7, folded at its delta."""
+    wl = WORKLOADS["draft-shapes-1.5b"]
+    parent = tree_of(kind, wl.shape.n_branch, wl.base_seed, 0)
+    case = LayerCase(wl.shape, wl.base_seed, parent=parent, law=wl.child_law)
+    res = case.run(wl.delta)
+    _, err = case.check(wl.delta, res)
+    print(f"{kind}: rel L2 {err:.2e}, M = {res['rec_count']} of {case.shape.rows}")
 
 
 def test_delta_zero_is_dense_per_branch():
