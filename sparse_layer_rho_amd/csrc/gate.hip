@@ -164,65 +164,159 @@ __global__ __launch_bounds__(1024) void compact_kernel(const CompactParams p) {
 
 // Large inputs: tiles of kCompactTile rows.  Pass 1 counts each tile's recompute rows into the
 // first row_slot entry of the tile (scratch that pass 3 overwrites), pass 2 turns the counts
-// into exclusive offsets, pass 3 scans every tile from its offset.
-constexpr int kCompactTile = 8192;
+// into exclusive offsets, pass 3 scans every tile from its offset.  A tile is 32768 rows, so a
+// 2^24-row input is 512 tiles: one workgroup per tile stays resident on the CUs at once.
+constexpr int kCompactTile = 32768;
+constexpr int kScatterSub = 8192;               // rows of one scan step of pass 3 (8 per thread)
+constexpr int kSmallCompact = 8192;             // up to this many rows one workgroup scans them all
 
-__global__ __launch_bounds__(256) void compact_count_kernel(const CompactParams p) {
-    __shared__ int s_tot[4];
+__global__ __launch_bounds__(1024) void compact_count_kernel(const CompactParams p) {
+    __shared__ int s_tot[16];
     const int tile = blockIdx.x, tid = threadIdx.x;
     const int r0 = tile * kCompactTile;
-    // thread t counts rows r0 + 32t .. +32: two 16-byte loads, or byte loads where the array ends
-    // inside them (the flags are bytes; nothing past R is read)
-    const int rt = r0 + 32 * tid;
+    // thread t counts the kRowsPerThread rows from r0 + kRowsPerThread t: 16-byte loads, or byte
+    // loads where the array ends inside them (the flags are bytes; nothing past R is read)
+    constexpr int kRowsPerThread = kCompactTile / 1024;
+    static_assert(kRowsPerThread % 16 == 0, "whole 16-byte loads");
+    const int rt = r0 + kRowsPerThread * tid;
     int cnt = 0;
-    if (rt + 32 <= p.R) {
-        const uint4 v0 = *reinterpret_cast<const uint4*>(p.fold + rt);
-        const uint4 v1 = *reinterpret_cast<const uint4*>(p.fold + rt + 16);
-        const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    if (rt + kRowsPerThread <= p.R) {
+        uint4 v[kRowsPerThread / 16];
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
+        for (int c = 0; c < kRowsPerThread / 16; ++c) v[c] = *reinterpret_cast<const uint4*>(p.fold + rt + 16 * c);
 #pragma unroll
-            for (int b = 0; b < 4; ++b) cnt += ((w[q] >> (8 * b)) & 0xffu) == 0 ? 1 : 0;
+        for (int c = 0; c < kRowsPerThread / 16; ++c) {
+            const uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) cnt += ((w[q] >> (8 * b)) & 0xffu) == 0 ? 1 : 0;
+        }
     } else {
-        for (int r = rt; r < p.R && r < rt + 32; ++r) cnt += p.fold[r] == 0 ? 1 : 0;
+        for (int r = rt; r < p.R && r < rt + kRowsPerThread; ++r) cnt += p.fold[r] == 0 ? 1 : 0;
     }
     cnt = static_cast<int>(wave_sum(static_cast<float>(cnt)));
     if ((tid & 63) == 0) s_tot[tid >> 6] = cnt;
     __syncthreads();
-    if (tid == 0) p.row_slot[r0] = s_tot[0] + s_tot[1] + s_tot[2] + s_tot[3];
+    if (tid == 0) {
+        int tot = 0;
+        for (int w = 0; w < 16; ++w) tot += s_tot[w];
+        p.row_slot[r0] = tot;
+    }
 }
 
 __global__ __launch_bounds__(1024) void compact_offsets_kernel(const CompactParams p, int ntiles) {
-    __shared__ int s_part[1024];
-    const int tid = threadIdx.x;
-    // thread t owns tiles 2t, 2t+1 (ntiles <= 2048)
+    __shared__ int s_wave[16];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    // thread t owns tiles 2t, 2t+1 (ntiles <= 2048); a wave scan with shuffles, then the waves'
+    // totals from LDS
     const int a = 2 * tid < ntiles ? p.row_slot[2 * tid * kCompactTile] : 0;
     const int b = 2 * tid + 1 < ntiles ? p.row_slot[(2 * tid + 1) * kCompactTile] : 0;
-    s_part[tid] = a + b;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {               // inclusive Hillis-Steele scan
-        const int v = tid >= d ? s_part[tid - d] : 0;
-        __syncthreads();
-        s_part[tid] += v;
-        __syncthreads();
+    int incl = a + b;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int t = __shfl_up(incl, d, kWave);
+        if (lane >= d) incl += t;
     }
-    const int excl = s_part[tid] - (a + b);
+    if (lane == kWave - 1) s_wave[wave] = incl;
+    __syncthreads();
+    int woff = 0, total = 0;
+    for (int w = 0; w < 16; ++w) {
+        const int t = s_wave[w];
+        woff += w < wave ? t : 0;
+        total += t;
+    }
+    const int excl = woff + incl - (a + b);
     if (2 * tid < ntiles) p.row_slot[2 * tid * kCompactTile] = excl;
     if (2 * tid + 1 < ntiles) p.row_slot[(2 * tid + 1) * kCompactTile] = excl + a;
-    if (tid == 1023) {
-        p.rec_count[0] = s_part[1023];
-        p.branch_off[p.nb] = s_part[1023];
+    if (tid == 0) {
+        p.rec_count[0] = total;
+        p.branch_off[p.nb] = total;
     }
 }
 
+// Pass 3: the tile is four steps of 8192 rows; in each, thread t owns the 8 consecutive rows
+// 8t .. 8t+7 of the step.  Every step's flags (one 8-byte load per thread) and the tile's offset
+// are requested at once (one memory round trip per tile); then, step by step, a
+// workgroup-wide exclusive scan of the per-thread counts places the thread's recompute rows,
+// the thread writes its 8 row -> slot entries as two 16-byte stores, and the step's list is
+// gathered in LDS and written out in consecutive stores.
 __global__ __launch_bounds__(1024) void compact_scatter_kernel(const CompactParams p) {
+    static_assert(kScatterSub == 8 * 1024 && kCompactTile % kScatterSub == 0, "8 rows per thread and step");
+    constexpr int kSteps = kCompactTile / kScatterSub;
+    __shared__ int s_wave[2][16];
     __shared__ int s_base;
+    __shared__ int s_list[kScatterSub];            // one step's recompute rows, in slot order
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     const int r0 = blockIdx.x * kCompactTile;
-    if (threadIdx.x == 0) s_base = p.row_slot[r0];
+    uint32_t bits[kSteps];                         // bit b: row rt + b exists and is recomputed
+#pragma unroll
+    for (int q = 0; q < kSteps; ++q) {
+        const int rt = r0 + q * kScatterSub + 8 * tid;
+        bits[q] = 0;
+        if (rt + 8 <= p.R) {
+            const uint2 v = *reinterpret_cast<const uint2*>(p.fold + rt);
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const uint32_t w = b < 4 ? v.x : v.y;
+                bits[q] |= (((w >> (8 * (b & 3))) & 0xffu) == 0 ? 1u : 0u) << b;
+            }
+        } else {
+            for (int b = 0; b < 8 && rt + b < p.R; ++b) bits[q] |= (p.fold[rt + b] == 0 ? 1u : 0u) << b;
+        }
+    }
+    if (tid == 0) s_base = p.row_slot[r0];         // the tile's offset (pass 2)
     __syncthreads();
-    const int base = s_base;
-    __syncthreads();                               // everyone has the offset before row r0 is rewritten
-    scan_rows(p, r0, min(p.R, r0 + kCompactTile), base);
+    int base = s_base;
+#pragma unroll
+    for (int q = 0; q < kSteps; ++q) {
+        const int rt = r0 + q * kScatterSub + 8 * tid;
+        const int cnt = __popc(bits[q]);
+        int incl = cnt;                            // inclusive scan over the wave
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int t = __shfl_up(incl, d, kWave);
+            if (lane >= d) incl += t;
+        }
+        if (lane == kWave - 1) s_wave[q & 1][wave] = incl;
+        __syncthreads();                           // (two buffers: step q+1 writes the other)
+        int local = 0, tot = 0;
+        for (int w = 0; w < 16; ++w) {
+            const int t = s_wave[q & 1][w];
+            local += w < wave ? t : 0;
+            tot += t;
+        }
+        local += incl - cnt;                       // step-local index of the thread's first recompute row
+        const int step_base = base;
+        int slot = base + local;                   // slot of the thread's first recompute row
+        base += tot;
+        const uint32_t bq = bits[q];
+        // branch starts among the thread's rows: one division per step, not one per row
+        if (rt < p.R) {
+            int br = (rt + p.N - 1) / p.N;
+            for (int m = br * p.N; m < rt + 8 && m < p.R; m += p.N, ++br)
+                p.branch_off[br] = slot + __popc(bq & ((1u << (m - rt)) - 1u));
+        }
+        int rs[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const int lb = local + __popc(bq & ((1u << b) - 1u));
+            const bool rec = (bq >> b) & 1u;
+            rs[b] = rec ? slot - local + lb : -1;
+            if (rec) s_list[lb] = rt + b;
+        }
+        if (rt + 8 <= p.R) {
+            int4* dst = reinterpret_cast<int4*>(p.row_slot + rt);
+            dst[0] = make_int4(rs[0], rs[1], rs[2], rs[3]);
+            dst[1] = make_int4(rs[4], rs[5], rs[6], rs[7]);
+        } else {
+            for (int b = 0; b < 8 && rt + b < p.R; ++b) p.row_slot[rt + b] = rs[b];
+        }
+        // the step's list leaves LDS in consecutive 4-byte stores (coalesced over each wave)
+        __syncthreads();
+        for (int e = tid; e < tot; e += 1024) p.rec_rows[step_base + e] = s_list[e];
+        __syncthreads();                           // the list is read before the next step refills it
+    }
 }
 
 __global__ __launch_bounds__(256) void resolve_kernel(const ResolveParams p) {
@@ -344,13 +438,13 @@ hipError_t launch_gate(const GateParams& p, hipStream_t st) {
 }
 
 hipError_t launch_compact(const CompactParams& p, hipStream_t st) {
-    if (p.R <= kCompactTile) {
+    if (p.R <= kSmallCompact) {
         hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, st, p);
         return hipGetLastError();
     }
     const int ntiles = (p.R + kCompactTile - 1) / kCompactTile;
     if (ntiles > 2048) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(compact_count_kernel, dim3(ntiles), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(compact_count_kernel, dim3(ntiles), dim3(1024), 0, st, p);
     hipLaunchKernelGGL(compact_offsets_kernel, dim3(1), dim3(1024), 0, st, p, ntiles);
     hipLaunchKernelGGL(compact_scatter_kernel, dim3(ntiles), dim3(1024), 0, st, p);
     return hipGetLastError();
