@@ -11,7 +11,11 @@ resident in HBM before the timed region.  Regime "cold" rotates through copies o
 weights totalling more than the 256 MB Infinity Cache, so every step streams its weights from
 HBM as a layer of a real stack does; "warm" reuses one copy.
 
-Prints one JSON line (see the README of the measurement in the design doc for every field).
+Prints one JSON line: the throughput fields (metric, value, unit, steps, ms_per_step, config,
+...), the dense (delta 0) path of the same kernels and their ratio, the dominant kernel's
+roofline object (achieved against peak, with the counter-measured HBM traffic while the GEMM
+sources match the committed record), per-launch stage times, and the CPU oracle's rate on a
+bounded sample of the same input (cpu_baseline) with the check of the GPU's output against it.
 """
 
 from __future__ import annotations
