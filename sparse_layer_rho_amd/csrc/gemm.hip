@@ -218,6 +218,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
     }
     M = M < 0 ? 0 : (M > p.m_cap ? p.m_cap : M);
     M = __builtin_amdgcn_readfirstlane(M);
+    if (M <= p.m_above || (p.m_upto > 0 && M > p.m_upto)) return;   // the other tile shape's launch owns M
     // rows [0, M) split evenly over c_use of the C row workgroups of each group: as many as M
     // needs, but at least min_chunks (two workgroups streaming the same weight tile, the
     // second from L2, run faster than one), decided here because M is only known on the device
