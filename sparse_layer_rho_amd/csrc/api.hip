@@ -25,8 +25,8 @@ struct Dims {
 
 struct Layout {
     GemmCfg c_qkv, c_o, c_gu, c_down;
-    GemmCfg c_gu_small;          // gate/up tiles for up to gu_small_rows recompute rows
-    int gu_small_rows;           // 0: one gate/up shape for every row count
+    GemmCfg c_gu_few, c_gu_many; // gate/up tile shapes for up to / above gu_split recompute rows
+    int gu_split;                // 0: c_gu for every row count
     size_t rho, fold, inv_rms, rec_rows, rec_count, branch_off, row_slot, src_branch, src_slot;
     size_t xn1, xn2, q_c, k_c, v_c, attn, h_mid, act, gemm_part, attn_o, attn_ml;
     size_t total;
@@ -97,18 +97,26 @@ GemmCfg pick_gemm(GemmKind kind, int n_cols, int k, int max_rows, int busy_chunk
     return c;
 }
 
-// Gate/up tiles for a folded row count: one 128-row chunk per column group and column groups
-// of at most 48 SwiGLU columns, as many as a whole number of workgroups per CU (256, 512, ...),
-// so every CU ingests the same weight bytes once.  Measured against the shape above at
-// M ~ 100: 1.5B 21.3 against 24.2 us, 7B 65.6 against 90.2 us, 14B 76.4 against 108 us; it
-// loses when nearly every row recomputes (1.5B and 14B at M = 288), so it takes M <= 256 only.
-GemmCfg pick_gate_up_small(int F) {
-    GemmCfg c{6, 1, 2, 1, 3, 2, 0, 1, true, 1, false};
-    const int cap = gemm_group_cols(c);              // 48 columns
-    const int per_cu = (F + 256 * cap - 1) / (256 * cap);
+// Gate/up tiles for more than 128 rows (R > 128): one launch holds two tile shapes and the
+// device picks by the recompute count M (gemm_pair_kernel).  Both keep 128-row chunks and stream
+// each group's weights once per chunk; the CU count sets the group counts.
+//   * many rows: 64-column groups (ntw 8), the fewest groups, so the activations -- read again
+//     by every group -- cost least; three chunks of <= 96 rows at M = 288.
+//   * few rows: 256 k groups, k the fewest workgroups per CU that keeps a group within 64
+//     columns, so every CU ingests the same weight bytes; the narrowest tile (ntw 6 for <= 48
+//     columns, else 8) that covers a group.  Used up to 256 rows when k = 1 (two chunks still
+//     fill two workgroups per CU), else up to 128.
+// Measured (gate/up alone, cold weights, us; few-rows / many-rows shape against the single
+// 32-column shape of pick_gemm): 1.5B M 108: 21.9 / 24.8, M 288: 32.4 / 39.8; 7B M 108: 66.1 /
+// 88.7, M 288: 121 / 155; 14B M 108: 65.9 / 104, M 288: 133 / 162.
+void pick_gate_up_pair(int F, GemmCfg* few, GemmCfg* many, int* split) {
+    const int k = (F + 256 * 64 - 1) / (256 * 64);
     const int tiles = (F + 15) / 16;
-    c.groups = 256 * per_cu < tiles ? 256 * per_cu : tiles;
-    return c;
+    const int g_few = 256 * k < tiles ? 256 * k : tiles;
+    const int ntw = (F + g_few - 1) / g_few <= 48 ? 6 : 8;
+    *few = GemmCfg{ntw, 1, 2, 1, 3, 2, g_few, 1, true, 1, false};
+    *many = GemmCfg{8, 1, 2, 1, 3, 2, (F + 63) / 64, 1, true, 1, false};
+    *split = k == 1 ? 256 : 128;
 }
 
 Layout layout_of(const Dims& d) {
@@ -117,8 +125,8 @@ Layout layout_of(const Dims& d) {
     L.c_qkv = pick_gemm(GEMM_QKV, d.Nq, d.D, d.R, 2);
     L.c_o = pick_gemm(GEMM_O, d.D, d.Do, d.R, 1 << 20);
     L.c_gu = pick_gemm(GEMM_GATE_UP, d.F, d.D, d.R, 2);
-    L.gu_small_rows = d.R > 128 ? 256 : 0;
-    L.c_gu_small = pick_gate_up_small(d.F);
+    L.gu_split = 0;
+    if (d.R > 128) pick_gate_up_pair(d.F, &L.c_gu_few, &L.c_gu_many, &L.gu_split);
     L.c_down = pick_gemm(GEMM_DOWN, d.D, d.F, d.R, 1);
     L.s_qkv = L.c_qkv.splits; L.s_o = L.c_o.splits; L.s_down = L.c_down.splits;
     L.chunk_len = d.P <= 1024 ? 128 : 512;
@@ -351,27 +359,20 @@ hipError_t run_out_proj(const Dims& d, const Layout& L, const uint16_t* attn, co
 }
 
 // FFN of the recompute rows of xn2 (RMSNorm'd h_mid) + fold-inherit + residual.
-// The gate/up projection has two tile shapes (layout_of): with `fold_expected` both are
-// enqueued, each limited to its row-count window, and the device runs the one that owns the
-// recompute count (the other's workgroups exit at once); otherwise only the shape for many rows.
-// Both form every output's sum in the same order, so the choice never changes a bit.
+// Above 128 rows the gate/up projection is one launch with two tile shapes, the device picking
+// by the recompute count (layout_of).  Every shape forms each output's sum in the same order, so
+// the choice never changes a bit.
 hipError_t run_ffn(const Dims& d, const Layout& L, const uint16_t* xn2, const uint16_t* h_mid,
                    const int32_t* rec_rows, const int32_t* rec_count, const int32_t* src_slot,
                    const uint16_t* w_gate_up, const uint16_t* w_down, uint16_t* H_out, void* ws, hipStream_t st,
-                   Tracer* tr, bool fold_expected) {
+                   Tracer* tr) {
     GemmArgs g{};
     g.A = xn2; g.lda = d.D; g.a_rows = rec_rows; g.a_row_limit = d.R; g.m_count = rec_count;
     g.m_cap = d.R; g.W = w_gate_up; g.K = d.D; g.Nout = 2 * d.F;
     g.act = at<uint16_t>(ws, L.act); g.F = d.F;
     if (tr) tr->begin();
-    hipError_t e = hipSuccess;
-    if (fold_expected && L.gu_small_rows > 0) {
-        GemmArgs gs = g;
-        gs.m_upto = L.gu_small_rows;
-        e = launch_gemm(gs, L.c_gu_small, st);
-        g.m_above = L.gu_small_rows;
-    }
-    if (e == hipSuccess) e = launch_gemm(g, L.c_gu, st);
+    hipError_t e = L.gu_split > 0 ? launch_gemm_pair(g, L.c_gu_few, L.c_gu_many, L.gu_split, st)
+                                  : launch_gemm(g, L.c_gu, st);
     if (tr) tr->end();
     if (e != hipSuccess) return e;
     GemmArgs h{};
@@ -635,7 +636,7 @@ int specfold_sparse_ffn(const specfold_shape* shape, const specfold_bf16* h_mid,
     hipError_t he = launch_row_norm(h_mid, d.R, d.D, nullptr, d.eps, ln2, xn, st);
     if (he != hipSuccess) return hip_status(he);
     return hip_status(run_ffn(d, L, xn, h_mid, rec_rows, rec_count, src_slot, w_gate_up, w_down, H_out, ws, st,
-                              nullptr, true));
+                              nullptr));
 }
 
 int specfold_verify_layer(const specfold_shape* shape, const int32_t* parent_host,
@@ -699,9 +700,8 @@ int specfold_verify_layer(const specfold_shape* shape, const int32_t* parent_hos
         return hip_status(he);
     if ((he = run_out_proj(d, L, attn, H_in, w->w_o, h_mid, w->ln2, xn2, ws, st, &tr)) != hipSuccess)
         return hip_status(he);
-    // at delta 0 only rows identical to their parent fold, so the shape for many rows is the one
     if ((he = run_ffn(d, L, xn2, h_mid, rec_rows, rec_count, src_slot, w->w_gate_up, w->w_down, H_out, ws, st,
-                      &tr, delta > 0.f)) != hipSuccess)
+                      &tr)) != hipSuccess)
         return hip_status(he);
     return SPECFOLD_OK;
 }

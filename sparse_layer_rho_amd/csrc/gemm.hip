@@ -195,30 +195,18 @@ struct Tile {
     static_assert(NBA >= 2 && NBW >= 2 && KSUB * LWU > LA && MAXN < 64, "ring depths");
 };
 
+// One workgroup's share of the product for M rows: workgroup `lin` of a launch with S K-splits
+// (smem: the rings, s_rows: the fused compaction's row list).
 template <int NTW, int WN, int TM, int KSUB, int NBW, int NBA, int EPI>
-__global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int M, const int lin, const int S, uint8_t* smem,
+                                          const int32_t* s_rows) {
     using T = Tile<NTW, WN, TM, KSUB, NBW, NBA>;
-    constexpr int WROWS = T::WROWS, MP = T::MP, QW = T::QW, QA = T::QA;
+    constexpr int MP = T::MP, QW = T::QW, QA = T::QA;
     static_assert(EPI != EPI_SWIGLU || NTW % 2 == 0, "SwiGLU tiles come in gate/up pairs");
-    extern __shared__ __align__(16) uint8_t smem[];
-    __shared__ int s_tot[4];
-    int32_t* s_rows = reinterpret_cast<int32_t*>(smem + T::LDS);
-
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
-    const int S = gridDim.y;
     const int C = p.m_chunks;
-
-    int M;
     const bool fused = p.fc_fold != nullptr;
-    if (fused) {
-        M = compact_in_lds(p, s_rows, s_tot, blockIdx.x == 0 && blockIdx.y == 0);   // (group 0, chunk 0)
-    } else {
-        M = p.m_count ? p.m_count[0] : p.m_fixed;
-    }
-    M = M < 0 ? 0 : (M > p.m_cap ? p.m_cap : M);
-    M = __builtin_amdgcn_readfirstlane(M);
-    if (M <= p.m_above || (p.m_upto > 0 && M > p.m_upto)) return;   // the other tile shape's launch owns M
     // rows [0, M) split evenly over c_use of the C row workgroups of each group: as many as M
     // needs, but at least min_chunks (two workgroups streaming the same weight tile, the
     // second from L2, run faster than one), decided here because M is only known on the device
@@ -233,7 +221,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
     // id % 8 and sit within 8 c_use ids of each other: they run on one XCD at about the same
     // time and the group's weights come from that XCD's L2 after the first fetched them.
     const int A = ((p.n_groups + 7) / 8) * 8 * c_use;          // busy workgroups per split
-    const int lin = blockIdx.x + gridDim.x * blockIdx.y;
     if (lin >= S * A) return;
     const int y = lin / A, id = lin - y * A;
     const int grp = id / (8 * c_use), rem = id - grp * 8 * c_use;
@@ -442,6 +429,39 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
 }
 
 template <int NTW, int WN, int TM, int KSUB, int NBW, int NBA, int EPI>
+__global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
+    using T = Tile<NTW, WN, TM, KSUB, NBW, NBA>;
+    extern __shared__ __align__(16) uint8_t smem[];
+    __shared__ int s_tot[4];
+    int32_t* s_rows = reinterpret_cast<int32_t*>(smem + T::LDS);
+    int M;
+    if (p.fc_fold != nullptr) {
+        M = compact_in_lds(p, s_rows, s_tot, blockIdx.x == 0 && blockIdx.y == 0);   // (group 0, chunk 0)
+    } else {
+        M = p.m_count ? p.m_count[0] : p.m_fixed;
+    }
+    M = M < 0 ? 0 : (M > p.m_cap ? p.m_cap : M);
+    M = __builtin_amdgcn_readfirstlane(M);
+    gemm_tile<NTW, WN, TM, KSUB, NBW, NBA, EPI>(p, M, blockIdx.x + gridDim.x * blockIdx.y, gridDim.y, smem, s_rows);
+}
+
+// Two tile shapes of one SwiGLU projection in one launch: shape A for M <= m_split rows, shape B
+// above.  M is only known on the device; two launches gated by row-count windows would cost the
+// idle one's workgroups a dispatch each, a single launch costs only the idle ids of the larger
+// grid.  The LDS is the larger shape's; pa and pb carry each shape's groups and chunks.
+template <int NA, int WA, int TA, int KA, int BA, int AA, int NB, int WB, int TB, int KB, int BB, int AB>
+__global__ __launch_bounds__(256) void gemm_pair_kernel(const GemmArgs pa, const GemmArgs pb, const int m_split) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    int M = pa.m_count ? pa.m_count[0] : pa.m_fixed;
+    M = M < 0 ? 0 : (M > pa.m_cap ? pa.m_cap : M);
+    M = __builtin_amdgcn_readfirstlane(M);
+    if (M <= m_split)
+        gemm_tile<NA, WA, TA, KA, BA, AA, EPI_SWIGLU>(pa, M, blockIdx.x, 1, smem, nullptr);
+    else
+        gemm_tile<NB, WB, TB, KB, BB, AB, EPI_SWIGLU>(pb, M, blockIdx.x, 1, smem, nullptr);
+}
+
+template <int NTW, int WN, int TM, int KSUB, int NBW, int NBA, int EPI>
 hipError_t launch_shape(GemmArgs a, const GemmCfg& c, int splits, hipStream_t st) {
     using T = Tile<NTW, WN, TM, KSUB, NBW, NBA>;
     const int groups = c.groups;
@@ -461,6 +481,39 @@ hipError_t launch_shape(GemmArgs a, const GemmCfg& c, int splits, hipStream_t st
     const dim3 grid(((groups + 7) / 8) * 8 * a.m_chunks, splits);
     hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, a);
     return hipGetLastError();
+}
+
+template <int NA, int WA, int TA, int KA, int BA, int AA, int NB, int WB, int TB, int KB, int BB, int AB>
+hipError_t launch_pair(GemmArgs a, const GemmCfg& ca, const GemmCfg& cb, int m_split, hipStream_t st) {
+    using TAs = Tile<NA, WA, TA, KA, BA, AA>;
+    using TBs = Tile<NB, WB, TB, KB, BB, AB>;
+    a.fc_fold = nullptr;
+    GemmArgs b = a;
+    a.n_groups = ca.groups;
+    a.min_chunks = ca.min_chunks;
+    const int rows_a = m_split < a.m_cap ? m_split : a.m_cap;   // shape A never sees more rows
+    a.m_chunks = (rows_a + TAs::MP - 1) / TAs::MP;
+    if (a.m_chunks < 1) a.m_chunks = 1;
+    b.n_groups = cb.groups;
+    b.min_chunks = cb.min_chunks;
+    b.m_chunks = (b.m_cap + TBs::MP - 1) / TBs::MP;
+    if (b.m_chunks < 1) b.m_chunks = 1;
+    const size_t lds = static_cast<size_t>(TAs::LDS > TBs::LDS ? TAs::LDS : TBs::LDS);
+    auto kern = gemm_pair_kernel<NA, WA, TA, KA, BA, AA, NB, WB, TB, KB, BB, AB>;
+    static size_t configured = 0;   // dynamic-LDS cap raised so far for this kernel
+    if (lds > configured) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+        configured = lds;
+    }
+    const int ga = ((ca.groups + 7) / 8) * 8 * a.m_chunks, gb = ((cb.groups + 7) / 8) * 8 * b.m_chunks;
+    hipLaunchKernelGGL(kern, dim3(ga > gb ? ga : gb), dim3(256), lds, st, a, b, m_split);
+    return hipGetLastError();
+}
+
+bool is_shape(const GemmCfg& c, int ntw, int wn, int tm, int ksub, int nbw, int nba) {
+    return c.ntw == ntw && c.wn == wn && c.tm == tm && c.ksub == ksub && c.nbw == nbw && c.nba == nba;
 }
 
 }  // namespace
@@ -487,6 +540,17 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmCfg& c, hipStream_t st) {
                         : launch_shape<NTW_, WN_, TM_, KS_, NBW_, NBA_, EPI_PARTIAL>(a, c, c.splits, st);
     SPECFOLD_GEMM_CASES(SPECFOLD_GEMM_CASE)
 #undef SPECFOLD_GEMM_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_pair(const GemmArgs& a, const GemmCfg& ca, const GemmCfg& cb, int m_split, hipStream_t st) {
+    if (!ca.swiglu || !cb.swiglu || ca.argmax || cb.argmax || a.fc_fold != nullptr || m_split < 0)
+        return hipErrorInvalidValue;
+#define SPECFOLD_GEMM_PAIR(NA, WA, TA, KA, BA, AA, NB, WB, TB, KB, BB, AB)                          \
+    if (is_shape(ca, NA, WA, TA, KA, BA, AA) && is_shape(cb, NB, WB, TB, KB, BB, AB))                   \
+        return launch_pair<NA, WA, TA, KA, BA, AA, NB, WB, TB, KB, BB, AB>(a, ca, cb, m_split, st);
+    SPECFOLD_GEMM_PAIRS(SPECFOLD_GEMM_PAIR)
+#undef SPECFOLD_GEMM_PAIR
     return hipErrorInvalidValue;
 }
 

@@ -64,9 +64,6 @@ struct GemmArgs {
     int K, Nout;
     int n_groups, m_chunks;  // set by the launcher
     int min_chunks;          // set by the launcher: rows split over at least this many workgroups
-    // row-count window of this launch: it does its work only when m_above < M and, if m_upto > 0,
-    // M <= m_upto (two tile shapes of one projection are enqueued, the device picks by M)
-    int m_above, m_upto;
     float* partial;          // [splits][m_cap][Nout]   (partial-sum epilogue)
     uint16_t* act;           // [m_cap][F]              (SwiGLU epilogue)
     int F;
@@ -103,12 +100,16 @@ struct GemmCfg {
 };
 // the (ntw, wn, tm, ksub, nbw, nba) shapes compiled
 #define SPECFOLD_GEMM_CASES(X) \
-    X(4, 1, 1, 2, 2, 2) X(4, 1, 1, 1, 3, 2) X(4, 1, 2, 1, 4, 2) X(2, 2, 2, 2, 2, 2) X(2, 1, 1, 1, 3, 2) \
-    X(6, 1, 2, 1, 3, 2)
+    X(4, 1, 1, 2, 2, 2) X(4, 1, 1, 1, 3, 2) X(4, 1, 2, 1, 4, 2) X(2, 2, 2, 2, 2, 2) X(2, 1, 1, 1, 3, 2)
 int gemm_chunk_rows(const GemmCfg& c);
 int gemm_group_cols(const GemmCfg& c);
 size_t gemm_lds_bytes(const GemmCfg& c);
 hipError_t launch_gemm(const GemmArgs& a, const GemmCfg& c, hipStream_t st);
+// SwiGLU projection with two tile shapes in one launch: ca for M <= m_split rows, cb above,
+// chosen on the device (no fused compaction).  Both form every output's sum in the same order.
+// The (ca ; cb) shape pairs compiled:
+#define SPECFOLD_GEMM_PAIRS(X) X(6, 1, 2, 1, 3, 2, 8, 1, 2, 1, 3, 2) X(8, 1, 2, 1, 3, 2, 8, 1, 2, 1, 3, 2)
+hipError_t launch_gemm_pair(const GemmArgs& a, const GemmCfg& ca, const GemmCfg& cb, int m_split, hipStream_t st);
 
 // ------------------------------------------------------------------ GEMM epilogues
 struct QkvEpiArgs {

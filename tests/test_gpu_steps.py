@@ -230,3 +230,41 @@ def test_out_proj_and_sparse_ffn_match_oracle(name):
     assert np.isfinite(got).all()
     assert rel_l2(got, exp_out) < 1e-2
     assert rel_l2(got - hm, exp_out - hm) < 2e-2
+
+
+@pytest.mark.parametrize("ffn,counts", [
+    (8960, (288, 257, 256, 100)),      # few-rows tiles 6 x 16 columns wide, switch above 256 rows
+    (13824, (288, 257, 256, 100)),     # few-rows tiles 8 x 16 columns wide
+    (18944, (288, 129, 128, 100)),     # two few-rows groups per CU: switch above 128 rows
+])
+def test_sparse_ffn_bits_independent_of_row_count_and_tile_shape(ffn, counts):
+    """Above 128 rows the FFN's gate/up projection holds two tile shapes in one launch and the
+    device picks one by the recompute count.  Every shape forms each sum in the same order, so a
+    row's output bits do not depend on how many other rows recompute -- on either side of the
+    switch -- and both shapes match the oracle's FFN."""
+    sh = Shape(9, 32, 1536, 12, 2, 128, ffn, 512)
+    case = LayerCase(sh, 17)
+    R, D = sh.n_branch * sh.block, sh.hidden
+    w, _, _ = case.device()
+    ws = sf.new_workspace(sh)
+    hm_np = case.H.reshape(R, D)
+    h_mid = dev_bf16(hm_np)
+    hm = host(h_mid)
+    rec_t = torch.arange(R, dtype=I32, device=DEV)
+    outs = {}
+    for M in counts:
+        cnt = torch.tensor([M], dtype=I32, device=DEV)
+        src = torch.from_numpy((np.arange(R) % M).astype(np.int32)).to(DEV)   # rows past M inherit a computed slot
+        out = torch.full((R, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+        sf.sparse_ffn(sh, h_mid, rec_t, cnt, src, w["ln2"], w["w_gate_up"], w["w_down"], out, ws)
+        torch.cuda.synchronize()
+        outs[M] = out.view(torch.int16).cpu().numpy()
+        print(f"sparse_ffn F={ffn} M={M}", flush=True)
+    for M in counts[1:]:
+        assert np.array_equal(outs[M][:M], outs[counts[0]][:M]), M
+    rows = np.array([0, 57, 99, 127, 200, 255, 256, 287])
+    f = oracle.ffn_rows(hm[rows], case.w["ln2"], case.w["w_gate_up"], case.w["w_down"], sh)
+    for M in (counts[0], counts[-1]):
+        sel = rows[rows < M]
+        got = torch.from_numpy(outs[M][sel]).view(torch.bfloat16).double().numpy()
+        assert rel_l2(got - hm[sel], f[:sel.size]) < 2e-2, M
