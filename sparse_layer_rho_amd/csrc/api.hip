@@ -44,13 +44,10 @@ Dims dims_of(const specfold_shape& s) {
     return d;
 }
 
-// Tile shape, column groups and K split of one projection.  A workgroup streams 64 weight rows
-// (32 output columns of SwiGLU) against a chunk of activation rows through small LDS rings, so
-// two or three workgroups share a CU and hide each other's waits.  Measured on the 1.5B shapes:
-// the recompute projections run two 64-row chunks per column group (M ~ 100), the gate/up weight
-// stage spans 256 bytes of every row, and the long-K down projection keeps 128-row chunks.
-// The projections: tile shape from the row count (performance only), K-splits from the
-// projection's shape alone.
+// Tile shape, column groups and K split of one projection.  A workgroup streams 64 or 128
+// weight rows against a chunk of activation rows through small LDS rings, so two or three
+// workgroups share a CU and hide each other's waits.  The tile shape is performance only (every
+// shape forms each sum in the same order); the K-splits come from the projection's shape alone.
 enum GemmKind { GEMM_QKV, GEMM_O, GEMM_GATE_UP, GEMM_DOWN };
 
 // K-splits of a partial-sum projection as a function of (kind, output columns, K) only -- not
@@ -74,18 +71,29 @@ int splits_for(GemmKind kind, int n_cols, int k) {
     return s < 1 ? 1 : s;
 }
 
-GemmCfg pick_gemm(GemmKind kind, int n_cols, int k, int max_rows, int busy_chunks) {
+// Measured on the 1.5B, 7B and 14B layers (each projection alone, cold weights, and whole layers):
+//   * QKV, the recompute rows (M ~ 100 folded): 64-column groups, two 64-row chunks; 1.5B
+//     6.9 us against 7.7 with 32-column groups;
+//   * o_proj, all R rows: 128-row chunks, three at R = 288 instead of five of 64, so the weights
+//     are re-read least; 1.5B 8.5 against 9.2 us, 7B 19.7 against 28.4, 14B 35 against 51;
+//   * gate/up up to 128 rows (above, gemm_pair_kernel's two shapes): weight stages of 256 bytes
+//     per row;
+//   * down: 128-row chunks; 128-column groups when a K-split spans at least 1024 elements (the
+//     7B and 14B shapes: 38 against 44 us at M = 108), else 64 (1.5B, 560 elements per split,
+//     where the wider tiles lose 4 us at M = 288).
+GemmCfg pick_gemm(GemmKind kind, int n_cols, int k, int max_rows) {
     GemmCfg c{};
     c.swiglu = kind == GEMM_GATE_UP;
-    c.ntw = 4; c.wn = 1;
-    if (kind == GEMM_GATE_UP) { c.tm = 1; c.ksub = 2; c.nbw = 2; c.nba = 2; }
-    else if (kind == GEMM_DOWN) { c.tm = 2; c.ksub = 1; c.nbw = 4; c.nba = 2; }
-    else {
-        // 64-column groups unless that leaves few workgroups: narrower groups re-read the
-        // activations more often, which only pays while it buys parallelism
-        const int chunks = (max_rows + 63) / 64;
-        const int busy = ((n_cols + 63) / 64) * (busy_chunks < chunks ? busy_chunks : chunks);
-        c.ntw = busy >= 128 ? 4 : 2; c.tm = 1; c.ksub = 1; c.nbw = 3; c.nba = 2;
+    c.wn = 1;
+    c.splits = splits_for(kind, n_cols, k);
+    switch (kind) {
+    case GEMM_QKV: c.ntw = 4; c.tm = 1; c.ksub = 1; c.nbw = 3; c.nba = 2; break;
+    case GEMM_O: c.ntw = 4; c.tm = 2; c.ksub = 1; c.nbw = 4; c.nba = 2; break;
+    case GEMM_GATE_UP: c.ntw = 4; c.tm = 1; c.ksub = 2; c.nbw = 2; c.nba = 2; break;
+    case GEMM_DOWN:
+        if (k / c.splits >= 1024) { c.ntw = 8; c.tm = 2; c.ksub = 1; c.nbw = 3; c.nba = 2; }
+        else { c.ntw = 4; c.tm = 2; c.ksub = 1; c.nbw = 4; c.nba = 2; }
+        break;
     }
     if (max_rows <= 64) { c.ntw = 2; c.wn = 2; c.tm = 2; c.ksub = 2; c.nbw = 2; c.nba = 2; }
     const int cap = gemm_group_cols(c);
@@ -93,7 +101,6 @@ GemmCfg pick_gemm(GemmKind kind, int n_cols, int k, int max_rows, int busy_chunk
     // the recompute-row projections keep two row workgroups per column group however small M
     // is (the split counts assume them)
     c.min_chunks = (kind == GEMM_QKV || kind == GEMM_GATE_UP) ? 2 : 1;
-    c.splits = splits_for(kind, n_cols, k);
     return c;
 }
 
@@ -107,7 +114,7 @@ GemmCfg pick_gemm(GemmKind kind, int n_cols, int k, int max_rows, int busy_chunk
 //     columns, else 8) that covers a group.  Used up to 256 rows when k = 1 (two chunks still
 //     fill two workgroups per CU), else up to 128.
 // Measured (gate/up alone, cold weights, us; few-rows / many-rows shape against the single
-// 32-column shape of pick_gemm): 1.5B M 108: 21.9 / 24.8, M 288: 32.4 / 39.8; 7B M 108: 66.1 /
+// 32-column shape pick_gemm uses up to 128 rows): 1.5B M 108: 21.9 / 24.8, M 288: 32.4 / 39.8; 7B M 108: 66.1 /
 // 88.7, M 288: 121 / 155; 14B M 108: 65.9 / 104, M 288: 133 / 162.
 void pick_gate_up_pair(int F, GemmCfg* few, GemmCfg* many, int* split) {
     const int k = (F + 256 * 64 - 1) / (256 * 64);
@@ -122,12 +129,12 @@ void pick_gate_up_pair(int F, GemmCfg* few, GemmCfg* many, int* split) {
 Layout layout_of(const Dims& d) {
     Layout L;
     // the recompute projections expect about 128 busy rows (folded M); o_proj has all R rows
-    L.c_qkv = pick_gemm(GEMM_QKV, d.Nq, d.D, d.R, 2);
-    L.c_o = pick_gemm(GEMM_O, d.D, d.Do, d.R, 1 << 20);
-    L.c_gu = pick_gemm(GEMM_GATE_UP, d.F, d.D, d.R, 2);
+    L.c_qkv = pick_gemm(GEMM_QKV, d.Nq, d.D, d.R);
+    L.c_o = pick_gemm(GEMM_O, d.D, d.Do, d.R);
+    L.c_gu = pick_gemm(GEMM_GATE_UP, d.F, d.D, d.R);
     L.gu_split = 0;
     if (d.R > 128) pick_gate_up_pair(d.F, &L.c_gu_few, &L.c_gu_many, &L.gu_split);
-    L.c_down = pick_gemm(GEMM_DOWN, d.D, d.F, d.R, 1);
+    L.c_down = pick_gemm(GEMM_DOWN, d.D, d.F, d.R);
     L.s_qkv = L.c_qkv.splits; L.s_o = L.c_o.splits; L.s_down = L.c_down.splits;
     L.chunk_len = d.P <= 1024 ? 128 : 512;
     L.n_chunks = d.P > 0 ? (d.P + L.chunk_len - 1) / L.chunk_len : 0;
