@@ -25,8 +25,9 @@ struct Dims {
 
 struct Layout {
     GemmCfg c_qkv, c_o, c_gu, c_down;
-    GemmCfg c_gu_few, c_gu_many; // gate/up tile shapes for up to / above gu_split recompute rows
-    int gu_split;                // 0: c_gu for every row count
+    GemmCfg c_gu_shapes[3];      // gate/up tile shapes for up to gu_upto[0], up to gu_upto[1], and more rows
+    int gu_upto[2];
+    bool gu_multi;               // false: c_gu for every row count
     size_t rho, fold, inv_rms, rec_rows, rec_count, branch_off, row_slot, src_branch, src_slot;
     size_t xn1, xn2, q_c, k_c, v_c, attn, h_mid, act, gemm_part, attn_o, attn_ml;
     size_t total;
@@ -76,7 +77,7 @@ int splits_for(GemmKind kind, int n_cols, int k) {
 //     6.9 us against 7.7 with 32-column groups;
 //   * o_proj, all R rows: 128-row chunks, three at R = 288 instead of five of 64, so the weights
 //     are re-read least; 1.5B 8.5 against 9.2 us, 7B 19.7 against 28.4, 14B 35 against 51;
-//   * gate/up up to 128 rows (above, gemm_pair_kernel's two shapes): weight stages of 256 bytes
+//   * gate/up up to 128 rows (above, gemm_shapes_kernel's three shapes): weight stages of 256 bytes
 //     per row;
 //   * down: 128-row chunks; 128-column groups when a K-split spans at least 1024 elements (the
 //     7B and 14B shapes: 38 against 44 us at M = 108), else 64 (1.5B, 560 elements per split,
@@ -104,26 +105,30 @@ GemmCfg pick_gemm(GemmKind kind, int n_cols, int k, int max_rows) {
     return c;
 }
 
-// Gate/up tiles for more than 128 rows (R > 128): one launch holds two tile shapes and the
-// device picks by the recompute count M (gemm_pair_kernel).  Both keep 128-row chunks and stream
-// each group's weights once per chunk; the CU count sets the group counts.
+// Gate/up tiles for more than 128 rows (R > 128): one launch holds three tile shapes and the
+// device picks by the recompute count M (gemm_shapes_kernel).  Each group's weights stream once
+// per row chunk; the CU count sets the group counts.
 //   * many rows: 64-column groups (ntw 8), the fewest groups, so the activations -- read again
-//     by every group -- cost least; three chunks of <= 96 rows at M = 288.
+//     by every group -- cost least; 128-row chunks, three of <= 96 rows at M = 288.
 //   * few rows: 256 k groups, k the fewest workgroups per CU that keeps a group within 64
 //     columns, so every CU ingests the same weight bytes; the narrowest tile (ntw 6 for <= 48
-//     columns, else 8) that covers a group.  Used up to 256 rows when k = 1 (two chunks still
-//     fill two workgroups per CU), else up to 128.
+//     columns, else 8) that covers a group; one 128-row chunk up to 256 rows when k = 1 (two
+//     chunks still fill two workgroups per CU), else up to 128.
+//   * up to 64 rows: the few-rows groups with a 64-row tile (no MFMAs on empty row tiles).
 // Measured (gate/up alone, cold weights, us; few-rows / many-rows shape against the single
-// 32-column shape pick_gemm uses up to 128 rows): 1.5B M 108: 21.9 / 24.8, M 288: 32.4 / 39.8; 7B M 108: 66.1 /
-// 88.7, M 288: 121 / 155; 14B M 108: 65.9 / 104, M 288: 133 / 162.
-void pick_gate_up_pair(int F, GemmCfg* few, GemmCfg* many, int* split) {
+// 32-column shape pick_gemm uses up to 128 rows): 1.5B M 108: 21.9 / 24.8, M 288: 32.4 / 39.8;
+// 7B M 108: 66.1 / 88.7, M 288: 121 / 155; 14B M 108: 65.9 / 104, M 288: 133 / 162.  At M = 60
+// the 64-row tile against the 128-row one: 1.5B 18.2 / 21.1, 7B 54.7 / 59.1, 14B 57.6 / 62.0.
+void pick_gate_up_shapes(int F, GemmCfg* c, int* upto) {
     const int k = (F + 256 * 64 - 1) / (256 * 64);
     const int tiles = (F + 15) / 16;
     const int g_few = 256 * k < tiles ? 256 * k : tiles;
     const int ntw = (F + g_few - 1) / g_few <= 48 ? 6 : 8;
-    *few = GemmCfg{ntw, 1, 2, 1, 3, 2, g_few, 1, true, 1, false};
-    *many = GemmCfg{8, 1, 2, 1, 3, 2, (F + 63) / 64, 1, true, 1, false};
-    *split = k == 1 ? 256 : 128;
+    c[0] = GemmCfg{ntw, 1, 1, 1, 3, 2, g_few, 1, true, 1, false};
+    c[1] = GemmCfg{ntw, 1, 2, 1, 3, 2, g_few, 1, true, 1, false};
+    c[2] = GemmCfg{8, 1, 2, 1, 3, 2, (F + 63) / 64, 1, true, 1, false};
+    upto[0] = 64;
+    upto[1] = k == 1 ? 256 : 128;
 }
 
 Layout layout_of(const Dims& d) {
@@ -132,8 +137,8 @@ Layout layout_of(const Dims& d) {
     L.c_qkv = pick_gemm(GEMM_QKV, d.Nq, d.D, d.R);
     L.c_o = pick_gemm(GEMM_O, d.D, d.Do, d.R);
     L.c_gu = pick_gemm(GEMM_GATE_UP, d.F, d.D, d.R);
-    L.gu_split = 0;
-    if (d.R > 128) pick_gate_up_pair(d.F, &L.c_gu_few, &L.c_gu_many, &L.gu_split);
+    L.gu_multi = d.R > 128;
+    if (L.gu_multi) pick_gate_up_shapes(d.F, L.c_gu_shapes, L.gu_upto);
     L.c_down = pick_gemm(GEMM_DOWN, d.D, d.F, d.R);
     L.s_qkv = L.c_qkv.splits; L.s_o = L.c_o.splits; L.s_down = L.c_down.splits;
     L.chunk_len = d.P <= 1024 ? 128 : 512;
@@ -366,7 +371,7 @@ hipError_t run_out_proj(const Dims& d, const Layout& L, const uint16_t* attn, co
 }
 
 // FFN of the recompute rows of xn2 (RMSNorm'd h_mid) + fold-inherit + residual.
-// Above 128 rows the gate/up projection is one launch with two tile shapes, the device picking
+// Above 128 rows the gate/up projection is one launch with three tile shapes, the device picking
 // by the recompute count (layout_of).  Every shape forms each output's sum in the same order, so
 // the choice never changes a bit.
 hipError_t run_ffn(const Dims& d, const Layout& L, const uint16_t* xn2, const uint16_t* h_mid,
@@ -378,8 +383,7 @@ hipError_t run_ffn(const Dims& d, const Layout& L, const uint16_t* xn2, const ui
     g.m_cap = d.R; g.W = w_gate_up; g.K = d.D; g.Nout = 2 * d.F;
     g.act = at<uint16_t>(ws, L.act); g.F = d.F;
     if (tr) tr->begin();
-    hipError_t e = L.gu_split > 0 ? launch_gemm_pair(g, L.c_gu_few, L.c_gu_many, L.gu_split, st)
-                                  : launch_gemm(g, L.c_gu, st);
+    hipError_t e = L.gu_multi ? launch_gemm_shapes(g, L.c_gu_shapes, L.gu_upto, st) : launch_gemm(g, L.c_gu, st);
     if (tr) tr->end();
     if (e != hipSuccess) return e;
     GemmArgs h{};

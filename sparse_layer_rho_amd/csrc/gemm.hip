@@ -445,20 +445,33 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
     gemm_tile<NTW, WN, TM, KSUB, NBW, NBA, EPI>(p, M, blockIdx.x + gridDim.x * blockIdx.y, gridDim.y, smem, s_rows);
 }
 
-// Two tile shapes of one SwiGLU projection in one launch: shape A for M <= m_split rows, shape B
-// above.  M is only known on the device; two launches gated by row-count windows would cost the
-// idle one's workgroups a dispatch each, a single launch costs only the idle ids of the larger
-// grid.  The LDS is the larger shape's; pa and pb carry each shape's groups and chunks.
-template <int NA, int WA, int TA, int KA, int BA, int AA, int NB, int WB, int TB, int KB, int BB, int AB>
-__global__ __launch_bounds__(256) void gemm_pair_kernel(const GemmArgs pa, const GemmArgs pb, const int m_split) {
+// A tile shape as a type, for the launch that holds several
+template <int NTW, int WN, int TM, int KSUB, int NBW, int NBA>
+struct Shape {
+    using T = Tile<NTW, WN, TM, KSUB, NBW, NBA>;
+    static bool is(const GemmCfg& c) {
+        return c.ntw == NTW && c.wn == WN && c.tm == TM && c.ksub == KSUB && c.nbw == NBW && c.nba == NBA;
+    }
+    static __device__ __forceinline__ void run(const GemmArgs& p, int M, uint8_t* smem) {
+        gemm_tile<NTW, WN, TM, KSUB, NBW, NBA, EPI_SWIGLU>(p, M, blockIdx.x, 1, smem, nullptr);
+    }
+};
+
+// Three tile shapes of one SwiGLU projection in one launch: shape A for M <= upto_a rows, B for
+// M <= upto_b, C above.  M is only known on the device; launches gated by row-count windows
+// would cost every idle launch's workgroups a dispatch, a single launch costs only the idle ids
+// of its grid (the largest shape's).  The LDS is the largest shape's; p[i] carries shape i's
+// groups and chunks.
+template <class SA, class SB, class SC>
+__global__ __launch_bounds__(256) void gemm_shapes_kernel(const GemmArgs pa, const GemmArgs pb, const GemmArgs pc,
+                                                          const int upto_a, const int upto_b) {
     extern __shared__ __align__(16) uint8_t smem[];
     int M = pa.m_count ? pa.m_count[0] : pa.m_fixed;
     M = M < 0 ? 0 : (M > pa.m_cap ? pa.m_cap : M);
     M = __builtin_amdgcn_readfirstlane(M);
-    if (M <= m_split)
-        gemm_tile<NA, WA, TA, KA, BA, AA, EPI_SWIGLU>(pa, M, blockIdx.x, 1, smem, nullptr);
-    else
-        gemm_tile<NB, WB, TB, KB, BB, AB, EPI_SWIGLU>(pb, M, blockIdx.x, 1, smem, nullptr);
+    if (M <= upto_a) SA::run(pa, M, smem);
+    else if (M <= upto_b) SB::run(pb, M, smem);
+    else SC::run(pc, M, smem);
 }
 
 template <int NTW, int WN, int TM, int KSUB, int NBW, int NBA, int EPI>
@@ -483,23 +496,26 @@ hipError_t launch_shape(GemmArgs a, const GemmCfg& c, int splits, hipStream_t st
     return hipGetLastError();
 }
 
-template <int NA, int WA, int TA, int KA, int BA, int AA, int NB, int WB, int TB, int KB, int BB, int AB>
-hipError_t launch_pair(GemmArgs a, const GemmCfg& ca, const GemmCfg& cb, int m_split, hipStream_t st) {
-    using TAs = Tile<NA, WA, TA, KA, BA, AA>;
-    using TBs = Tile<NB, WB, TB, KB, BB, AB>;
+template <class SA, class SB, class SC>
+hipError_t launch_shapes(GemmArgs a, const GemmCfg* c, const int* upto, hipStream_t st) {
     a.fc_fold = nullptr;
-    GemmArgs b = a;
-    a.n_groups = ca.groups;
-    a.min_chunks = ca.min_chunks;
-    const int rows_a = m_split < a.m_cap ? m_split : a.m_cap;   // shape A never sees more rows
-    a.m_chunks = (rows_a + TAs::MP - 1) / TAs::MP;
-    if (a.m_chunks < 1) a.m_chunks = 1;
-    b.n_groups = cb.groups;
-    b.min_chunks = cb.min_chunks;
-    b.m_chunks = (b.m_cap + TBs::MP - 1) / TBs::MP;
-    if (b.m_chunks < 1) b.m_chunks = 1;
-    const size_t lds = static_cast<size_t>(TAs::LDS > TBs::LDS ? TAs::LDS : TBs::LDS);
-    auto kern = gemm_pair_kernel<NA, WA, TA, KA, BA, AA, NB, WB, TB, KB, BB, AB>;
+    GemmArgs p[3] = {a, a, a};
+    const int mp[3] = {SA::T::MP, SB::T::MP, SC::T::MP};
+    const int rows[3] = {upto[0], upto[1], a.m_cap};   // the most rows each shape ever sees
+    int grid = 1;
+    for (int i = 0; i < 3; ++i) {
+        p[i].n_groups = c[i].groups;
+        p[i].min_chunks = c[i].min_chunks;
+        const int r = rows[i] < a.m_cap ? rows[i] : a.m_cap;
+        p[i].m_chunks = (r + mp[i] - 1) / mp[i];
+        if (p[i].m_chunks < 1) p[i].m_chunks = 1;
+        const int g = ((c[i].groups + 7) / 8) * 8 * p[i].m_chunks;
+        if (g > grid) grid = g;
+    }
+    size_t lds = static_cast<size_t>(SA::T::LDS);
+    if (static_cast<size_t>(SB::T::LDS) > lds) lds = SB::T::LDS;
+    if (static_cast<size_t>(SC::T::LDS) > lds) lds = SC::T::LDS;
+    auto kern = gemm_shapes_kernel<SA, SB, SC>;
     static size_t configured = 0;   // dynamic-LDS cap raised so far for this kernel
     if (lds > configured) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -507,13 +523,8 @@ hipError_t launch_pair(GemmArgs a, const GemmCfg& ca, const GemmCfg& cb, int m_s
         if (e != hipSuccess) return e;
         configured = lds;
     }
-    const int ga = ((ca.groups + 7) / 8) * 8 * a.m_chunks, gb = ((cb.groups + 7) / 8) * 8 * b.m_chunks;
-    hipLaunchKernelGGL(kern, dim3(ga > gb ? ga : gb), dim3(256), lds, st, a, b, m_split);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, p[0], p[1], p[2], upto[0], upto[1]);
     return hipGetLastError();
-}
-
-bool is_shape(const GemmCfg& c, int ntw, int wn, int tm, int ksub, int nbw, int nba) {
-    return c.ntw == ntw && c.wn == wn && c.tm == tm && c.ksub == ksub && c.nbw == nbw && c.nba == nba;
 }
 
 }  // namespace
@@ -543,14 +554,19 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmCfg& c, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm_pair(const GemmArgs& a, const GemmCfg& ca, const GemmCfg& cb, int m_split, hipStream_t st) {
-    if (!ca.swiglu || !cb.swiglu || ca.argmax || cb.argmax || a.fc_fold != nullptr || m_split < 0)
-        return hipErrorInvalidValue;
-#define SPECFOLD_GEMM_PAIR(NA, WA, TA, KA, BA, AA, NB, WB, TB, KB, BB, AB)                          \
-    if (is_shape(ca, NA, WA, TA, KA, BA, AA) && is_shape(cb, NB, WB, TB, KB, BB, AB))                   \
-        return launch_pair<NA, WA, TA, KA, BA, AA, NB, WB, TB, KB, BB, AB>(a, ca, cb, m_split, st);
-    SPECFOLD_GEMM_PAIRS(SPECFOLD_GEMM_PAIR)
-#undef SPECFOLD_GEMM_PAIR
+hipError_t launch_gemm_shapes(const GemmArgs& a, const GemmCfg* c, const int* upto, hipStream_t st) {
+    if (a.fc_fold != nullptr || upto[0] < 0 || upto[1] < upto[0]) return hipErrorInvalidValue;
+    for (int i = 0; i < 3; ++i)
+        if (!c[i].swiglu || c[i].argmax) return hipErrorInvalidValue;
+#define SPECFOLD_GEMM_TRIPLE(A0, A1, A2, A3, A4, A5, B0, B1, B2, B3, B4, B5, C0, C1, C2, C3, C4, C5)      \
+    {                                                                                              \
+        using SA = Shape<A0, A1, A2, A3, A4, A5>;                                                  \
+        using SB = Shape<B0, B1, B2, B3, B4, B5>;                                                  \
+        using SC = Shape<C0, C1, C2, C3, C4, C5>;                                                  \
+        if (SA::is(c[0]) && SB::is(c[1]) && SC::is(c[2])) return launch_shapes<SA, SB, SC>(a, c, upto, st); \
+    }
+    SPECFOLD_GEMM_TRIPLES(SPECFOLD_GEMM_TRIPLE)
+#undef SPECFOLD_GEMM_TRIPLE
     return hipErrorInvalidValue;
 }
 

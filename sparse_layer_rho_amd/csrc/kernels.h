@@ -105,11 +105,13 @@ int gemm_chunk_rows(const GemmCfg& c);
 int gemm_group_cols(const GemmCfg& c);
 size_t gemm_lds_bytes(const GemmCfg& c);
 hipError_t launch_gemm(const GemmArgs& a, const GemmCfg& c, hipStream_t st);
-// SwiGLU projection with two tile shapes in one launch: ca for M <= m_split rows, cb above,
-// chosen on the device (no fused compaction).  Both form every output's sum in the same order.
-// The (ca ; cb) shape pairs compiled:
-#define SPECFOLD_GEMM_PAIRS(X) X(6, 1, 2, 1, 3, 2, 8, 1, 2, 1, 3, 2) X(8, 1, 2, 1, 3, 2, 8, 1, 2, 1, 3, 2)
-hipError_t launch_gemm_pair(const GemmArgs& a, const GemmCfg& ca, const GemmCfg& cb, int m_split, hipStream_t st);
+// SwiGLU projection with three tile shapes in one launch: c[0] for M <= upto[0] rows, c[1] for
+// M <= upto[1], c[2] above, chosen on the device (no fused compaction).  Every shape forms each
+// output's sum in the same order.  The (c[0] ; c[1] ; c[2]) triples compiled:
+#define SPECFOLD_GEMM_TRIPLES(X)                                                                   \
+    X(6, 1, 1, 1, 3, 2, 6, 1, 2, 1, 3, 2, 8, 1, 2, 1, 3, 2)                                        \
+    X(8, 1, 1, 1, 3, 2, 8, 1, 2, 1, 3, 2, 8, 1, 2, 1, 3, 2)
+hipError_t launch_gemm_shapes(const GemmArgs& a, const GemmCfg* c, const int* upto, hipStream_t st);
 
 // ------------------------------------------------------------------ GEMM epilogues
 struct QkvEpiArgs {

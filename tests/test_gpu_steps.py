@@ -233,15 +233,16 @@ def test_out_proj_and_sparse_ffn_match_oracle(name):
 
 
 @pytest.mark.parametrize("ffn,counts", [
-    (8960, (288, 257, 256, 100)),      # few-rows tiles 6 x 16 columns wide, switch above 256 rows
-    (13824, (288, 257, 256, 100)),     # few-rows tiles 8 x 16 columns wide
-    (18944, (288, 129, 128, 100)),     # two few-rows groups per CU: switch above 128 rows
+    (8960, (288, 257, 256, 100, 65, 64, 40)),     # few-rows tiles 6 x 16 columns wide, switch above 256 rows
+    (13824, (288, 257, 256, 100, 65, 64, 40)),    # few-rows tiles 8 x 16 columns wide
+    (18944, (288, 129, 128, 100, 65, 64, 40)),    # two few-rows groups per CU: switch above 128 rows
 ])
 def test_sparse_ffn_bits_independent_of_row_count_and_tile_shape(ffn, counts):
-    """Above 128 rows the FFN's gate/up projection holds two tile shapes in one launch and the
-    device picks one by the recompute count.  Every shape forms each sum in the same order, so a
-    row's output bits do not depend on how many other rows recompute -- on either side of the
-    switch -- and both shapes match the oracle's FFN."""
+    """Above 128 rows the FFN's gate/up projection holds three tile shapes in one launch and the
+    device picks one by the recompute count (up to 64 rows, up to the few-rows limit, above).
+    Every shape forms each sum in the same order, so a row's output bits do not depend on how
+    many other rows recompute -- on either side of each switch -- and the shapes match the
+    oracle's FFN."""
     sh = Shape(9, 32, 1536, 12, 2, 128, ffn, 512)
     case = LayerCase(sh, 17)
     R, D = sh.n_branch * sh.block, sh.hidden
@@ -262,9 +263,9 @@ def test_sparse_ffn_bits_independent_of_row_count_and_tile_shape(ffn, counts):
         print(f"sparse_ffn F={ffn} M={M}", flush=True)
     for M in counts[1:]:
         assert np.array_equal(outs[M][:M], outs[counts[0]][:M]), M
-    rows = np.array([0, 57, 99, 127, 200, 255, 256, 287])
+    rows = np.array([0, 5, 33, 57, 99, 127, 200, 255, 256, 287])
     f = oracle.ffn_rows(hm[rows], case.w["ln2"], case.w["w_gate_up"], case.w["w_down"], sh)
-    for M in (counts[0], counts[-1]):
+    for M in (counts[0], counts[3], counts[-1]):
         sel = rows[rows < M]
         got = torch.from_numpy(outs[M][sel]).view(torch.bfloat16).double().numpy()
         assert rel_l2(got - hm[sel], f[:sel.size]) < 2e-2, M
