@@ -402,14 +402,19 @@ hipError_t launch_prefix_qt(const AttnArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Two query tiles per workgroup while that keeps the grid small (fewer waves per CU read each
-// block from LDS); four once the grid is large, where every workgroup's K/V stages cost L2
-// bandwidth and sharing them over more queries pays.
+// Two query tiles per workgroup while their workgroups fit on the CUs at once (fewer waves per
+// CU read each block from LDS); four once two would need a second round, where sharing each
+// K/V stage over more queries pays.  A chunk of one stage leaves room for two workgroups per
+// CU, a longer one (two stage buffers) for one.  The recompute count is known on the device
+// only; the tiles are sized for half the rows recomputing.  Measured: the 7B layer at P = 2048
+// (M = 100, 352 busy two-tile workgroups) 28.3 against 18.9 us with four; the 1.5B layer at
+// P = 2048 (M = 108, 168 busy) 14.0 against 15.5.
 template <int HD>
 hipError_t launch_prefix_hd(const AttnArgs& a, hipStream_t st) {
     const int G = a.Hq / a.Hkv;
-    const long wgs2 = static_cast<long>(a.n_chunks) * a.Hkv * ((a.m_cap * G + 31) / 32);
-    return wgs2 <= 1024 ? launch_prefix_qt<HD, 2>(a, st) : launch_prefix_qt<HD, 4>(a, st);
+    const long slots = a.chunk_len > kStageKeys ? 256 : 512;
+    const long busy2 = static_cast<long>(a.n_chunks) * a.Hkv * ((((a.m_cap + 1) / 2) * G + 31) / 32);
+    return busy2 <= slots ? launch_prefix_qt<HD, 2>(a, st) : launch_prefix_qt<HD, 4>(a, st);
 }
 
 }  // namespace
