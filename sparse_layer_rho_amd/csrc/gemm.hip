@@ -25,6 +25,8 @@
 // Epilogues: fp32 partial sums (reduced in a fixed order by the next kernel, so results are
 // deterministic), or SwiGLU for the FFN's gate/up projection, where a wave's two weight tiles
 // are the gate and up rows of the same 16 output columns.
+#include <atomic>
+
 #include "kernels.h"
 
 namespace specfold {
@@ -445,6 +447,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
     gemm_tile<NTW, WN, TM, KSUB, NBW, NBA, EPI>(p, M, blockIdx.x + gridDim.x * blockIdx.y, gridDim.y, smem, s_rows);
 }
 
+// Raise a kernel's dynamic-LDS cap to at least `lds` bytes.  `cap` holds the cap raised so far
+// for that kernel (one atomic per launcher instance), so concurrent host threads at worst both
+// set the same attribute.
+inline hipError_t raise_lds_cap(const void* kern, size_t lds, std::atomic<size_t>& cap) {
+    if (lds <= cap.load(std::memory_order_relaxed)) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e == hipSuccess) {
+        size_t cur = cap.load(std::memory_order_relaxed);
+        while (cur < lds && !cap.compare_exchange_weak(cur, lds, std::memory_order_relaxed)) {
+        }
+    }
+    return e;
+}
+
 // A tile shape as a type, for the launch that holds several
 template <int NTW, int WN, int TM, int KSUB, int NBW, int NBA>
 struct Shape {
@@ -484,13 +500,9 @@ hipError_t launch_shape(GemmArgs a, const GemmCfg& c, int splits, hipStream_t st
     if (a.m_chunks < 1) a.m_chunks = 1;
     const size_t lds = static_cast<size_t>(T::LDS) + (a.fc_fold ? static_cast<size_t>(a.fc_R) * 4 : 0);
     auto kern = gemm_kernel<NTW, WN, TM, KSUB, NBW, NBA, EPI>;
-    static size_t configured = 0;   // dynamic-LDS cap raised so far for this kernel
-    if (lds > configured) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        if (e != hipSuccess) return e;
-        configured = lds;
-    }
+    static std::atomic<size_t> cap{0};
+    hipError_t e = raise_lds_cap(reinterpret_cast<const void*>(kern), lds, cap);
+    if (e != hipSuccess) return e;
     const dim3 grid(((groups + 7) / 8) * 8 * a.m_chunks, splits);
     hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, a);
     return hipGetLastError();
@@ -516,13 +528,9 @@ hipError_t launch_shapes(GemmArgs a, const GemmCfg* c, const int* upto, hipStrea
     if (static_cast<size_t>(SB::T::LDS) > lds) lds = SB::T::LDS;
     if (static_cast<size_t>(SC::T::LDS) > lds) lds = SC::T::LDS;
     auto kern = gemm_shapes_kernel<SA, SB, SC>;
-    static size_t configured = 0;   // dynamic-LDS cap raised so far for this kernel
-    if (lds > configured) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        if (e != hipSuccess) return e;
-        configured = lds;
-    }
+    static std::atomic<size_t> cap{0};
+    hipError_t e = raise_lds_cap(reinterpret_cast<const void*>(kern), lds, cap);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, p[0], p[1], p[2], upto[0], upto[1]);
     return hipGetLastError();
 }
