@@ -106,7 +106,10 @@ __global__ __launch_bounds__(1024) void oproj_epilogue_kernel(const float* __res
     const __amdgpu_buffer_rsrc_t rH = make_rsrc(H, static_cast<uint32_t>(static_cast<size_t>(R) * D * 2));
     const uint32_t stride = static_cast<uint32_t>(R) * D * 4;
     f32x4 acc[MAXU];
-    uint2 hv[MAXU];
+    uint2 hv[MAXU], wv[MAXU];
+    // the norm weights come with the partials and the residual (one round trip, not a second
+    // one after the row's reduction)
+    const __amdgpu_buffer_rsrc_t rL = make_rsrc(ln, static_cast<uint32_t>(D) * 2);
 #pragma unroll
     for (int k = 0; k < MAXU; ++k) {
         const int u = tid + k * B;
@@ -114,6 +117,7 @@ __global__ __launch_bounds__(1024) void oproj_epilogue_kernel(const float* __res
         const uint32_t e = static_cast<uint32_t>(r) * D + 4 * u;
         acc[k] = sum_splits<SPL>(rP, valid ? e * 4 : kOob, stride, splits);
         hv[k] = buf_load8(rH, valid ? e * 2 : kOob);
+        wv[k] = xn && ln ? buf_load8(rL, valid ? 8 * u : kOob) : make_uint2(0, 0);
     }
     float ss = 0.f;
 #pragma unroll
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(1024) void oproj_epilogue_kernel(const float* __res
         if (u >= D4) continue;
         float h[4], w[4] = {1.f, 1.f, 1.f, 1.f};
         unpack4(hv[k], h);
-        if (ln) unpack4(*reinterpret_cast<const uint2*>(ln + 4 * u), w);
+        if (ln) unpack4(wv[k], w);
 #pragma unroll
         for (int e = 0; e < 4; ++e) h[e] = h[e] * inv * w[e];
         *reinterpret_cast<uint2*>(xn + static_cast<size_t>(r) * D + 4 * u) = pack4(h);

@@ -31,25 +31,41 @@ __device__ __forceinline__ float rho_of(float a, float b) {
     return __builtin_nanf("");
 }
 
-// xn chunk = bf16(x * s * ln) for the 8 elements of chunk k of a row
-__device__ __forceinline__ uint4 norm_chunk(const float* x, float s, const uint16_t* ln, int k) {
-    float y[8];
-    if (ln) {
-        float w[8];
-        unpack8(*reinterpret_cast<const uint4*>(ln + 8 * k), w);
+// xn chunk = bf16(x * s * w) for the 8 elements of a chunk, wv its 8 norm weights
+__device__ __forceinline__ uint4 norm_chunk_w(const float* x, float s, const uint4& wv) {
+    float w[8], y[8];
+    unpack8(wv, w);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = x[e] * s * w[e];
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = x[e] * s;
-    }
+    for (int e = 0; e < 8; ++e) y[e] = x[e] * s * w[e];
     return pack8(y);
 }
 
+// xn chunk = bf16(x * s * ln) for the 8 elements of chunk k of a row (no ln: bf16(x * s))
+__device__ __forceinline__ uint4 norm_chunk(const float* x, float s, const uint16_t* ln, int k) {
+    if (ln) return norm_chunk_w(x, s, *reinterpret_cast<const uint4*>(ln + 8 * k));
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = x[e] * s;
+    return pack8(y);
+}
+
+// the norm weights of the CPL chunks a lane normalises, requested with the row (chunks past the
+// row read zeros) so the norm does not wait for a second round trip after the reductions
+template <int CPL>
+__device__ __forceinline__ void load_norm_weights(const uint16_t* ln, int D, int lane, uint4 (&wv)[CPL]) {
+    const __amdgpu_buffer_rsrc_t rL = make_rsrc(ln, static_cast<uint32_t>(D) * 2);
+    const int nch = D >> 3;
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+        const int k = lane + t * kWave;
+        wv[t] = buf_load16(rL, k < nch ? 16 * k : kOob);
+    }
+}
+
 // One wave computes rho, fold, inv_rms (and optionally the normalised row) of one row.  Lane l
-// holds chunks l, l + 64, ... (CPL of them) of the child and the parent row; all of them are
-// requested before any is used (chunks past the row, and the parent of a main row, read zeros
-// from an out-of-range offset), so a row costs one memory round trip.
+// holds chunks l, l + 64, ... (CPL of them) of the child and the parent row and of the norm
+// weights; all of them are requested before any is used (chunks past the row, and the parent of
+// a main row, read zeros from an out-of-range offset), so a row costs one memory round trip.
 template <int CPL>
 __device__ __forceinline__ void gate_row(const GateParams& p, int row, int lane) {
     const int i = row / p.N, n = row - i * p.N;
@@ -57,7 +73,8 @@ __device__ __forceinline__ void gate_row(const GateParams& p, int row, int lane)
     const bool need_rows = need_pair || (p.inv_rms != nullptr) || (p.xn != nullptr);
     const int nch = p.D >> 3;
     float a = 0.f, b = 0.f, ss = 0.f;
-    uint4 cv[CPL];
+    uint4 cv[CPL], wv[CPL];
+    if (p.xn && p.ln) load_norm_weights<CPL>(p.ln, p.D, lane, wv);
     if (need_rows) {
         const __amdgpu_buffer_rsrc_t rH =
             make_rsrc(p.H, static_cast<uint32_t>(static_cast<size_t>(p.nb) * p.N * p.D * 2));
@@ -108,7 +125,7 @@ __device__ __forceinline__ void gate_row(const GateParams& p, int row, int lane)
             if (k < nch) {
                 float x[8];
                 unpack8(cv[t], x);
-                o[k] = norm_chunk(x, inv, p.ln, k);
+                o[k] = p.ln ? norm_chunk_w(x, inv, wv[t]) : norm_chunk(x, inv, nullptr, k);
             }
         }
     }
@@ -373,12 +390,13 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const uint16_t* H, in
     const int nch = D >> 3;
     const __amdgpu_buffer_rsrc_t rH = make_rsrc(H, static_cast<uint32_t>(static_cast<size_t>(R) * D * 2));
     const uint32_t base = static_cast<uint32_t>(row) * D * 2;
-    uint4 cv[CPL];
+    uint4 cv[CPL], wv[CPL];
 #pragma unroll
     for (int t = 0; t < CPL; ++t) {
         const int k = lane + t * kWave;
         cv[t] = buf_load16(rH, k < nch ? base + 16 * k : kOob);
     }
+    if (ln) load_norm_weights<CPL>(ln, D, lane, wv);
     float ss = 0.f;
 #pragma unroll
     for (int t = 0; t < CPL; ++t) {
@@ -396,7 +414,7 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const uint16_t* H, in
         if (k < nch) {
             float x[8];
             unpack8(cv[t], x);
-            o[k] = norm_chunk(x, inv, ln, k);
+            o[k] = ln ? norm_chunk_w(x, inv, wv[t]) : norm_chunk(x, inv, nullptr, k);
         }
     }
 }
