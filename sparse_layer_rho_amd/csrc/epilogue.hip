@@ -63,18 +63,22 @@ __global__ __launch_bounds__(1024) void qkv_epilogue_kernel(const QkvEpiArgs a) 
         make_rsrc(a.part, static_cast<uint32_t>(static_cast<size_t>(a.splits) * a.m_cap * nq * 4));
     const uint32_t stride = static_cast<uint32_t>(a.m_cap) * nq * 4;
     const uint32_t base = (static_cast<uint32_t>(m) * nq + c1) * 4;
+    // the rotation angles (P + n) theta^(-2j/d), formed in double, are computed before the
+    // partial sums so the frequency table is read in the same round trip as the partials
+    const double pos = static_cast<double>(a.P + (ok ? row % a.N : 0));
+    double ang[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ang[e] = pos * a.inv_freq[j0 + e];
     f32x4 x1 = sum_splits<SPL>(rP, base, stride, a.splits);
     f32x4 x2 = sum_splits<SPL>(rP, base + half * 4, stride, a.splits);
     if (!ok) x1 = x2 = f32x4{1.f, 1.f, 1.f, 1.f} * __builtin_nanf("");
     float y1[4], y2[4];
     if (hh < a.Hq + a.Hkv) {
-        const double pos = static_cast<double>(a.P + (ok ? row % a.N : 0));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            // angle (P + n) theta^(-2j/d) formed in double and reduced to [-pi, pi]
-            const double ang = pos * a.inv_freq[j0 + e];
+            // angle reduced to [-pi, pi]
             const double twopi = 6.283185307179586476925286766559;
-            const float red = static_cast<float>(ang - twopi * rint(ang / twopi));
+            const float red = static_cast<float>(ang[e] - twopi * rint(ang[e] / twopi));
             float sn, cs;
             sincosf(red, &sn, &cs);
             y1[e] = x1[e] * cs - x2[e] * sn;
