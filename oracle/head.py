@@ -11,8 +11,11 @@ verification pass scores every branch's block, so the per-row greedy token is th
 reading of what the head produces for acceptance (readings listed in the design notes):
 * the final RMSNorm has a weight vector and the layer's eps;
 * no bias on the LM head; logits[r][v] = xn[r] . W_lm[v];
-* the greedy token of a row is the lowest index among its maximal logits; a token id outside
-  [0, V) embeds as a row of NaN.
+* the greedy token of a row is the lowest index among its maximal logits, where a NaN logit
+  is no candidate at all (it is neither larger nor smaller than any other value, so it can
+  never be "the maximum"); a row with no candidate (every logit NaN) has token -1 and best
+  logit NaN; +inf and -inf are ordinary candidates;
+* a token id outside [0, V) embeds as a row of NaN.
 """
 
 from __future__ import annotations
@@ -43,10 +46,18 @@ def lm_head_logits(xn, W_lm):
 
 
 def greedy_tokens(logits):
-    """Per row: the lowest index among the maximal logits, and that maximum."""
+    """Per row: the lowest index among the maximal non-NaN logits, and that maximum; a row
+    whose logits are all NaN gives token -1 and NaN."""
     logits = np.asarray(logits, dtype=np.float64)
-    mx = logits.max(axis=-1)
-    tok = np.argmax(logits == mx[..., None], axis=-1)     # first index reaching the maximum
+    cand = ~np.isnan(logits)
+    has = cand.any(axis=-1)
+    # NaN entries become -inf for the max; a row that has candidates reaches its maximum at a
+    # candidate (if that maximum is -inf, the first -inf candidate, never a former NaN)
+    filled = np.where(cand, logits, -np.inf)
+    mx = filled.max(axis=-1)
+    tok = np.argmax((filled == mx[..., None]) & cand, axis=-1)
+    tok = np.where(has, tok, -1)
+    mx = np.where(has, mx, np.nan)
     return tok.astype(np.int64), mx
 
 

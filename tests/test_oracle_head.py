@@ -84,3 +84,40 @@ def test_verify_head_designed_argmax():
         H[0, 0], H[0, 1] = float(t), 1.0       # logits ~ t v - v^2 / 2, maximal at v = t
         tok, _ = oracle.verify_head(H, np.ones(D), W, 0.0)
         assert tok[0] == t
+
+
+def test_greedy_token_nan_logits_are_never_chosen():
+    """A NaN logit is no candidate: it neither wins nor blocks a later maximum; a row of NaN has
+    no candidate (token -1, best logit NaN); +inf and -inf are ordinary candidates."""
+    nan, inf = np.nan, np.inf
+    logits = np.array([[0.5, nan, 2.0, 1.0],          # NaN before the maximum
+                       [nan, nan, nan, nan],          # no candidate
+                       [nan, -inf, -inf, nan],        # only -inf candidates: the first one
+                       [1.0, inf, nan, inf],          # +inf is the maximum, lowest index wins
+                       [nan, -3.0, nan, -3.0],        # tie after a NaN
+                       [7.0, nan, nan, nan]])         # maximum before the NaNs
+    tok, mx = oracle.greedy_tokens(logits)
+    assert tok.tolist() == [2, -1, 1, 1, 1, 0]
+    assert mx[0] == 2.0 and np.isnan(mx[1]) and mx[2] == -inf and mx[3] == inf
+    assert mx[4] == -3.0 and mx[5] == 7.0
+
+
+def test_greedy_token_nan_brute_force():
+    rng = np.random.default_rng(4)
+    logits = np.round(rng.standard_normal((60, 9)), 1)
+    logits[rng.random(logits.shape) < 0.3] = np.nan
+    logits[5] = np.nan
+    tok, mx = oracle.greedy_tokens(logits)
+    for r in range(60):
+        best = -1
+        for v in range(9):
+            x = logits[r, v]
+            if x != x:                    # NaN: skipped
+                continue
+            if best < 0 or x > logits[r, best]:
+                best = v
+        assert tok[r] == best
+        if best < 0:
+            assert np.isnan(mx[r])
+        else:
+            assert mx[r] == logits[r, best]
