@@ -159,7 +159,9 @@ int specfold_event_elapsed_ms(void* start, void* stop, float* ms);
  * Zero parent row: rho = 0 if the child row is zero too, +inf otherwise; NaN never folds.
  * Norms accumulate in fp32; sqrt and division are IEEE correctly rounded.
  *   parent_host [n_branch] host int32: par[0] = -1, 0 <= par[i] < i
- *   H      [R][D] bf16 layer-input hidden states (the raw residual stream)
+ *   H      [R][D] bf16 layer-input hidden states (the raw residual stream); when H is read
+ *          (rho_in NULL or inv_rms given) it must be smaller than 1 GB, i.e. 2 R D < 2^30
+ *          (SPECFOLD_ERR_UNSUPPORTED otherwise)
  *   rho_in [R] fp32 or NULL: when given, threshold these values instead of computing rho
  *          (H is then read only for inv_rms)
  *   rho    [R] fp32 out;  fold [R] u8 out (1 = folded)

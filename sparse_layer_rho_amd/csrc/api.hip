@@ -401,7 +401,73 @@ hipError_t run_ffn(const Dims& d, const Layout& L, const uint16_t* xn2, const ui
     return e;
 }
 
+// Checks of specfold_verify_layer's arguments other than the shape and the workspace.
+int check_layer_args(const Dims& d, const int32_t* parent_host, const specfold_layer_weights* w,
+                     const specfold_prefix_kv* prefix, const specfold_bf16* H_in, const specfold_bf16* H_out,
+                     const specfold_layer_stats* stats, ParentMap& par) {
+    int e;
+    if ((e = check_tree(parent_host, d.nb, par))) return e;
+    if (!w) return SPECFOLD_ERR_NULL;
+    if ((e = dev(w->ln1)) || (e = dev(w->w_qkv)) || (e = dev(w->w_o)) || (e = dev(w->ln2)) ||
+        (e = dev(w->w_gate_up)) || (e = dev(w->w_down)) || (e = dev(H_in)) || (e = dev(H_out)))
+        return e;
+    if (stats && ((e = opt_dev(stats->rho)) || (e = opt_dev(stats->fold)) || (e = opt_dev(stats->rec_count)) ||
+                  (e = opt_dev(stats->src_slot))))
+        return e;
+    if ((e = check_prefix(prefix, d))) return e;
+    const size_t nh = static_cast<size_t>(d.R) * d.D * 2;
+    if (overlaps(H_out, nh, H_in, nh)) return SPECFOLD_ERR_ALIAS;
+    return SPECFOLD_OK;
+}
+
+// The launch sequence of one layer on workspace ws (checked by the caller).
+int launch_layer(const Dims& d, const Layout& L, const ParentMap& par, const specfold_layer_weights* w,
+                 const specfold_prefix_kv* prefix, const specfold_bf16* H_in, float delta, specfold_bf16* H_out,
+                 specfold_layer_stats* stats, const specfold_trace* trace, void* ws, hipStream_t st) {
+    Tracer tr{trace, st};
+    GateParams g{};
+    g.H = H_in; g.par = par; g.nb = d.nb; g.N = d.N; g.D = d.D; g.delta = delta; g.rho_in = nullptr;
+    g.rho = (stats && stats->rho) ? stats->rho : at<float>(ws, L.rho);
+    g.fold = at<uint8_t>(ws, L.fold); g.inv_rms = at<float>(ws, L.inv_rms); g.eps = d.eps;
+    g.ln = w->ln1; g.xn = at<uint16_t>(ws, L.xn1); g.fold_copy = stats ? stats->fold : nullptr;
+    tr.begin();
+    hipError_t he = launch_gate(g, st);
+    tr.end();
+    if (he != hipSuccess) return hip_status(he);
+
+    // the QKV GEMM compacts the fold flags itself and publishes the recompute list and sources
+    int32_t* rec_rows = at<int32_t>(ws, L.rec_rows);
+    int32_t* rec_count = at<int32_t>(ws, L.rec_count);
+    int32_t* src_slot = at<int32_t>(ws, L.src_slot);
+    GemmArgs fc{};
+    fc.fc_fold = g.fold; fc.fc_R = d.R; fc.fc_N = d.N; fc.fc_nb = d.nb; fc.fc_par = par;
+    fc.fc_rec_rows = rec_rows; fc.fc_rec_count = rec_count; fc.fc_branch_off = at<int32_t>(ws, L.branch_off);
+    fc.fc_row_slot = at<int32_t>(ws, L.row_slot); fc.fc_src_branch = at<int32_t>(ws, L.src_branch);
+    fc.fc_src_slot = src_slot;
+    fc.fc_count_copy = stats ? stats->rec_count : nullptr;
+    fc.fc_src_slot_copy = stats ? stats->src_slot : nullptr;
+
+    uint16_t* q_c = at<uint16_t>(ws, L.q_c);
+    uint16_t* k_c = at<uint16_t>(ws, L.k_c);
+    uint16_t* v_c = at<uint16_t>(ws, L.v_c);
+    uint16_t* attn = at<uint16_t>(ws, L.attn);
+    uint16_t* h_mid = at<uint16_t>(ws, L.h_mid);
+    uint16_t* xn2 = at<uint16_t>(ws, L.xn2);
+    if ((he = run_qkv(d, L, g.xn, rec_rows, rec_count, w->w_qkv, q_c, k_c, v_c, ws, st, &tr, &fc)) != hipSuccess)
+        return hip_status(he);
+    if ((he = run_attention(d, L, q_c, k_c, v_c, rec_count, src_slot, prefix, attn, nullptr, ws, st, &tr)) !=
+        hipSuccess)
+        return hip_status(he);
+    if ((he = run_out_proj(d, L, attn, H_in, w->w_o, h_mid, w->ln2, xn2, ws, st, &tr)) != hipSuccess)
+        return hip_status(he);
+    if ((he = run_ffn(d, L, xn2, h_mid, rec_rows, rec_count, src_slot, w->w_gate_up, w->w_down, H_out, ws, st,
+                      &tr)) != hipSuccess)
+        return hip_status(he);
+    return SPECFOLD_OK;
+}
+
 }  // namespace
+
 
 // ---------------------------------------------------------------- LM head layout
 // Vocabulary pieces: the GEMM addresses its weights with 32-bit buffer offsets below 1 GB, so
@@ -511,6 +577,10 @@ int specfold_gate(const specfold_shape* shape, const int32_t* parent_host, const
     if ((e = check_tree(parent_host, shape->n_branch, par))) return e;
     const bool need_h = (rho_in == nullptr) || (inv_rms != nullptr);
     if (need_h && (e = dev(H))) return e;
+    // the gate addresses H with 32-bit buffer offsets and reads zeros past 1 GB (rows past the
+    // end, the parent of a main row), so H must stay below 1 GB
+    if (need_h && 2 * static_cast<int64_t>(shape->n_branch) * shape->block * shape->hidden >= (int64_t(1) << 30))
+        return SPECFOLD_ERR_UNSUPPORTED;
     if ((e = opt_dev(rho_in)) || (e = dev(rho)) || (e = dev(fold)) || (e = opt_dev(inv_rms))) return e;
     const size_t R = static_cast<size_t>(shape->n_branch) * shape->block;
     if (overlaps(rho, R * 4, fold, R) || (inv_rms && (overlaps(inv_rms, R * 4, rho, R * 4) ||
@@ -662,63 +732,12 @@ int specfold_verify_layer(const specfold_shape* shape, const int32_t* parent_hos
     const Dims d = dims_of(*shape);
     const Layout L = layout_of(d);
     ParentMap par;
-    if ((e = check_tree(parent_host, d.nb, par))) return e;
-    if (!w) return SPECFOLD_ERR_NULL;
-    if ((e = dev(w->ln1)) || (e = dev(w->w_qkv)) || (e = dev(w->w_o)) || (e = dev(w->ln2)) ||
-        (e = dev(w->w_gate_up)) || (e = dev(w->w_down)) || (e = dev(H_in)) || (e = dev(H_out)))
-        return e;
-    if (stats && ((e = opt_dev(stats->rho)) || (e = opt_dev(stats->fold)) || (e = opt_dev(stats->rec_count)) ||
-                  (e = opt_dev(stats->src_slot))))
-        return e;
-    if ((e = check_prefix(prefix, d))) return e;
+    if ((e = check_layer_args(d, parent_host, w, prefix, H_in, H_out, stats, par))) return e;
     if ((e = check_ws(ws, ws_bytes, L))) return e;
     const size_t nh = static_cast<size_t>(d.R) * d.D * 2;
-    if (overlaps(H_out, nh, H_in, nh) || overlaps(H_out, nh, ws, ws_bytes) || overlaps(H_in, nh, ws, ws_bytes))
-        return SPECFOLD_ERR_ALIAS;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    Tracer tr{trace, st};
-
-    GateParams g{};
-    g.H = H_in; g.par = par; g.nb = d.nb; g.N = d.N; g.D = d.D; g.delta = delta; g.rho_in = nullptr;
-    g.rho = (stats && stats->rho) ? stats->rho : at<float>(ws, L.rho);
-    g.fold = at<uint8_t>(ws, L.fold); g.inv_rms = at<float>(ws, L.inv_rms); g.eps = d.eps;
-    g.ln = w->ln1; g.xn = at<uint16_t>(ws, L.xn1); g.fold_copy = stats ? stats->fold : nullptr;
-    tr.begin();
-    hipError_t he = launch_gate(g, st);
-    tr.end();
-    if (he != hipSuccess) return hip_status(he);
-
-    // the QKV GEMM compacts the fold flags itself and publishes the recompute list and sources
-    int32_t* rec_rows = at<int32_t>(ws, L.rec_rows);
-    int32_t* rec_count = at<int32_t>(ws, L.rec_count);
-    int32_t* src_slot = at<int32_t>(ws, L.src_slot);
-    GemmArgs fc{};
-    fc.fc_fold = g.fold; fc.fc_R = d.R; fc.fc_N = d.N; fc.fc_nb = d.nb; fc.fc_par = par;
-    fc.fc_rec_rows = rec_rows; fc.fc_rec_count = rec_count; fc.fc_branch_off = at<int32_t>(ws, L.branch_off);
-    fc.fc_row_slot = at<int32_t>(ws, L.row_slot); fc.fc_src_branch = at<int32_t>(ws, L.src_branch);
-    fc.fc_src_slot = src_slot;
-    fc.fc_count_copy = stats ? stats->rec_count : nullptr;
-    fc.fc_src_slot_copy = stats ? stats->src_slot : nullptr;
-
-    uint16_t* q_c = at<uint16_t>(ws, L.q_c);
-    uint16_t* k_c = at<uint16_t>(ws, L.k_c);
-    uint16_t* v_c = at<uint16_t>(ws, L.v_c);
-    uint16_t* attn = at<uint16_t>(ws, L.attn);
-    uint16_t* h_mid = at<uint16_t>(ws, L.h_mid);
-    uint16_t* xn2 = at<uint16_t>(ws, L.xn2);
-    if ((he = run_qkv(d, L, g.xn, rec_rows, rec_count, w->w_qkv, q_c, k_c, v_c, ws, st, &tr, &fc)) != hipSuccess)
-        return hip_status(he);
-    if ((he = run_attention(d, L, q_c, k_c, v_c, rec_count, src_slot, prefix, attn, nullptr, ws, st, &tr)) !=
-        hipSuccess)
-        return hip_status(he);
-    if ((he = run_out_proj(d, L, attn, H_in, w->w_o, h_mid, w->ln2, xn2, ws, st, &tr)) != hipSuccess)
-        return hip_status(he);
-    if ((he = run_ffn(d, L, xn2, h_mid, rec_rows, rec_count, src_slot, w->w_gate_up, w->w_down, H_out, ws, st,
-                      &tr)) != hipSuccess)
-        return hip_status(he);
-    return SPECFOLD_OK;
+    if (overlaps(H_out, nh, ws, ws_bytes) || overlaps(H_in, nh, ws, ws_bytes)) return SPECFOLD_ERR_ALIAS;
+    return launch_layer(d, L, par, w, prefix, H_in, delta, H_out, stats, trace, ws, static_cast<hipStream_t>(stream));
 }
-
 
 size_t specfold_head_workspace_bytes(const specfold_shape* shape, int32_t vocab) {
     if (check_head_shape(shape, vocab)) return 0;

@@ -232,11 +232,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int M, const 
     if (g >= p.n_groups || m0 >= M) return;    // uniform: nothing to do here
     const int mrows = min(per, M - m0);
 
-    // output columns [c0, c1) of this group: the columns spread evenly over the groups, in
-    // multiples of 4 (a lane stores 4 consecutive columns)
+    // output columns [c0, c1) of this group: units of 4 columns (a lane holds 4 consecutive
+    // columns), the last unit possibly partial, spread evenly over the groups; the last group
+    // ends at ncols.  With ceil(ncols / 4) units no group is wider than the group capacity the
+    // host sized the grid for (ncols <= groups * capacity, capacity a multiple of 4).
     const int ncols = EPI == EPI_SWIGLU ? p.F : p.Nout;
-    const int c0 = static_cast<int>(static_cast<int64_t>(g) * (ncols / 4) / p.n_groups) * 4;
-    const int c1 = static_cast<int>(static_cast<int64_t>(g + 1) * (ncols / 4) / p.n_groups) * 4;
+    const int units = (ncols + 3) / 4;
+    const int c0 = static_cast<int>(static_cast<int64_t>(g) * units / p.n_groups) * 4;
+    const int c1 = min(ncols, static_cast<int>(static_cast<int64_t>(g + 1) * units / p.n_groups) * 4);
 
     // K range of this split: whole units of kSplitUnit elements (a multiple of every weight
     // stage), so the split boundaries -- and with them the order in which every output's sum
@@ -493,7 +496,11 @@ __global__ __launch_bounds__(256) void gemm_shapes_kernel(const GemmArgs pa, con
 template <int NTW, int WN, int TM, int KSUB, int NBW, int NBA, int EPI>
 hipError_t launch_shape(GemmArgs a, const GemmCfg& c, int splits, hipStream_t st) {
     using T = Tile<NTW, WN, TM, KSUB, NBW, NBA>;
+    // the partial-sum and SwiGLU epilogues store whole 4-column units; only the greedy-token
+    // epilogue takes a column count that is not a multiple of 4
+    if (EPI != EPI_ARGMAX && ((EPI == EPI_SWIGLU ? a.F : a.Nout) % 4) != 0) return hipErrorInvalidValue;
     const int groups = c.groups;
+    if (groups < 1) return hipErrorInvalidValue;
     a.n_groups = groups;
     a.min_chunks = c.min_chunks;
     a.m_chunks = (a.m_cap + T::MP - 1) / T::MP;

@@ -274,6 +274,21 @@ def layer_weights_struct(w: dict) -> LayerWeights:
                           ("ln1", "w_qkv", "w_o", "ln2", "w_gate_up", "w_down")))
 
 
+def _layer_args(shape, parent, weights, prefix_k, prefix_v, stats):
+    par = _parent_host(parent, shape.n_branch)
+    lw = weights if isinstance(weights, LayerWeights) else layer_weights_struct(weights)
+    pf = prefix_k if isinstance(prefix_k, PrefixKV) else (
+        prefix_view(prefix_k, prefix_v) if shape.prefix_len > 0 else PrefixKV())
+    R = shape.n_branch * shape.block
+    st_obj = None
+    if stats:
+        st_obj = LayerStats(_ptr(stats.get("rho"), torch.float32, R, "rho", True),
+                            _ptr(stats.get("fold"), torch.uint8, R, "fold", True),
+                            _ptr(stats.get("rec_count"), torch.int32, 1, "rec_count", True),
+                            _ptr(stats.get("src_slot"), torch.int32, R, "src_slot", True))
+    return par, lw, pf, st_obj
+
+
 def verify_layer(shape, parent, weights, prefix_k, prefix_v, H_in, delta, H_out, ws, stats=None, trace=None):
     """One folded verification layer.  ``weights`` is a dict of bf16 device tensors (or a
     prebuilt ``LayerWeights``); ``stats`` an optional dict with any of rho (f32 [R]), fold

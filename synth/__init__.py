@@ -16,6 +16,7 @@ from .inputs import (  # noqa: F401
     bf16_round,
     bf16_bits_to_f32,
     child_hidden,
+    device_layer,
     layer_weights,
     main_hidden,
     parent_tree,

@@ -83,6 +83,8 @@ class Workload:
     branch_sweep: tuple = ()
     delta_sweep: tuple = ()
     tree_sweep: tuple = ()          # tree shapes: "star", "depthK" (random, depth <= K), "chain"
+    # standard deviations of the random-init projections (w_qkv, w_o, w_gate_up, w_down)
+    weight_std: tuple = (0.02, 0.02, 0.02, 0.02)
     note: str = ""
 
 
@@ -93,9 +95,13 @@ WORKLOADS: dict[str, Workload] = {
                      tree="chain", child_law="tiny"),
     # one layer at 1.5B-class shape, B = 8 drafts, prefix 512
     "layer-1.5b": Workload("layer-1.5b", Shape(9, 32, 1536, 12, 2, 128, 8960, 512), 1, 0.1),
-    # 28-layer stack at 1.5B-class shape, prefix 2048, 8 steps with a new tree each step
+    # 28-layer stack at 1.5B-class shape, prefix 2048, 8 steps with a new tree each step.  The
+    # attention projections and the down projection are drawn with std 0.04: then a folded
+    # position's branch-specific attention output moves its residual away from the parent's
+    # layer after layer, so the per-branch divergence accumulates and positions leave the fold
+    # set as the stack deepens (with std 0.02 every layer's fold set is the first layer's)
     "stack-1.5b": Workload("stack-1.5b", Shape(9, 32, 1536, 12, 2, 128, 8960, 2048), 2, 0.1,
-                           layers=28, steps=8),
+                           layers=28, steps=8, weight_std=(0.04, 0.04, 0.02, 0.04)),
     # 28-layer stack at 7B-class shape, prefix 2048
     "stack-7b": Workload("stack-7b", Shape(9, 32, 3584, 28, 4, 128, 18944, 2048), 3, 0.1,
                          layers=28),
@@ -175,6 +181,28 @@ def layer_weights(shape: Shape, base_seed: int, layer: int, random_norm: bool = 
         "w_gate_up": lin(_T_WGU, 2 * F, D),
         "w_down": lin(_T_WDOWN, D, F),
     }
+
+
+def device_layer(torch, shape: Shape, seed: int, device, std=(0.02, 0.02, 0.02, 0.02)):
+    """Random-init weights and prefix cache of one layer drawn on the device by torch (stacks of
+    28 layers hold several GB of weights, too slow to draw on the host): projections
+    N(0, std^2) in ``layer_weights``' layout and order (w_qkv, w_o, w_gate_up, w_down), RMSNorm
+    weights 1, prefix K and V N(0, 1), all rounded to bfloat16.  One torch generator seeded
+    with ``seed`` draws them in a fixed order.  Returns (weights dict, pk, pv)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    D, F = shape.hidden, shape.ffn
+
+    def rnd(sd, *sz):
+        return (torch.randn(*sz, device=device, generator=g) * sd).to(torch.bfloat16)
+
+    w = {"w_qkv": rnd(std[0], shape.qkv_out, D), "w_o": rnd(std[1], D, shape.n_q_heads * shape.head_dim),
+         "w_gate_up": rnd(std[2], 2 * F, D), "w_down": rnd(std[3], D, F),
+         "ln1": torch.ones(D, device=device, dtype=torch.bfloat16),
+         "ln2": torch.ones(D, device=device, dtype=torch.bfloat16)}
+    pk = rnd(1.0, shape.prefix_len, shape.n_kv_heads, shape.head_dim)
+    pv = rnd(1.0, shape.prefix_len, shape.n_kv_heads, shape.head_dim)
+    return w, pk, pv
 
 
 def prefix_kv(shape: Shape, base_seed: int, layer: int) -> tuple[np.ndarray, np.ndarray]:

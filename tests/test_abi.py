@@ -185,3 +185,16 @@ def test_correction_variant_exports_and_validates():
     st = corr._lib.specfold_variant_correction_fresh(ctypes.byref(sf.make_shape(sh)), None, None, None, None, None,
                                                      None, None, None, None)
     assert st == -1
+
+
+def test_gate_rejects_inputs_of_1gb_and_more():
+    """The gate addresses H with 32-bit offsets and reads zeros past 1 GB, so an H of 1 GB or more
+    is refused before anything is launched."""
+    p, keep = _parent([-1] + [0] * 63)
+    big = _shape(n_branch=16, block=1 << 20, hidden=64)          # 2^24 rows, 2 GB
+    edge = _shape(n_branch=64, block=65536, hidden=128)          # exactly 1 GB
+    for sh in (big, edge):
+        assert L.specfold_gate(ctypes.byref(sh), p, FAKE, 0.1, None, FAKE, FAKE * 4096, None, None) == -6
+        # rho given but inv_rms asked for: H is read, so the limit still applies
+        assert L.specfold_gate(ctypes.byref(sh), p, FAKE, 0.1, 0x100000000, 0x200000000, 0x300000000,
+                               0x400000000, None) == -6

@@ -24,20 +24,34 @@ def _shape(B1, N, D):
 
 
 def _check_tokens(H, ln, W, tok_gpu, logit_gpu, eps, rows=None):
-    """Compare GPU tokens with the oracle's on `rows` (all by default)."""
+    """Compare GPU tokens with the oracle's on `rows` (all by default).  NaN logits are no
+    candidates on either side; a row without candidates must give token -1 and logit NaN."""
     rows = np.arange(H.shape[0]) if rows is None else np.asarray(rows)
     xn = oracle.final_norm(H[rows], ln, eps)
-    logits = oracle.lm_head_logits(xn, W)
+    with np.errstate(invalid="ignore"):
+        logits = oracle.lm_head_logits(xn, W)
     tok_o, mx = oracle.greedy_tokens(logits)
-    # bf16 rounding of xn (relative 2^-8) plus fp32 accumulation over D terms
-    bound = (2.0 ** -8 + H.shape[1] * 2.0 ** -24) * (np.abs(xn) @ np.abs(W).T).max(axis=1)
-    srt = np.sort(logits, axis=1)
-    gap = srt[:, -1] - srt[:, -2]
     tg = tok_gpu[rows]
+    none = tok_o < 0
+    assert np.array_equal(tg[none], tok_o[none]) and np.isnan(logit_gpu[rows][none]).all()
+    keep = ~none
+    rows, xn, logits, tok_o, mx, tg = rows[keep], xn[keep], logits[keep], tok_o[keep], mx[keep], tg[keep]
+    if rows.size == 0:
+        return 0.0
+    nanc = np.isnan(logits)
+    # bf16 rounding of xn (relative 2^-8) plus fp32 accumulation over D terms
+    with np.errstate(invalid="ignore"):
+        mag = np.nan_to_num(np.abs(xn) @ np.nan_to_num(np.abs(W)).T)
+    bound = (2.0 ** -8 + H.shape[1] * 2.0 ** -24) * mag.max(axis=1)
+    srt = np.sort(np.where(nanc, -np.inf, logits), axis=1)
+    gap = srt[:, -1] - srt[:, -2] if logits.shape[1] > 1 else np.full(rows.size, np.inf)
     clear = gap > 2 * bound
     assert np.array_equal(tg[clear], tok_o[clear])
-    assert (logits[np.arange(rows.size), tg] >= mx - 2 * bound).all()
-    assert np.all(np.abs(logit_gpu[rows] - logits[np.arange(rows.size), tg]) <= bound + 1e-6)
+    assert ((tg >= 0) & (tg < W.shape[0])).all()
+    chosen = logits[np.arange(rows.size), tg]
+    assert not np.isnan(chosen).any(), "a NaN logit was chosen"
+    assert (chosen >= mx - 2 * bound).all()
+    assert np.all(np.abs(logit_gpu[rows] - chosen) <= bound + 1e-6)
     return clear.mean()
 
 
@@ -143,3 +157,56 @@ def test_lm_head_vocab_in_pieces():
     Wh = W.float().cpu().numpy().astype(np.float64)
     _check_tokens(Hd.float().cpu().numpy().astype(np.float64), np.ones(D), Wh, got, logit.cpu().numpy(),
                   sh.rms_eps, rows)
+
+
+def _run_head(sh, H, ln, W):
+    R = sh.n_branch * sh.block
+    V = W.shape[0]
+    tok = torch.full((R,), -7, dtype=torch.int32, device=DEV)
+    logit = torch.full((R,), 7.0, device=DEV)
+    ws = sf.head_workspace(sh, V)
+    sf.lm_head(sh, dev_bf16(H), dev_bf16(ln), dev_bf16(W), tok, logit, ws)
+    torch.cuda.synchronize()
+    return tok.cpu().numpy(), logit.cpu().numpy()
+
+
+def test_lm_head_nan_logits_are_never_chosen():
+    """NaN weight rows give a NaN logit in every row (never chosen, even where the row's maximum
+    would have been); a NaN in a hidden row makes all its logits NaN (token -1, logit NaN)."""
+    sh = _shape(3, 8, 128)
+    R, D, V = 24, 128, 1000
+    rng = np.random.default_rng(21)
+    H = bf16_round(rng.standard_normal((R, D)).astype(np.float32))
+    ln = np.ones(D, np.float32)
+    W = bf16_round((0.02 * rng.standard_normal((V, D))).astype(np.float32))
+    # row 0's maximum is planted at column 123, then that weight row gets a NaN
+    W[123] = bf16_round((0.05 * H[0] / np.linalg.norm(H[0]) * np.sqrt(D)).astype(np.float32))
+    W[123, 7] = np.nan
+    W[[5, V - 1]] = np.nan
+    H[5] = np.nan
+    H[6, 17] = np.nan
+    tok, logit = _run_head(sh, H, ln, W)
+    assert tok[5] == -1 and tok[6] == -1 and np.isnan(logit[5]) and np.isnan(logit[6])
+    assert tok[0] != 123 and not np.isin(tok, [5, V - 1, 123]).any()
+    _check_tokens(H.astype(np.float64), ln.astype(np.float64), W.astype(np.float64), tok, logit, sh.rms_eps)
+
+
+@pytest.mark.parametrize("V", [1, 3, 6, 4099])
+def test_lm_head_last_columns_of_a_vocab_not_a_multiple_of_4(V):
+    """The last V % 4 columns are scored: row 0's maximum is planted in column V - 1, row 1's in
+    column V - 2 (when there is one)."""
+    sh = _shape(2, 16, 128)
+    R, D = 32, 128
+    rng = np.random.default_rng(V)
+    H = bf16_round(rng.standard_normal((R, D)).astype(np.float32))
+    ln = np.ones(D, np.float32)
+    W = bf16_round((0.01 * rng.standard_normal((V, D))).astype(np.float32))
+    W[V - 1] = bf16_round((0.05 * H[0] / np.linalg.norm(H[0]) * np.sqrt(D)).astype(np.float32))
+    if V > 1:
+        W[V - 2] = bf16_round((0.05 * H[1] / np.linalg.norm(H[1]) * np.sqrt(D)).astype(np.float32))
+    tok, logit = _run_head(sh, H, ln, W)
+    assert tok[0] == V - 1
+    if V > 1:
+        assert tok[1] == V - 2
+    assert ((tok >= 0) & (tok < V)).all() and np.isfinite(logit).all()
+    _check_tokens(H.astype(np.float64), ln.astype(np.float64), W.astype(np.float64), tok, logit, sh.rms_eps)
