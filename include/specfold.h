@@ -265,6 +265,27 @@ int specfold_verify_layer(const specfold_shape* shape, const int32_t* parent_hos
                           const specfold_trace* trace, void* ws, size_t ws_bytes,
                           void* stream);
 
+/* ---------------------------------------------------------------- the whole layer, no workspace
+ * For callers that cannot allocate device memory or pass a workspace (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): specfold_verify_layer with
+ * its workspace taken from a device array inside the library instead of `ws`.  The array holds
+ * SPECFOLD_NOALLOC_SCRATCH_BYTES on every device the library runs on, from the first call on
+ * that device (which looks its address up, with that device current) until the process ends.
+ * Nothing is allocated or freed by any call.  Arguments, outputs and errors are those of
+ * specfold_verify_layer (same kernels, same bits); a shape whose workspace
+ * (specfold_workspace_bytes) exceeds SPECFOLD_NOALLOC_SCRATCH_BYTES returns
+ * SPECFOLD_ERR_WORKSPACE before anything is enqueued.  The calling thread's current device must
+ * be the stream's device.  Every call on one device shares the array: calls that may overlap on
+ * one device (concurrent streams, threads) race and must be serialized by the caller.
+ */
+#define SPECFOLD_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+int specfold_verify_layer_noalloc(const specfold_shape* shape, const int32_t* parent_host,
+                                  const specfold_layer_weights* weights,
+                                  const specfold_prefix_kv* prefix, const specfold_bf16* H_in,
+                                  float delta, specfold_bf16* H_out, specfold_layer_stats* stats,
+                                  const specfold_trace* trace, void* stream);
+
 /* ---------------------------------------------------------------- either side of the stack
  * [SpecFold summary, App. B]: the folded kernels cover the transformer layers; the token
  * embedding before the first layer and the language-model head after the last one stay

@@ -5,7 +5,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "../../include/specfold.h"
 #include "kernels.h"
@@ -466,6 +468,40 @@ int launch_layer(const Dims& d, const Layout& L, const ParentMap& par, const spe
     return SPECFOLD_OK;
 }
 
+// ---------------------------------------------------------------- allocation-free scratch
+// specfold_verify_layer_noalloc's workspace: a file-scope device array, so callers that cannot
+// allocate (graph capture, serving loops) need no workspace.  Each device holds its own copy
+// at its own address; host code never uses the array's name as an address (on the host it is
+// only a stand-in for the symbol): the device address is looked up once per device with
+// hipGetSymbolAddress, with that device current, and kept.  Every call on a device shares the
+// array, so calls that overlap on one device race.
+__device__ __align__(256) uint8_t scratch[SPECFOLD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// the current device's copy of `scratch` (looked up on the first call on that device)
+int device_scratch(void** out) {
+    int device = -1;
+    hipError_t he = hipGetDevice(&device);
+    if (he != hipSuccess) return hip_status(he);
+    if (device < 0 || device >= kMaxDevices) return SPECFOLD_ERR_UNSUPPORTED;
+    void* p = g_scratch[device].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[device].load(std::memory_order_relaxed);
+        if (!p) {
+            he = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (he != hipSuccess) return hip_status(he);
+            if (!p || !aligned16(p)) return SPECFOLD_ERR_HIP;
+            g_scratch[device].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return SPECFOLD_OK;
+}
+
 }  // namespace
 
 
@@ -736,6 +772,22 @@ int specfold_verify_layer(const specfold_shape* shape, const int32_t* parent_hos
     if ((e = check_ws(ws, ws_bytes, L))) return e;
     const size_t nh = static_cast<size_t>(d.R) * d.D * 2;
     if (overlaps(H_out, nh, ws, ws_bytes) || overlaps(H_in, nh, ws, ws_bytes)) return SPECFOLD_ERR_ALIAS;
+    return launch_layer(d, L, par, w, prefix, H_in, delta, H_out, stats, trace, ws, static_cast<hipStream_t>(stream));
+}
+
+int specfold_verify_layer_noalloc(const specfold_shape* shape, const int32_t* parent_host,
+                                  const specfold_layer_weights* w, const specfold_prefix_kv* prefix,
+                                  const specfold_bf16* H_in, float delta, specfold_bf16* H_out,
+                                  specfold_layer_stats* stats, const specfold_trace* trace, void* stream) {
+    int e = check_layer_shape(shape);
+    if (e) return e;
+    const Dims d = dims_of(*shape);
+    const Layout L = layout_of(d);
+    ParentMap par;
+    if ((e = check_layer_args(d, parent_host, w, prefix, H_in, H_out, stats, par))) return e;
+    if (L.total > SPECFOLD_NOALLOC_SCRATCH_BYTES) return SPECFOLD_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if ((e = device_scratch(&ws))) return e;
     return launch_layer(d, L, par, w, prefix, H_in, delta, H_out, stats, trace, ws, static_cast<hipStream_t>(stream));
 }
 

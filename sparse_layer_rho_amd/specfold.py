@@ -34,8 +34,10 @@ EXPORTS = (
     "specfold_stage_name", "specfold_event_create", "specfold_event_destroy",
     "specfold_event_elapsed_ms", "specfold_gate", "specfold_compact", "specfold_resolve_sources",
     "specfold_sparse_qkv", "specfold_folded_attention", "specfold_out_proj", "specfold_sparse_ffn",
-    "specfold_verify_layer", "specfold_embed", "specfold_head_workspace_bytes", "specfold_lm_head",
+    "specfold_verify_layer", "specfold_verify_layer_noalloc", "specfold_embed", "specfold_head_workspace_bytes",
+    "specfold_lm_head",
 )
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class SpecfoldError(RuntimeError):
@@ -102,6 +104,8 @@ def _load():
         "specfold_lm_head": ([pS, P, P, P, ctypes.c_int32, P, P, P, SZ, P], ctypes.c_int),
         "specfold_verify_layer": ([pS, P, ctypes.POINTER(LayerWeights), ctypes.POINTER(PrefixKV), P, F32, P,
                                    ctypes.POINTER(LayerStats), ctypes.POINTER(Trace), P, SZ, P], ctypes.c_int),
+        "specfold_verify_layer_noalloc": ([pS, P, ctypes.POINTER(LayerWeights), ctypes.POINTER(PrefixKV), P, F32, P,
+                                           ctypes.POINTER(LayerStats), ctypes.POINTER(Trace), P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -287,6 +291,20 @@ def _layer_args(shape, parent, weights, prefix_k, prefix_v, stats):
                             _ptr(stats.get("rec_count"), torch.int32, 1, "rec_count", True),
                             _ptr(stats.get("src_slot"), torch.int32, R, "src_slot", True))
     return par, lw, pf, st_obj
+
+
+def verify_layer_noalloc(shape, parent, weights, prefix_k, prefix_v, H_in, delta, H_out, stats=None, trace=None):
+    """``verify_layer`` without a workspace: the library's own device scratch array serves as
+    workspace (see ``specfold_verify_layer_noalloc``); calls on one device must not overlap."""
+    sh = make_shape(shape)
+    R, D = shape.n_branch * shape.block, shape.hidden
+    par, lw, pf, st_obj = _layer_args(shape, parent, weights, prefix_k, prefix_v, stats)
+    status = _lib.specfold_verify_layer_noalloc(
+        ctypes.byref(sh), ctypes.c_void_p(par.data_ptr()), ctypes.byref(lw), ctypes.byref(pf),
+        _ptr(H_in, torch.bfloat16, R * D, "H_in"), float(delta), _ptr(H_out, torch.bfloat16, R * D, "H_out"),
+        ctypes.byref(st_obj) if st_obj is not None else None, ctypes.byref(trace) if trace is not None else None,
+        _stream())
+    _check(status, "specfold_verify_layer_noalloc")
 
 
 def verify_layer(shape, parent, weights, prefix_k, prefix_v, H_in, delta, H_out, ws, stats=None, trace=None):
