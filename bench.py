@@ -38,8 +38,12 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=200,
+                    help="steps per timed graph replay (exactly this many; the median of --rounds replays is reported)")
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rounds", type=int, default=5, help="timed replays of the K-step graph (median reported)")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="layer workloads: skip the 28-layer stack leg (stack-1.5b) of the default line")
     ap.add_argument("--warmup-seconds", type=float, default=1.0,
                     help="keep replaying (untimed) at least this long before timing, so clocks have ramped")
     ap.add_argument("--workload", default="layer-1.5b")
@@ -104,8 +108,8 @@ def main():
     print(f"[bench] inputs ready in {time.time() - t0:.1f}s: {args.workload}, R={R}, "
           f"weights {sh.weight_bytes_bf16() / 1e6:.1f} MB/layer", file=sys.stderr, flush=True)
 
-    # weight copies: cold rotates through enough of them to overflow the 256 MB cache
-    n_copies = 1 if args.regime == "warm" else max(2, int(np.ceil(600e6 / sh.weight_bytes_bf16())))
+    # weight copies for the cold regime: enough of them to overflow the 256 MB cache
+    n_copies = max(2, int(np.ceil(600e6 / sh.weight_bytes_bf16())))
     copies = [w0] + [{k: v.clone() for k, v in w0.items()} for _ in range(n_copies - 1)]
     lws = [sf.layer_weights_struct(c) for c in copies]
     pf = sf.prefix_view(pk, pv)
@@ -126,53 +130,28 @@ def main():
                           "M": int(stats["rec_count"].item())}
 
     # ---------------------------------------------------------------- graph-timed throughput
-    def timed(delta, steps, warmup):
-        # one captured graph runs a full rotation of the weight copies
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            for k in range(n_copies):
-                step(delta, k)
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for k in range(n_copies):
-                step(delta, k)
-        reps = max(1, steps // n_copies)
-        wreps = max(1, warmup // n_copies)
-        t_w = time.perf_counter()
-        done = 0
-        while done < wreps or time.perf_counter() - t_w < args.warmup_seconds:
-            g.replay()
-            done += 1
-            if done % 64 == 0:
-                torch.cuda.synchronize()
-        torch.cuda.synchronize()
-        # every replay reproduces the eager result bit for bit
-        if not torch.equal(H_out.view(torch.int16), results[delta]["H_out"].view(torch.int16)):
-            raise RuntimeError("graph replay differs from the eager call")
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        wall0 = time.perf_counter()
-        e0.record()
-        for _ in range(reps):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
-        ms = e0.elapsed_time(e1)
-        n = reps * n_copies
-        if not torch.equal(H_out.view(torch.int16), results[delta]["H_out"].view(torch.int16)):
-            raise RuntimeError("graph replay differs from the eager call")
-        del g
-        return {"steps": n, "ms_per_step": ms / n, "wall_ms_per_step": 1e3 * wall / n,
-                "branch_tokens_per_s": R * n / (ms / 1e3)}
+    # exactly K = --steps layer steps per graph replay; consecutive steps read consecutive weight
+    # copies (cold: the copies total more than the 256 MB Infinity Cache, so every step streams
+    # its weights from HBM; warm: one copy, resident in the cache)
+    K = max(1, args.steps)
 
-    folded = timed(wl.delta, args.steps, args.warmup)
-    dense = timed(0.0, args.steps, args.warmup)
-    print(f"[bench] folded {folded['ms_per_step'] * 1e3:.1f} us/step, dense {dense['ms_per_step'] * 1e3:.1f} "
-          f"us/step", file=sys.stderr, flush=True)
+    def timed(delta, copies_used):
+        def check():
+            if not torch.equal(H_out.view(torch.int16), results[delta]["H_out"].view(torch.int16)):
+                raise RuntimeError("graph replay differs from the eager call")
+        fns = [lambda k=k: step(delta, k % copies_used) for k in range(K)]
+        ms = time_graph(torch, fns, rounds=args.rounds, warmup_replays=-(-args.warmup // K),
+                        warmup_s=args.warmup_seconds, check=check)
+        med = float(np.median(ms))
+        return {"steps": K, "ms_per_step": med / K, "round_ms_per_step": [round(x / K, 5) for x in ms],
+                "branch_tokens_per_s": R * K / (med / 1e3)}
+
+    cold_f, cold_d = timed(wl.delta, n_copies), timed(0.0, n_copies)
+    warm_f, warm_d = timed(wl.delta, 1), timed(0.0, 1)
+    folded, dense = (warm_f, warm_d) if args.regime == "warm" else (cold_f, cold_d)
+    print(f"[bench] cold: folded {cold_f['ms_per_step'] * 1e3:.1f} us/step, dense {cold_d['ms_per_step'] * 1e3:.1f}; "
+          f"warm: folded {warm_f['ms_per_step'] * 1e3:.1f}, dense {warm_d['ms_per_step'] * 1e3:.1f}",
+          file=sys.stderr, flush=True)
 
     # ---------------------------------------------------------------- per-launch durations (events)
     def stage_times(delta):
@@ -208,37 +187,65 @@ def main():
                 "tflops": round(2 * M * 2 * F * D / (gu_us * 1e-6) / 1e12, 1)}
 
     # per-kernel fractions of the vendor peaks (folded step, event-timed launches): MFMA for the
-    # GEMMs and attention, HBM for every kernel; bytes are what each step must read and write
-    # (weights, activations, outputs), not split-K partials or chunk states
-    def kernel_pct(st, m):
+    # contractions (GEMMs, attention), HBM for every kernel.  Bytes are what each step must move
+    # (weights, activations, outputs, prefix cache), not split-K partials or chunk states; the
+    # epilogue kernels have no algorithmic bytes of their own beyond the rows they write.  Cold,
+    # a contraction of intensity I = flops/bytes cannot exceed I * 8 TB/s of MFMA work, i.e. a
+    # fraction mfma_cap_cold = min(1, I * HBM peak / MFMA peak) of the MFMA peak.
+    def kernel_work(name, m):
         d, Hq, Hkv, P, N = sh.head_dim, sh.n_q_heads, sh.n_kv_heads, sh.prefix_len, sh.block
         Nq, Do = (Hq + 2 * Hkv) * d, Hq * d
-        rows = {
-            "gate_rmsnorm": (st["gate_rmsnorm"], 0, 2 * R * D + 2 * R * D + 9 * R),
-            "qkv_gemm_compact_resolve": (st["qkv_gemm_compact_resolve"], 2 * m * Nq * D, 2 * Nq * D + 2 * m * D + 2 * m * Nq),
-            "attention": (st["attn_prefix"] + st["attn_block_merge"], 4 * d * Hq * (P * m + N * R),
-                          4 * P * Hkv * d + 2 * m * Nq + 2 * R * Do),
-            "oproj_gemm": (st["oproj_gemm"], 2 * R * Do * D, 2 * Do * D + 2 * R * Do + 2 * R * D),
-            "gate_up_swiglu_gemm": (st["gate_up_swiglu_gemm"], 2 * m * 2 * F * D, gu_bytes),
-            "down_gemm": (st["down_gemm"], 2 * m * F * D, 2 * F * D + 2 * m * F + 2 * m * D),
+        table = {
+            "gate_rmsnorm": (0, 2 * R * D + 2 * D + 2 * R * D + 9 * R),
+            "qkv_gemm_compact_resolve": (2 * m * Nq * D, 2 * Nq * D + 2 * m * D + 2 * m * Nq),
+            "qkv_rope_epilogue": (0, 2 * m * Nq),
+            "attention": (4 * d * Hq * (P * m + N * R), 4 * P * Hkv * d + 2 * m * Nq + 2 * R * Do),
+            "oproj_gemm": (2 * R * Do * D, 2 * Do * D + 2 * R * Do + 2 * R * D),
+            "oproj_residual_rmsnorm": (0, 2 * R * D + 4 * R * D),
+            "gate_up_swiglu_gemm": (2 * m * 2 * F * D, 2 * 2 * F * D + 2 * m * D + 2 * m * F),
+            "down_gemm": (2 * m * F * D, 2 * F * D + 2 * m * F + 2 * m * D),
+            "down_inherit_epilogue": (0, 4 * R * D),
         }
+        return table.get(name)
+
+    def kernel_pct(st, m):
+        st = dict(st)
+        attn = sum(v for k, v in st.items() if k.startswith("attn"))
+        st = {k: v for k, v in st.items() if not k.startswith("attn")}
+        st["attention"] = attn
         out_ = {}
-        for k, (us, flops, byts) in rows.items():
+        for k, us in st.items():
+            w_ = kernel_work(k, m)
+            if w_ is None:
+                continue
+            flops, byts = w_
             sec = us * 1e-6
-            out_[k] = {"us": round(us, 2), "mfma_frac": round(flops / sec / (BF16_PEAK_TFLOPS * 1e12), 4) if flops else None,
-                       "hbm_frac": round(byts / sec / (HBM_PEAK_GBS * 1e9), 4)}
+            row = {"us": round(us, 2), "hbm_frac": round(byts / sec / (HBM_PEAK_GBS * 1e9), 4), "bytes": byts}
+            if flops:
+                row["mfma_frac"] = round(flops / sec / (BF16_PEAK_TFLOPS * 1e12), 4)
+                row["mfma_cap_cold"] = round(min(1.0, flops / byts * HBM_PEAK_GBS * 1e9 / (BF16_PEAK_TFLOPS * 1e12)), 4)
+            out_[k] = row
         return out_
 
-    # whole-layer roofline at the vendor peaks: sum over kernels of max(bytes/BW, flops/MFMA)
+    # whole-layer roofline at the vendor peaks: sum over the contractions and the gate of
+    # max(bytes / BW, flops / MFMA) (the epilogues' rows are written by the kernels they follow in
+    # a fused design)
     def layer_roof_us(m):
-        Nq, Do = (sh.n_q_heads + 2 * sh.n_kv_heads) * sh.head_dim, sh.n_q_heads * sh.head_dim
         t = 0.0
-        for flops, byts in ((2 * m * Nq * D, 2 * Nq * D), (2 * R * Do * D, 2 * Do * D),
-                            (2 * m * 2 * F * D, 2 * 2 * F * D), (2 * m * F * D, 2 * F * D),
-                            (4 * sh.head_dim * sh.n_q_heads * (sh.prefix_len * m + sh.block * R),
-                             4 * sh.prefix_len * sh.n_kv_heads * sh.head_dim)):
+        for k in ("gate_rmsnorm", "qkv_gemm_compact_resolve", "attention", "oproj_gemm", "gate_up_swiglu_gemm",
+                  "down_gemm"):
+            flops, byts = kernel_work(k, m)
             t += max(flops / (BF16_PEAK_TFLOPS * 1e12), byts / (HBM_PEAK_GBS * 1e9))
         return t * 1e6
+
+    def regime(f, d_):
+        return {"value": round(f["branch_tokens_per_s"], 1), "ms_per_step": round(f["ms_per_step"], 5),
+                "round_ms_per_step": f["round_ms_per_step"],
+                "dense_value": round(d_["branch_tokens_per_s"], 1), "dense_ms_per_step": round(d_["ms_per_step"], 5),
+                "dense_round_ms_per_step": d_["round_ms_per_step"],
+                "speedup_vs_dense": round(d_["ms_per_step"] / f["ms_per_step"], 4),
+                "layer_roofline_frac": {"folded": round(layer_roof_us(M) / (f["ms_per_step"] * 1e3), 4),
+                                        "dense": round(layer_roof_us(R) / (d_["ms_per_step"] * 1e3), 4)}}
 
     out = {
         "metric": METRIC,
@@ -256,7 +263,9 @@ def main():
         "config": {"workload": args.workload, "hidden": D, "n_q_heads": sh.n_q_heads, "n_kv_heads": sh.n_kv_heads,
                    "head_dim": sh.head_dim, "ffn": F, "block": sh.block, "drafts": sh.n_branch - 1,
                    "prefix": sh.prefix_len, "delta": wl.delta, "rows": R, "regime": args.regime,
-                   "weight_copies": n_copies, "timing": "HIP graph replay, events", "parallelism": "single GPU"},
+                   "weight_copies": n_copies if args.regime == "cold" else 1,
+                   "timing": f"HIP graph of exactly {K} steps, median of {args.rounds} event-timed replays",
+                   "parallelism": "single GPU"},
         "speedup_vs_dense": round(dense["ms_per_step"] / folded["ms_per_step"], 4),
         "dense": {"value": round(dense["branch_tokens_per_s"], 1), "ms_per_step": round(dense["ms_per_step"], 5),
                   "rec_rows": results[0.0]["M"]},
@@ -264,12 +273,17 @@ def main():
         "rec_rows": M,
         "layer_roofline_frac": {"folded": round(layer_roof_us(M) / (folded["ms_per_step"] * 1e3), 4),
                                 "dense": round(layer_roof_us(R) / (dense["ms_per_step"] * 1e3), 4)},
+        "regimes": {"cold": regime(cold_f, cold_d), "warm": regime(warm_f, warm_d)},
         "roofline": roofline,
         "kernel_frac_of_peak": kernel_pct(st_f, M),
+        "kernel_frac_of_peak_dense": kernel_pct(st_d, R),
         "stages_us": {"folded": {k: round(v, 2) for k, v in st_f.items()},
                       "dense": {k: round(v, 2) for k, v in st_d.items()}},
-        "wall_ms_per_step": round(folded["wall_ms_per_step"], 5),
     }
+
+    if not args.no_stack and args.workload == "layer-1.5b":
+        # the 28-layer stack at the same model shape (prefix 2048, 8 steps with a new tree each)
+        out["stack"] = stack_measure(torch, sf, WORKLOADS["stack-1.5b"], 0, 0, args, dev)
 
     if not args.no_gate_flat:
         out["gate_flat"] = gate_flat_leg(torch, sf, dev)
@@ -440,9 +454,11 @@ def measured_traffic():
     return rec.get("traffic_bytes") if rec.get("source_sha256") == h.hexdigest() else None
 
 
-def graph_time(torch, fns, reps, warmup_s=0.5):
-    """Capture fns (a list of callables launching on the current stream) in one graph; replay it,
-    untimed for warmup_s, then `reps` times between events.  Returns ms per replay."""
+def time_graph(torch, fns, rounds=5, warmup_replays=1, warmup_s=0.5, check=None, reps=1):
+    """Capture fns (callables launching on the current stream) in one HIP graph, replay it untimed
+    for at least `warmup_replays` replays and `warmup_s` seconds, then time `rounds` rounds of
+    `reps` replays, each round between its own pair of events.  Returns ms per replay of every
+    round.  check() runs after the warm-up and after the timed rounds."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -454,19 +470,32 @@ def graph_time(torch, fns, reps, warmup_s=0.5):
     with torch.cuda.graph(g):
         for f in fns:
             f()
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < warmup_s:
+    t0, done = time.perf_counter(), 0
+    while done < warmup_replays or time.perf_counter() - t0 < warmup_s:
         g.replay()
-        torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        g.replay()
-    e1.record()
+        done += 1
+        if done % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    if check:
+        check()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(rounds)]
+    for e0, e1 in ev:
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    if check:
+        check()
     del g
-    return ms
+    return [e0.elapsed_time(e1) / reps for e0, e1 in ev]
+
+
+def graph_time(torch, fns, reps, warmup_s=0.5):
+    """ms per replay of a graph of fns: the median of 5 rounds of `reps` replays."""
+    import statistics
+    return statistics.median(time_graph(torch, fns, rounds=5, warmup_s=warmup_s, reps=max(1, reps)))
 
 
 def gate_flat_leg(torch, sf, dev):
@@ -481,8 +510,9 @@ def gate_flat_leg(torch, sf, dev):
     fold = torch.empty(R, dtype=torch.uint8, device=dev)
     # 8 back-to-back calls per graph replay, so the replay's own launch is not in the figure
     ms = graph_time(torch, [lambda: sf.gate(sh, parent, H, 0.1, rho, fold)] * 8, reps=10) / 8
-    # algorithmic bytes: every draft row reads itself and its parent row; rho + fold written
-    gbytes = (R - sh.block) * 2 * D * 2 + R * 5
+    # algorithmic bytes: every row of H read once (a parent row serves all its children), rho and
+    # fold written
+    gbytes = R * D * 2 + R * 5
     del H
     sc = Shape(64, 262144, 64, 4, 2, 16, 128, 0)
     Rc = sc.rows
@@ -494,8 +524,8 @@ def gate_flat_leg(torch, sf, dev):
     ms_c = graph_time(torch, [lambda: sf.compact(sc, fold_c, rec_rows, rec_count, branch_off, row_slot)] * 8,
                       reps=10) / 8
     M = int(rec_count.item())
-    # algorithmic bytes: the flags (read twice: count and scan) and the row map, list and offsets written
-    cbytes = 2 * Rc + 4 * Rc + 4 * M + 4 * (sc.n_branch + 1)
+    # algorithmic bytes: the flags read once; the row map, list and offsets written
+    cbytes = Rc + 4 * Rc + 4 * M + 4 * (sc.n_branch + 1)
     return {"gate": {"rows": R, "hidden": D, "us": round(ms * 1e3, 2), "bytes": gbytes,
                      "gbs": round(gbytes / (ms * 1e-3) / 1e9, 1),
                      "hbm_frac": round(gbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
@@ -504,60 +534,30 @@ def gate_flat_leg(torch, sf, dev):
                         "hbm_frac": round(cbytes / (ms_c * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
 
 
-def _device_layer(torch, sh, seed, dev):
-    """Random-init layer weights on the device: N(0, 0.02^2) rounded to bf16, RMSNorm weights 1,
-    prefix K/V N(0, 1) -- the generator's distributions, drawn by torch for speed."""
-    g = torch.Generator(device=dev)
-    g.manual_seed(seed)
-    D, F = sh.hidden, sh.ffn
-    nq = (sh.n_q_heads + 2 * sh.n_kv_heads) * sh.head_dim
-
-    def rnd(*shape, std=0.02):
-        return (torch.randn(*shape, device=dev, generator=g) * std).to(torch.bfloat16)
-    w = {"w_qkv": rnd(nq, D), "w_o": rnd(D, sh.n_q_heads * sh.head_dim), "w_gate_up": rnd(2 * F, D),
-         "w_down": rnd(D, F), "ln1": torch.ones(D, device=dev, dtype=torch.bfloat16),
-         "ln2": torch.ones(D, device=dev, dtype=torch.bfloat16)}
-    pk = rnd(sh.prefix_len, sh.n_kv_heads, sh.head_dim, std=1.0)
-    pv = rnd(sh.prefix_len, sh.n_kv_heads, sh.head_dim, std=1.0)
-    return w, pk, pv
-
-
-def stack_bench(args, wl):
+def stack_measure(torch, sf, wl, layers, steps, args, dev, with_head=False):
     """A full verification pass through an L-layer stack, S steps with a new draft tree each step:
-    per-branch residual streams carried across layers, every layer re-gating on its own input."""
+    per-branch residual streams carried across layers, every layer re-gating on its own input.
+    One graph holds the S steps; the median of --rounds timed replays is reported."""
     import numpy as np
-    import torch
 
-    from sparse_layer_rho_amd import specfold as sf
-    from synth import bf16_round, layer_weights, prefix_kv, step_inputs
+    from synth import bf16_round, device_layer, step_inputs
 
     sh = wl.shape
     R, D = sh.rows, sh.hidden
-    L = args.layers if args.layers > 1 else wl.layers
-    S = args.stack_steps if args.stack_steps > 0 else max(1, wl.steps)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
-    def to_dev(x):
-        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev).to(torch.bfloat16)
-
+    L = layers if layers > 1 else wl.layers
+    S = steps if steps > 0 else max(1, wl.steps)
     t0 = time.time()
-    # layer 0 from the seeded host generator the tests use; the others drawn on the device with
-    # the same distributions
-    w0_host = layer_weights(sh, wl.base_seed, 0)
-    pk0_h, pv0_h = prefix_kv(sh, wl.base_seed, 0)
-    layers = [({k: to_dev(v) for k, v in w0_host.items()}, to_dev(pk0_h), to_dev(pv0_h))]
-    for l in range(1, L):
-        layers.append(_device_layer(torch, sh, 1000 * wl.base_seed + l, dev))
-    lws = [sf.layer_weights_struct(w) for w, _, _ in layers]
-    pfs = [sf.prefix_view(pk, pv) for _, pk, pv in layers]
-    steps = []
+    # every layer's weights and prefix cache drawn on the device (synth.device_layer)
+    layer_list = [device_layer(torch, sh, 1000 * wl.base_seed + l, dev, wl.weight_std) for l in range(L)]
+    lws = [sf.layer_weights_struct(w) for w, _, _ in layer_list]
+    pfs = [sf.prefix_view(pk, pv) for _, pk, pv in layer_list]
+    steps_in = []
     for s in range(S):
         inp = step_inputs(sh, wl.base_seed, s, tree=wl.tree, child_law=wl.child_law)
-        steps.append((inp["parent"], bf16_round(inp["H"].astype(np.float32)), to_dev(
-            bf16_round(inp["H"].astype(np.float32)).reshape(R, D))))
+        Hs = bf16_round(inp["H"].astype(np.float32))
+        steps_in.append((inp["parent"], torch.from_numpy(Hs.reshape(R, D)).to(dev).to(torch.bfloat16)))
     torch.cuda.synchronize()
-    print(f"[bench] stack ready in {time.time() - t0:.1f}s: {args.workload}, {L} layers, {S} steps, "
+    print(f"[bench] stack ready in {time.time() - t0:.1f}s: {wl.name}, {L} layers, {S} steps, "
           f"{L * sh.weight_bytes_bf16() / 1e9:.2f} GB of weights", file=sys.stderr, flush=True)
 
     ws = sf.new_workspace(sh)
@@ -568,7 +568,7 @@ def stack_bench(args, wl):
     cnt = torch.zeros((L, 4), dtype=torch.int32, device=dev)
 
     def run_step(s, delta):
-        parent, _, H0 = steps[s]
+        parent, H0 = steps_in[s]
         x = H0
         for l in range(L):
             y = buf[l % 2]
@@ -579,53 +579,65 @@ def stack_bench(args, wl):
 
     res = {}
     for delta in (wl.delta, 0.0):
-        out0 = None
-        Ms, ff = [], []
+        Ms, ff, outs = [], [], []
         for s in range(S):
             x = run_step(s, delta)
             torch.cuda.synchronize()
-            if s == 0:
-                out0 = x.clone()
+            outs.append(x.clone())
             Ms.append(cnt[:, 0].cpu().numpy().copy())
-            f = fold[:, :R].cpu().numpy().reshape(L, sh.n_branch, sh.block)[:, 1:].mean(axis=(1, 2))
-            ff.append(f)
-        reps = max(1, args.steps // (S * 4))
-        ms = graph_time(torch, [lambda s=s: run_step(s, delta) for s in range(S)], reps=reps)
-        res[delta] = {"ms_per_step": ms / S, "M": np.mean(Ms, axis=0), "fold": np.mean(ff, axis=0)}
-        print(f"[bench] delta {delta}: {ms / S:.3f} ms per stack step", file=sys.stderr, flush=True)
+            ff.append(fold[:, :R].cpu().numpy().reshape(L, sh.n_branch, sh.block)[:, 1:].mean(axis=(1, 2)))
+        last = outs[-1]
 
-    # the folded pass's output must be finite in every layer's stream (its parity with the
-    # oracle, layer by layer and across the stack, is checked by the tests)
-    x = run_step(0, wl.delta)
-    torch.cuda.synchronize()
-    finite = bool(torch.isfinite(x.float()).all().item())
+        def check(last=last, delta=delta):
+            if not torch.equal(buf[(L - 1) % 2].view(torch.int16), last.view(torch.int16)):
+                raise RuntimeError(f"stack graph replay differs from the eager pass (delta {delta})")
+        ms = time_graph(torch, [lambda s=s, delta=delta: run_step(s, delta) for s in range(S)], rounds=args.rounds,
+                        warmup_s=args.warmup_seconds, check=check)
+        med = float(np.median(ms))
+        res[delta] = {"ms_per_step": med / S, "round_ms_per_step": [round(x / S, 5) for x in ms],
+                      "M": np.mean(Ms, axis=0), "fold": np.mean(ff, axis=0),
+                      "finite": all(bool(torch.isfinite(o.float()).all().item()) for o in outs)}
+        print(f"[bench] stack delta {delta}: {med / S:.3f} ms per step", file=sys.stderr, flush=True)
 
     f, d = res[wl.delta], res[0.0]
     out = {
-        "metric": METRIC,
-        "value": round(R / (f["ms_per_step"] * 1e-3), 1),
-        "unit": "branch-tokens/s",
-        "n_gpus": 1,
-        "steps": S,
-        "ms_per_step": round(f["ms_per_step"], 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded random weights and prefix KV per layer, parent-linked draft hidden states per step)",
-        "config": {"workload": args.workload, "layers": L, "hidden": D, "n_q_heads": sh.n_q_heads,
-                   "n_kv_heads": sh.n_kv_heads, "ffn": sh.ffn, "block": sh.block, "drafts": sh.n_branch - 1,
-                   "prefix": sh.prefix_len, "delta": wl.delta, "rows": R, "timing": "HIP graph replay, events",
-                   "parallelism": "single GPU"},
+        "workload": wl.name, "layers": L, "steps": S,
+        "value": round(R / (f["ms_per_step"] * 1e-3), 1), "unit": "branch-tokens/s",
+        "ms_per_step": round(f["ms_per_step"], 5), "round_ms_per_step": f["round_ms_per_step"],
+        "dense_value": round(R / (d["ms_per_step"] * 1e-3), 1), "dense_ms_per_step": round(d["ms_per_step"], 5),
+        "dense_round_ms_per_step": d["round_ms_per_step"],
         "speedup_vs_dense": round(d["ms_per_step"] / f["ms_per_step"], 4),
-        "dense": {"value": round(R / (d["ms_per_step"] * 1e-3), 1), "ms_per_step": round(d["ms_per_step"], 5)},
         "us_per_layer": {"folded": round(1e3 * f["ms_per_step"] / L, 2), "dense": round(1e3 * d["ms_per_step"] / L, 2)},
+        "rec_rows_mean": round(float(np.mean(f["M"])), 1),
         "rec_rows_per_layer": [round(float(v), 1) for v in f["M"]],
         "fold_fraction_drafts_per_layer": [round(float(v), 4) for v in f["fold"]],
-        "finite_output": finite,
+        "finite_output": bool(f["finite"] and d["finite"]),
+        "config": {"hidden": D, "n_q_heads": sh.n_q_heads, "n_kv_heads": sh.n_kv_heads, "ffn": sh.ffn,
+                   "block": sh.block, "drafts": sh.n_branch - 1, "prefix": sh.prefix_len, "delta": wl.delta,
+                   "rows": R, "weight_std": list(wl.weight_std),
+                   "timing": f"HIP graph of the {S} steps x {L} layers, median of {args.rounds} event-timed replays"},
     }
-    if args.with_head:
-        out["pass_with_head"] = pass_leg(torch, sf, sh, wl, args, steps, lws, pfs, ws, buf, fold, cnt, L, S, dev)
+    if with_head:
+        out["pass_with_head"] = pass_leg(torch, sf, sh, wl, args, [(p, None, H) for p, H in steps_in], lws, pfs, ws,
+                                         buf, fold, cnt, L, S, dev)
+    return out
+
+
+def stack_bench(args, wl):
+    """--workload stack-*: the stack's own JSON line."""
+    import torch
+
+    from sparse_layer_rho_amd import specfold as sf
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    st = stack_measure(torch, sf, wl, args.layers, args.stack_steps, args, dev, with_head=args.with_head)
+    out = {"metric": METRIC, "value": st["value"], "unit": "branch-tokens/s", "n_gpus": 1, "steps": st["steps"],
+           "ms_per_step": st["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16",
+           "data": "synthetic (seeded random weights and prefix KV per layer, parent-linked draft hidden states per step)",
+           "config": {"workload": args.workload, **st["config"], "layers": st["layers"], "parallelism": "single GPU"},
+           "speedup_vs_dense": st["speedup_vs_dense"], "stack": st}
     print(json.dumps(out), flush=True)
 
 
@@ -824,10 +836,17 @@ def tree_bench(args, wl):
 
 
 def cpu_baseline_leg(sh, wl, parent, H_host, w_host, pk_h, pv_h, gpu_res, seconds):
-    """Time the CPU oracle on the bench's first input (bounded), and check the GPU's output of that
-    same step against it (teacher-forced on the GPU's mask within 1e-4 of delta)."""
+    """Time the CPU oracle on the bench's first input and check the GPU's output of that same step
+    against it (teacher-forced on the GPU's mask within 1e-4 of delta).  Timings are the median
+    of 3 passes after one warm-up: with the BLAS threads the host gives this process, with one
+    thread, and the dense pass (delta 0); `seconds` bounds each of the three (fewer passes are
+    timed when one pass takes longer)."""
+    import contextlib
+    import platform
+    import statistics
+
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle
 
@@ -841,17 +860,42 @@ def cpu_baseline_leg(sh, wl, parent, H_host, w_host, pk_h, pv_h, gpu_res, second
     err = float(np.linalg.norm(got - ref["H_out"]) / np.linalg.norm(ref["H_out"]))
     verified = ok_mask and err <= 2e-2 and gpu_res["M"] == ref["rec_rows"].size
 
-    n, t0 = 0, time.perf_counter()
-    while True:
-        oracle.verify_layer(H, parent, w_host, pk_h, pv_h, wl.delta, sh)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or n >= 200:
-            break
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    cpu = {"value": round(sh.rows * n / el, 1), "unit": "branch-tokens/s", "cores": threads, "kind": "oracle",
-           "sample": f"{n} float64 oracle passes of the bench's first step ({sh.rows} rows) in {el:.1f}s",
-           "seconds": round(el, 2)}
+    def timed(delta, limit):
+        ctx = threadpool_limits(limits=limit) if limit else contextlib.nullcontext()
+        with ctx:
+            threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+            t0 = time.perf_counter()
+            oracle.verify_layer(H, parent, w_host, pk_h, pv_h, delta, sh)       # warm-up
+            first = time.perf_counter() - t0
+            n = 3 if 3 * first <= seconds else 1
+            ts = []
+            for _ in range(n):
+                t0 = time.perf_counter()
+                oracle.verify_layer(H, parent, w_host, pk_h, pv_h, delta, sh)
+                ts.append(time.perf_counter() - t0)
+        return statistics.median(ts), n, threads
+
+    t_all, n_all, threads = timed(wl.delta, None)
+    t_one, n_one, _ = timed(wl.delta, 1)
+    t_dense, n_dense, _ = timed(0.0, None)
+    model = platform.processor() or ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = sorted({f"{p.get('internal_api')} {p.get('version')}" for p in threadpool_info()
+                   if p.get("user_api") == "blas"})
+    cpu = {"value": round(sh.rows / t_all, 1), "unit": "branch-tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"median of {n_all} float64 oracle passes (after one warm-up) of the bench's first step "
+                     f"({sh.rows} rows, delta {wl.delta}) on {threads} BLAS threads",
+           "seconds_per_pass": round(t_all, 4),
+           "one_thread": {"value": round(sh.rows / t_one, 1), "seconds_per_pass": round(t_one, 4), "passes": n_one},
+           "dense_delta0": {"value": round(sh.rows / t_dense, 1), "seconds_per_pass": round(t_dense, 4),
+                            "passes": n_dense, "speedup_of_folding": round(t_dense / t_all, 4)},
+           "cpu_model": model, "host_cpus_available": len(os.sched_getaffinity(0)), "blas": blas}
     return cpu, {"ok": bool(verified), "rel_l2": round(err, 6), "mask_match_outside_band": ok_mask}
 
 
