@@ -521,7 +521,8 @@ def gate_flat_leg(torch, sf, dev):
     rec_count = torch.empty(1, dtype=torch.int32, device=dev)
     branch_off = torch.empty(sc.n_branch + 1, dtype=torch.int32, device=dev)
     row_slot = torch.empty(Rc, dtype=torch.int32, device=dev)
-    ms_c = graph_time(torch, [lambda: sf.compact(sc, fold_c, rec_rows, rec_count, branch_off, row_slot)] * 8,
+    cws = sf.compact_workspace(sc, dev)
+    ms_c = graph_time(torch, [lambda: sf.compact(sc, fold_c, rec_rows, rec_count, branch_off, row_slot, ws=cws)] * 8,
                       reps=10) / 8
     M = int(rec_count.item())
     # algorithmic bytes: the flags read once; the row map, list and offsets written

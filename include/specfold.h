@@ -180,9 +180,18 @@ int specfold_gate(const specfold_shape* shape, const int32_t* parent_host,
  *   rec_count  [1] int32 out: M
  *   branch_off [n_branch + 1] int32 out
  *   row_slot   [R] int32 out: slot of row r in rec_rows, -1 when folded
+ *   ws         device scratch of specfold_compact_workspace_bytes(shape) bytes, any contents
+ *              (may be NULL when that is 0).  Past 8192 rows the scan is one pass over 32768-row
+ *              tiles with a decoupled look-back between them; its status words live here and
+ *              are cleared by the call itself.  One workspace must not serve two calls that may
+ *              run concurrently.
  */
 int specfold_compact(const specfold_shape* shape, const uint8_t* fold, int32_t* rec_rows,
-                     int32_t* rec_count, int32_t* branch_off, int32_t* row_slot, void* stream);
+                     int32_t* rec_count, int32_t* branch_off, int32_t* row_slot, void* ws, size_t ws_bytes,
+                     void* stream);
+/* Bytes of workspace specfold_compact needs for this shape (0 if the shape is invalid or needs
+   none: up to 8192 rows one workgroup scans them all). */
+size_t specfold_compact_workspace_bytes(const specfold_shape* shape);
 
 /* ---------------------------------------------------------------- step 3: fold sources
  * [SpecFold summary, App. B and §A.3]: each folded position follows its fold chain to the

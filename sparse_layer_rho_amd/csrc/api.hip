@@ -631,24 +631,41 @@ int specfold_gate(const specfold_shape* shape, const int32_t* parent_host, const
     return hip_status(launch_gate(p, static_cast<hipStream_t>(stream)));
 }
 
+size_t specfold_compact_workspace_bytes(const specfold_shape* shape) {
+    if (check_rows_shape(shape, kMaxGateBlock) != SPECFOLD_OK) return 0;
+    return compact_workspace_bytes(shape->n_branch * shape->block);
+}
+
 int specfold_compact(const specfold_shape* shape, const uint8_t* fold, int32_t* rec_rows,
-                     int32_t* rec_count, int32_t* branch_off, int32_t* row_slot, void* stream) {
+                     int32_t* rec_count, int32_t* branch_off, int32_t* row_slot, void* ws, size_t ws_bytes,
+                     void* stream) {
     int e = check_rows_shape(shape, kMaxGateBlock);
     if (e) return e;
     if ((e = dev(fold)) || (e = dev(rec_rows)) || (e = dev(rec_count)) || (e = dev(branch_off)) ||
         (e = dev(row_slot)))
         return e;
     const size_t R = static_cast<size_t>(shape->n_branch) * shape->block;
+    const size_t need = compact_workspace_bytes(static_cast<int>(R));
+    if (need > 0) {
+        if (!ws || ws_bytes < need) return SPECFOLD_ERR_WORKSPACE;
+        if (!aligned16(ws)) return SPECFOLD_ERR_ALIGN;
+    }
     const size_t nbo = (static_cast<size_t>(shape->n_branch) + 1) * 4;
     if (overlaps(rec_rows, R * 4, row_slot, R * 4) || overlaps(rec_rows, R * 4, branch_off, nbo) ||
         overlaps(row_slot, R * 4, branch_off, nbo) || overlaps(rec_count, 4, rec_rows, R * 4) ||
         overlaps(rec_count, 4, row_slot, R * 4) || overlaps(rec_count, 4, branch_off, nbo) ||
         overlaps(fold, R, rec_rows, R * 4) || overlaps(fold, R, row_slot, R * 4))
         return SPECFOLD_ERR_ALIAS;
+    if (need > 0) {
+        const void* outs[5] = {fold, rec_rows, rec_count, branch_off, row_slot};
+        const size_t sizes[5] = {R, R * 4, 4, nbo, R * 4};
+        for (int k = 0; k < 5; ++k)
+            if (overlaps(ws, need, outs[k], sizes[k])) return SPECFOLD_ERR_ALIAS;
+    }
     CompactParams p{};
     p.fold = fold; p.R = static_cast<int>(R); p.N = shape->block; p.nb = shape->n_branch;
     p.rec_rows = rec_rows; p.rec_count = rec_count; p.branch_off = branch_off; p.row_slot = row_slot;
-    return hip_status(launch_compact(p, static_cast<hipStream_t>(stream)));
+    return hip_status(launch_compact(p, need > 0 ? ws : nullptr, static_cast<hipStream_t>(stream)));
 }
 
 int specfold_resolve_sources(const specfold_shape* shape, const int32_t* parent_host,

@@ -10,8 +10,8 @@
 //
 // Compaction [SpecFold summary, App. B]: an exclusive scan of the recompute flags in row order
 // (wave ballots + a cross-wave scan in LDS) writes the global list, the per-branch offsets and
-// the inverse map row -> slot.  Past 8192 rows the scan runs over tiles in three passes (count,
-// tile offsets, scan from the offset), so large inputs use the whole GPU.
+// the inverse map row -> slot.  Past 8192 rows one pass over 32768-row tiles with a decoupled
+// look-back between them, so large inputs use the whole GPU and read the flags once.
 //
 // Sources [SpecFold summary, App. B and §A.3]: every row walks its fold chain up the parent map
 // (at most n_branch steps; branch 0 always terminates) -- rows are independent, so one
@@ -63,47 +63,55 @@ __device__ __forceinline__ void load_norm_weights(const uint16_t* ln, int D, int
 }
 
 // One wave computes rho, fold, inv_rms (and optionally the normalised row) of one row.  Lane l
-// holds chunks l, l + 64, ... (CPL of them) of the child and the parent row and of the norm
-// weights; all of them are requested before any is used (chunks past the row, and the parent of
-// a main row, read zeros from an out-of-range offset), so a row costs one memory round trip.
+// holds chunks l, l + 64, ... (CPL of them) of the child and the parent row; all of them are
+// requested before any is used (chunks past the row, and the parent of a main row, read zeros
+// from an out-of-range offset), so a row costs one memory round trip.  The loads of a row are
+// issued by gate_issue and consumed by gate_finish, so a wave can request its next row before it
+// reduces the current one.
 template <int CPL>
-__device__ __forceinline__ void gate_row(const GateParams& p, int row, int lane) {
+struct GateRow {
+    uint4 cv[CPL], pv[CPL];
+};
+
+template <int CPL>
+__device__ __forceinline__ void gate_issue(const GateParams& p, __amdgpu_buffer_rsrc_t rH, int row, int lane,
+                                           GateRow<CPL>& g) {
     const int i = row / p.N, n = row - i * p.N;
     const bool need_pair = (i > 0) && (p.rho_in == nullptr);
     const bool need_rows = need_pair || (p.inv_rms != nullptr) || (p.xn != nullptr);
     const int nch = p.D >> 3;
-    float a = 0.f, b = 0.f, ss = 0.f;
-    uint4 cv[CPL], wv[CPL];
-    if (p.xn && p.ln) load_norm_weights<CPL>(p.ln, p.D, lane, wv);
-    if (need_rows) {
-        const __amdgpu_buffer_rsrc_t rH =
-            make_rsrc(p.H, static_cast<uint32_t>(static_cast<size_t>(p.nb) * p.N * p.D * 2));
-        const uint32_t cb = static_cast<uint32_t>(row) * p.D * 2;
-        const uint32_t pb = need_pair ? static_cast<uint32_t>(p.par.p[i] * p.N + n) * p.D * 2 : kOob;
-        uint4 pv[CPL];
+    const uint32_t cb = need_rows ? static_cast<uint32_t>(row) * p.D * 2 : kOob;
+    const uint32_t pb = need_pair ? static_cast<uint32_t>(p.par.p[i] * p.N + n) * p.D * 2 : kOob;
 #pragma unroll
-        for (int t = 0; t < CPL; ++t) {
-            const int k = lane + t * kWave;
-            cv[t] = buf_load16(rH, k < nch ? cb + 16 * k : kOob);
-            pv[t] = buf_load16(rH, k < nch ? pb + 16 * k : kOob);
-        }
-#pragma unroll
-        for (int t = 0; t < CPL; ++t) {
-            float x[8], yv[8];
-            unpack8(cv[t], x);
-            unpack8(pv[t], yv);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float d = x[e] - yv[e];
-                ss += x[e] * x[e];
-                a += d * d;
-                b += yv[e] * yv[e];
-            }
-        }
-        a = wave_sum(a);
-        b = wave_sum(b);
-        ss = wave_sum(ss);
+    for (int t = 0; t < CPL; ++t) {
+        const int k = lane + t * kWave;
+        g.cv[t] = buf_load16(rH, k < nch ? cb + 16 * k : kOob);
+        g.pv[t] = buf_load16(rH, k < nch ? pb + 16 * k : kOob);
     }
+}
+
+template <int CPL>
+__device__ __forceinline__ void gate_finish(const GateParams& p, int row, int lane, const GateRow<CPL>& g,
+                                            const uint4 (&wv)[CPL]) {
+    const int i = row / p.N;
+    const int nch = p.D >> 3;
+    float a = 0.f, b = 0.f, ss = 0.f;
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+        float x[8], yv[8];
+        unpack8(g.cv[t], x);
+        unpack8(g.pv[t], yv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float d = x[e] - yv[e];
+            ss += x[e] * x[e];
+            a += d * d;
+            b += yv[e] * yv[e];
+        }
+    }
+    a = wave_sum(a);
+    b = wave_sum(b);
+    ss = wave_sum(ss);
     const float inv = 1.0f / sqrtf(ss / static_cast<float>(p.D) + p.eps);
     if (lane == 0) {
         float r = 0.f;
@@ -124,17 +132,47 @@ __device__ __forceinline__ void gate_row(const GateParams& p, int row, int lane)
             const int k = lane + t * kWave;
             if (k < nch) {
                 float x[8];
-                unpack8(cv[t], x);
+                unpack8(g.cv[t], x);
                 o[k] = p.ln ? norm_chunk_w(x, inv, wv[t]) : norm_chunk(x, inv, nullptr, k);
             }
         }
     }
 }
 
+// Grid of one wave per row, 4 waves per workgroup.  Rows are visited in windows of `win`
+// positions, branch-major inside a window: consecutive waves read consecutive (contiguous) rows
+// of one branch, and a child's parent row -- same positions, an earlier branch -- is read by the
+// same window's waves shortly before or after, so the second read is an L2 hit.  With at least 8
+// windows, window w's workgroups all sit on XCD w % 8 (the dispatcher deals workgroup ids
+// round-robin to the 8 XCDs), so the hit is in that XCD's own L2.  Measured on 9 x 16384 rows of
+// 1536 (453 MB): 82 us with 128-position windows on one XCD each, 86-90 us in plain window order,
+// 98 us position-major (one workgroup per position), 123 us branch-major over whole branches,
+// where every parent row is read again far from its first read.
+constexpr int kGateWin = 128;
+
 template <int CPL>
-__global__ __launch_bounds__(256) void gate_kernel(const GateParams p) {
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row < p.nb * p.N) gate_row<CPL>(p, row, threadIdx.x & (kWave - 1));
+__global__ __launch_bounds__(256) void gate_kernel(const GateParams p, int win, int n_win, int xcd_map) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar index math
+    const int wg_per_win = p.nb * win / 4;              // the host keeps win a multiple of 4
+    int g = static_cast<int>(blockIdx.x);
+    if (xcd_map) {
+        const int x = g & 7, k = g >> 3;
+        g = ((k / wg_per_win) * 8 + x) * wg_per_win + k % wg_per_win;
+    }
+    const int w = g * 4 + wave;                         // wave index in (window, branch, position) order
+    const int per_win = p.nb * win;                     // (fewer than 2^31 waves: R <= 2^24, win <= 128)
+    const int wi = w / per_win, rem = w - wi * per_win;
+    const int i = rem / win, n = wi * win + (rem - i * win);
+    if (wi >= n_win || n >= p.N) return;
+    uint4 wv[CPL];
+    if (p.xn && p.ln) load_norm_weights<CPL>(p.ln, p.D, lane, wv);
+    const __amdgpu_buffer_rsrc_t rH =
+        make_rsrc(p.H, static_cast<uint32_t>(static_cast<size_t>(p.nb) * p.N * p.D * 2));
+    GateRow<CPL> r;
+    const int row = __builtin_amdgcn_readfirstlane(i * p.N + n);
+    gate_issue<CPL>(p, rH, row, lane, r);
+    gate_finish<CPL>(p, row, lane, r, wv);
 }
 
 // Exclusive scan of the recompute flags of rows [r_begin, r_end) in ascending order, starting
@@ -179,97 +217,76 @@ __global__ __launch_bounds__(1024) void compact_kernel(const CompactParams p) {
     }
 }
 
-// Large inputs: tiles of kCompactTile rows.  Pass 1 counts each tile's recompute rows into the
-// first row_slot entry of the tile (scratch that pass 3 overwrites), pass 2 turns the counts
-// into exclusive offsets, pass 3 scans every tile from its offset.  A tile is 32768 rows, so a
-// 2^24-row input is 512 tiles: one workgroup per tile stays resident on the CUs at once.
-constexpr int kCompactTile = 32768;
-constexpr int kScatterSub = 8192;               // rows of one scan step of pass 3 (8 per thread)
+// Large inputs: one pass over the flags with a look-back in the manner of Merrill and Garland's
+// single-pass scan ("Single-pass Parallel Prefix Scan with Decoupled Look-back", 2016).  Each
+// workgroup takes a ticket -- tiles are numbered in the order workgroups start, so a tile only ever
+// waits for tiles that are already running -- loads its tile's flags, counts them and publishes the
+// count; it then reads every predecessor's published count (at most 512 tiles at 2^24 rows, one
+// batch of independent loads rather than a walk that waits for inclusive prefixes to ripple
+// down) and scatters its rows from their sum.  The status words and the ticket counter live in
+// the caller's workspace and are cleared by a fill kernel just before (a fill kernel, not a memset
+// node, so the sequence can be captured in a graph).  Status word: 2 flag bits (0 empty, 1 count
+// published) above a 30-bit count (R <= 2^24).
+// Measured on 2^24 rows (30 % recomputed): 31.6 us for the clear and scan kernels, against 15.7 us
+// for the bare traffic (flags read, row map written, no scan) and 21.7 us for the kernel with
+// every store removed: the ticket (3.8 us), the look-back (3.5 us) and the loads run before any
+// store can start, and with every tile resident at once nothing overlaps them.  Tiles of 8192 or
+// 16384 rows (more rounds) took 82 and 41 us (the ticket and look-back grow with the tile count);
+// 65536 rows 31.9 us.
+constexpr int kLookbackThreads = 1024;          // threads per workgroup of the look-back scan
+constexpr int kLookbackSteps = 4;               // steps of 8 rows per thread in one tile
+constexpr int kCompactTile = 8 * kLookbackThreads * kLookbackSteps;   // rows per tile
 constexpr int kSmallCompact = 8192;             // up to this many rows one workgroup scans them all
+constexpr uint32_t kStAgg = 1u << 30, kStFlags = 3u << 30;
+// A predecessor always publishes, so the wait below ends; the bound only guarantees that no
+// wave can spin forever whatever happens (about a second of polling); a tile that gives up marks
+// the run in its status area (word 1) and takes offset 0.
+constexpr int kSpinLimit = 1 << 22;
 
-__global__ __launch_bounds__(1024) void compact_count_kernel(const CompactParams p) {
-    __shared__ int s_tot[16];
-    const int tile = blockIdx.x, tid = threadIdx.x;
-    const int r0 = tile * kCompactTile;
-    // thread t counts the kRowsPerThread rows from r0 + kRowsPerThread t: 16-byte loads, or byte
-    // loads where the array ends inside them (the flags are bytes; nothing past R is read)
-    constexpr int kRowsPerThread = kCompactTile / 1024;
-    static_assert(kRowsPerThread % 16 == 0, "whole 16-byte loads");
-    const int rt = r0 + kRowsPerThread * tid;
-    int cnt = 0;
-    if (rt + kRowsPerThread <= p.R) {
-        uint4 v[kRowsPerThread / 16];
-#pragma unroll
-        for (int c = 0; c < kRowsPerThread / 16; ++c) v[c] = *reinterpret_cast<const uint4*>(p.fold + rt + 16 * c);
-#pragma unroll
-        for (int c = 0; c < kRowsPerThread / 16; ++c) {
-            const uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) cnt += ((w[q] >> (8 * b)) & 0xffu) == 0 ? 1 : 0;
-        }
-    } else {
-        for (int r = rt; r < p.R && r < rt + kRowsPerThread; ++r) cnt += p.fold[r] == 0 ? 1 : 0;
-    }
-    cnt = static_cast<int>(wave_sum(static_cast<float>(cnt)));
-    if ((tid & 63) == 0) s_tot[tid >> 6] = cnt;
-    __syncthreads();
-    if (tid == 0) {
-        int tot = 0;
-        for (int w = 0; w < 16; ++w) tot += s_tot[w];
-        p.row_slot[r0] = tot;
-    }
+// Workgroup barrier that orders LDS only: waits for this wave's LDS operations, not for its
+// global stores (__syncthreads also drains every outstanding store, so a loop that stores and
+// then synchronizes on LDS would wait for its stores' write acknowledgements at every step).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__global__ __launch_bounds__(1024) void compact_offsets_kernel(const CompactParams p, int ntiles) {
-    __shared__ int s_wave[16];
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-    // thread t owns tiles 2t, 2t+1 (ntiles <= 2048); a wave scan with shuffles, then the waves'
-    // totals from LDS
-    const int a = 2 * tid < ntiles ? p.row_slot[2 * tid * kCompactTile] : 0;
-    const int b = 2 * tid + 1 < ntiles ? p.row_slot[(2 * tid + 1) * kCompactTile] : 0;
-    int incl = a + b;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int t = __shfl_up(incl, d, kWave);
-        if (lane >= d) incl += t;
-    }
-    if (lane == kWave - 1) s_wave[wave] = incl;
-    __syncthreads();
-    int woff = 0, total = 0;
-    for (int w = 0; w < 16; ++w) {
-        const int t = s_wave[w];
-        woff += w < wave ? t : 0;
-        total += t;
-    }
-    const int excl = woff + incl - (a + b);
-    if (2 * tid < ntiles) p.row_slot[2 * tid * kCompactTile] = excl;
-    if (2 * tid + 1 < ntiles) p.row_slot[(2 * tid + 1) * kCompactTile] = excl + a;
-    if (tid == 0) {
-        p.rec_count[0] = total;
-        p.branch_off[p.nb] = total;
-    }
+__device__ __forceinline__ uint32_t ld_status(const uint32_t* a) {
+    return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_status(uint32_t* a, uint32_t v) {
+    __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Pass 3: the tile is four steps of 8192 rows; in each, thread t owns the 8 consecutive rows
-// 8t .. 8t+7 of the step.  Every step's flags (one 8-byte load per thread) and the tile's offset
-// are requested at once (one memory round trip per tile); then, step by step, a
-// workgroup-wide exclusive scan of the per-thread counts places the thread's recompute rows,
-// the thread writes its 8 row -> slot entries as two 16-byte stores, and the step's list is
-// gathered in LDS and written out in consecutive stores.
-__global__ __launch_bounds__(1024) void compact_scatter_kernel(const CompactParams p) {
-    static_assert(kScatterSub == 8 * 1024 && kCompactTile % kScatterSub == 0, "8 rows per thread and step");
-    constexpr int kSteps = kCompactTile / kScatterSub;
-    __shared__ int s_wave[2][16];
-    __shared__ int s_base;
-    __shared__ int s_list[kScatterSub];            // one step's recompute rows, in slot order
+__global__ __launch_bounds__(1024) void compact_clear_kernel(uint32_t* state, int n) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) state[i] = 0;
+}
+
+// The tile is kSteps steps of 8192 rows; in each, thread t owns the 8 consecutive rows 8t .. 8t+7
+// of the step.  Every step's flags (one 8-byte load per thread) are requested at once.  One
+// workgroup-wide exclusive scan of the per-thread counts of all steps at once (wave scans, the
+// wave totals of every step through LDS, one barrier) places every recompute row; the tile's
+// count is published and the offset looked back; then every thread writes its 8 row -> slot
+// entries of each step as two 16-byte stores, and each step's list is gathered in LDS (two
+// buffers, so one barrier per step) and written out in consecutive stores.
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(8, 8))) void compact_lookback_kernel(const CompactParams p, uint32_t* state, int ntiles) {
+    constexpr int kSub = 8 * THREADS;              // rows of one step
+    constexpr int kSteps = kLookbackSteps;
+    constexpr int kTile = kSub * kSteps;
+    constexpr int kWaves = THREADS / kWave;
+    __shared__ int s_wave[kSteps][kWaves];         // each step's per-wave totals
+    __shared__ int s_tile, s_base;
+    __shared__ int s_list[2][kSub];                // two steps' recompute rows, in slot order
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-    const int r0 = blockIdx.x * kCompactTile;
+    if (tid == 0) s_tile = static_cast<int>(atomicAdd(state, 1u));
+    __syncthreads();
+    const int tile = s_tile;
+    if (tile >= ntiles) return;                    // (never: the grid has one workgroup per tile)
+    const int r0 = tile * kTile;
     uint32_t bits[kSteps];                         // bit b: row rt + b exists and is recomputed
 #pragma unroll
     for (int q = 0; q < kSteps; ++q) {
-        const int rt = r0 + q * kScatterSub + 8 * tid;
+        const int rt = r0 + q * kSub + 8 * tid;
         bits[q] = 0;
         if (rt + 8 <= p.R) {
             const uint2 v = *reinterpret_cast<const uint2*>(p.fold + rt);
@@ -282,32 +299,92 @@ __global__ __launch_bounds__(1024) void compact_scatter_kernel(const CompactPara
             for (int b = 0; b < 8 && rt + b < p.R; ++b) bits[q] |= (p.fold[rt + b] == 0 ? 1u : 0u) << b;
         }
     }
-    if (tid == 0) s_base = p.row_slot[r0];         // the tile's offset (pass 2)
+    // inclusive scans over the wave, one per step
+    int incl[kSteps];
+#pragma unroll
+    for (int q = 0; q < kSteps; ++q) incl[q] = __popc(bits[q]);
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+#pragma unroll
+        for (int q = 0; q < kSteps; ++q) {
+            const int t = __shfl_up(incl[q], d, kWave);
+            if (lane >= d) incl[q] += t;
+        }
+    }
+    if (lane == kWave - 1) {
+#pragma unroll
+        for (int q = 0; q < kSteps; ++q) s_wave[q][wave] = incl[q];
+    }
     __syncthreads();
-    int base = s_base;
+    // local[q]: tile-local slot of the thread's first recompute row of step q; step_off[q]: the
+    // tile-local slot of step q's first recompute row
+    // (each step's wave totals are scanned across the first kWaves lanes of every wave, so a
+    // thread holds two values per step instead of all the totals)
+    int local[kSteps], step_off[kSteps + 1];
+    step_off[0] = 0;
 #pragma unroll
     for (int q = 0; q < kSteps; ++q) {
-        const int rt = r0 + q * kScatterSub + 8 * tid;
-        const int cnt = __popc(bits[q]);
-        int incl = cnt;                            // inclusive scan over the wave
+        const int v = lane < kWaves ? s_wave[q][lane] : 0;
+        int sc = v;
 #pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const int t = __shfl_up(incl, d, kWave);
-            if (lane >= d) incl += t;
+        for (int d = 1; d < kWaves; d <<= 1) {
+            const int t = __shfl_up(sc, d, kWave);
+            if (lane >= d) sc += t;
         }
-        if (lane == kWave - 1) s_wave[q & 1][wave] = incl;
-        __syncthreads();                           // (two buffers: step q+1 writes the other)
-        int local = 0, tot = 0;
-        for (int w = 0; w < 16; ++w) {
-            const int t = s_wave[q & 1][w];
-            local += w < wave ? t : 0;
-            tot += t;
+        const int before = __shfl(sc - v, wave, kWave), tot = __shfl(sc, kWaves - 1, kWave);
+        local[q] = step_off[q] + before + incl[q] - __popc(bits[q]);
+        step_off[q + 1] = step_off[q] + tot;
+    }
+    const int cnt = step_off[kSteps];
+    if (tid == 0) st_status(state + 4 + tile, kStAgg | static_cast<uint32_t>(cnt));
+    // look-back by wave 0: every predecessor's count is read in one batch of independent loads
+    // (lane l reads tiles l, l + 64, ...; at most 64 * kBatch tiles per batch) and summed; a
+    // predecessor that has not published yet is read again
+    if (wave == 0) {
+        constexpr int kBatch = 8;
+        const uint32_t* status = state + 4;
+        int base = 0, spins = 0;
+        for (int j0 = 0; j0 < tile; j0 += kBatch * kWave) {
+            uint32_t sw[kBatch];
+            while (true) {
+                bool missing = false;
+#pragma unroll
+                for (int b = 0; b < kBatch; ++b) {
+                    const int k = j0 + b * kWave + lane;
+                    sw[b] = k < tile ? ld_status(status + k) : kStAgg;
+                }
+#pragma unroll
+                for (int b = 0; b < kBatch; ++b) missing |= (sw[b] & kStFlags) == 0;
+                if (!__ballot(missing)) break;
+                if (++spins > kSpinLimit) {
+                    if (lane == 0) st_status(state + 1, 1u);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+            int v = 0;
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) v += static_cast<int>(sw[b] & ~kStFlags);
+#pragma unroll
+            for (int d = 32; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
+            base += v;
         }
-        local += incl - cnt;                       // step-local index of the thread's first recompute row
-        const int step_base = base;
-        int slot = base + local;                   // slot of the thread's first recompute row
-        base += tot;
+        if (lane == 0) {
+            s_base = base;
+            if (tile == ntiles - 1) {
+                p.rec_count[0] = base + cnt;
+                p.branch_off[p.nb] = base + cnt;
+            }
+        }
+    }
+    __syncthreads();
+    const int base = s_base;
+#pragma unroll
+    for (int q = 0; q < kSteps; ++q) {
+        const int rt = r0 + q * kSub + 8 * tid;
         const uint32_t bq = bits[q];
+        const int lq = local[q] - step_off[q];     // step-local index of the thread's first recompute row
+        const int slot = base + local[q];          // slot of the thread's first recompute row
         // branch starts among the thread's rows: one division per step, not one per row
         if (rt < p.R) {
             int br = (rt + p.N - 1) / p.N;
@@ -317,10 +394,10 @@ __global__ __launch_bounds__(1024) void compact_scatter_kernel(const CompactPara
         int rs[8];
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
-            const int lb = local + __popc(bq & ((1u << b) - 1u));
+            const int k = __popc(bq & ((1u << b) - 1u));
             const bool rec = (bq >> b) & 1u;
-            rs[b] = rec ? slot - local + lb : -1;
-            if (rec) s_list[lb] = rt + b;
+            rs[b] = rec ? slot + k : -1;
+            if (rec) s_list[q & 1][lq + k] = rt + b;
         }
         if (rt + 8 <= p.R) {
             int4* dst = reinterpret_cast<int4*>(p.row_slot + rt);
@@ -329,10 +406,12 @@ __global__ __launch_bounds__(1024) void compact_scatter_kernel(const CompactPara
         } else {
             for (int b = 0; b < 8 && rt + b < p.R; ++b) p.row_slot[rt + b] = rs[b];
         }
-        // the step's list leaves LDS in consecutive 4-byte stores (coalesced over each wave)
-        __syncthreads();
-        for (int e = tid; e < tot; e += 1024) p.rec_rows[step_base + e] = s_list[e];
-        __syncthreads();                           // the list is read before the next step refills it
+        // the step's list leaves LDS in consecutive 4-byte stores (coalesced over each wave); the
+        // other buffer takes the next step, and this one is refilled only two steps on, after the
+        // next step's barrier
+        lds_barrier();
+        const int tot = step_off[q + 1] - step_off[q];
+        for (int e = tid; e < tot; e += THREADS) p.rec_rows[base + step_off[q] + e] = s_list[q & 1][e];
     }
 }
 
@@ -443,10 +522,15 @@ hipError_t launch_gate(const GateParams& p, hipStream_t st) {
     if (R <= 0) return hipSuccess;
     const int cpl = ((p.D >> 3) + kWave - 1) / kWave;
     if (cpl > kMaxChunksPerLane) return hipErrorInvalidValue;
-    const dim3 grid((R + 3) / 4), block(256);
+    const int win = p.N >= kGateWin ? kGateWin : (p.N + 3) / 4 * 4;
+    const int n_win = (p.N + win - 1) / win;
+    const int xcd_map = n_win >= 8 ? 1 : 0;
+    const long windows = xcd_map ? (n_win + 7) / 8 * 8 : n_win;
+    const long waves = windows * p.nb * win;
+    const dim3 grid(static_cast<unsigned>(waves / 4)), block(256);
     switch (cpl) {
 #define SPECFOLD_GATE_CASE(C) \
-    case C: hipLaunchKernelGGL(gate_kernel<C>, grid, block, 0, st, p); break;
+    case C: hipLaunchKernelGGL(gate_kernel<C>, grid, block, 0, st, p, win, n_win, xcd_map); break;
         SPECFOLD_GATE_CASE(1) SPECFOLD_GATE_CASE(2) SPECFOLD_GATE_CASE(3) SPECFOLD_GATE_CASE(4)
         SPECFOLD_GATE_CASE(5) SPECFOLD_GATE_CASE(6) SPECFOLD_GATE_CASE(7) SPECFOLD_GATE_CASE(8)
         SPECFOLD_GATE_CASE(9) SPECFOLD_GATE_CASE(10)
@@ -455,16 +539,23 @@ hipError_t launch_gate(const GateParams& p, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_compact(const CompactParams& p, hipStream_t st) {
+size_t compact_workspace_bytes(int R) {
+    if (R <= kSmallCompact) return 0;
+    const size_t ntiles = (static_cast<size_t>(R) + kCompactTile - 1) / kCompactTile;
+    return (4 + ntiles) * 4;
+}
+
+hipError_t launch_compact(const CompactParams& p, void* ws, hipStream_t st) {
     if (p.R <= kSmallCompact) {
         hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, st, p);
         return hipGetLastError();
     }
     const int ntiles = (p.R + kCompactTile - 1) / kCompactTile;
-    if (ntiles > 2048) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(compact_count_kernel, dim3(ntiles), dim3(1024), 0, st, p);
-    hipLaunchKernelGGL(compact_offsets_kernel, dim3(1), dim3(1024), 0, st, p, ntiles);
-    hipLaunchKernelGGL(compact_scatter_kernel, dim3(ntiles), dim3(1024), 0, st, p);
+    if (!ws) return hipErrorInvalidValue;
+    uint32_t* state = static_cast<uint32_t*>(ws);
+    hipLaunchKernelGGL(compact_clear_kernel, dim3(1), dim3(1024), 0, st, state, 4 + ntiles);
+    hipLaunchKernelGGL(compact_lookback_kernel<kLookbackThreads>, dim3(ntiles), dim3(kLookbackThreads), 0, st, p, state,
+                       ntiles);
     return hipGetLastError();
 }
 

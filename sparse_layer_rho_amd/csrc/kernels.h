@@ -42,7 +42,9 @@ struct ResolveParams {
 };
 
 hipError_t launch_gate(const GateParams& p, hipStream_t st);
-hipError_t launch_compact(const CompactParams& p, hipStream_t st);
+// ws: compact_workspace_bytes(R) bytes (may be NULL when that is 0), any contents
+size_t compact_workspace_bytes(int R);
+hipError_t launch_compact(const CompactParams& p, void* ws, hipStream_t st);
 hipError_t launch_resolve(const ResolveParams& p, hipStream_t st);
 
 // xn[r] = X[r] * s_r * ln (bf16), s_r = inv_rms[r] or, when inv_rms is NULL, 1/sqrt(mean(X[r]^2)+eps)

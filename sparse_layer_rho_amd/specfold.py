@@ -32,7 +32,8 @@ MAX_BLOCK = 64
 EXPORTS = (
     "specfold_version", "specfold_status_str", "specfold_last_error", "specfold_workspace_bytes", "specfold_stage_count",
     "specfold_stage_name", "specfold_event_create", "specfold_event_destroy",
-    "specfold_event_elapsed_ms", "specfold_gate", "specfold_compact", "specfold_resolve_sources",
+    "specfold_event_elapsed_ms", "specfold_gate", "specfold_compact", "specfold_compact_workspace_bytes",
+    "specfold_resolve_sources",
     "specfold_sparse_qkv", "specfold_folded_attention", "specfold_out_proj", "specfold_sparse_ffn",
     "specfold_verify_layer", "specfold_verify_layer_noalloc", "specfold_embed", "specfold_head_workspace_bytes",
     "specfold_lm_head",
@@ -92,7 +93,8 @@ def _load():
         "specfold_event_destroy": ([P], ctypes.c_int),
         "specfold_event_elapsed_ms": ([P, P, ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
         "specfold_gate": ([pS, P, P, F32, P, P, P, P, P], ctypes.c_int),
-        "specfold_compact": ([pS, P, P, P, P, P, P], ctypes.c_int),
+        "specfold_compact": ([pS, P, P, P, P, P, P, SZ, P], ctypes.c_int),
+        "specfold_compact_workspace_bytes": ([pS], SZ),
         "specfold_resolve_sources": ([pS, P, P, P, P, P, P], ctypes.c_int),
         "specfold_sparse_qkv": ([pS, P, P, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
         "specfold_folded_attention": ([pS, P, P, P, P, P, P, ctypes.POINTER(PrefixKV), P, P, P, SZ, P],
@@ -201,13 +203,23 @@ def gate(shape, parent, H, delta, rho, fold, inv_rms=None, rho_in=None):
     _check(st, "specfold_gate")
 
 
-def compact(shape, fold, rec_rows, rec_count, branch_off, row_slot):
+def compact_workspace(shape, device="cuda"):
+    """Scratch for ``compact`` (None when the shape needs none)."""
+    n = int(_lib.specfold_compact_workspace_bytes(ctypes.byref(make_shape(shape))))
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def compact(shape, fold, rec_rows, rec_count, branch_off, row_slot, ws=None):
+    """``ws``: a ``compact_workspace(shape)`` tensor; made here when not given (an allocation)."""
     sh = make_shape(shape)
     R = shape.n_branch * shape.block
+    if ws is None:
+        ws = compact_workspace(shape, fold.device)
     st = _lib.specfold_compact(ctypes.byref(sh), _ptr(fold, torch.uint8, R, "fold"),
                                _ptr(rec_rows, torch.int32, R, "rec_rows"), _ptr(rec_count, torch.int32, 1, "rec_count"),
                                _ptr(branch_off, torch.int32, shape.n_branch + 1, "branch_off"),
-                               _ptr(row_slot, torch.int32, R, "row_slot"), _stream())
+                               _ptr(row_slot, torch.int32, R, "row_slot"),
+                               _ptr(ws, torch.uint8, None, "ws", True), 0 if ws is None else ws.numel(), _stream())
     _check(st, "specfold_compact")
 
 

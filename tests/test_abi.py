@@ -88,8 +88,17 @@ def test_gate_rejects_null_misaligned_alias():
 def test_compact_and_resolve_validation():
     sh = _shape()
     p, keep = _parent([-1, 0, 1])
-    assert L.specfold_compact(ctypes.byref(sh), FAKE, None, FAKE * 2, FAKE * 3, FAKE * 4, None) == -1
-    assert L.specfold_compact(ctypes.byref(sh), FAKE, FAKE * 2, FAKE * 2, FAKE * 3, FAKE * 4, None) == -7
+    assert L.specfold_compact(ctypes.byref(sh), FAKE, None, FAKE * 2, FAKE * 3, FAKE * 4, None, 0, None) == -1
+    assert L.specfold_compact(ctypes.byref(sh), FAKE, FAKE * 2, FAKE * 2, FAKE * 3, FAKE * 4, None, 0, None) == -7
+    # past 8192 rows the look-back scan needs its workspace
+    big = _shape(n_branch=3, block=8193)
+    need = L.specfold_compact_workspace_bytes(ctypes.byref(big))
+    assert L.specfold_compact_workspace_bytes(ctypes.byref(sh)) == 0 and need >= 4 * (4 + 1)
+    assert L.specfold_compact(ctypes.byref(big), FAKE, 0x100000, 0x200000, 0x300000, 0x400000, None, 0, None) == -5
+    assert L.specfold_compact(ctypes.byref(big), FAKE, 0x100000, 0x200000, 0x300000, 0x400000, 0x500000,
+                              need - 1, None) == -5
+    assert L.specfold_compact(ctypes.byref(big), FAKE, 0x100000, 0x200000, 0x300000, 0x400000, 0x100000,
+                              need, None) == -7
     assert L.specfold_resolve_sources(ctypes.byref(sh), p, FAKE, FAKE * 2, FAKE * 3, FAKE * 3, None) == -7
     bad, keep2 = _parent([-1, 5, 1])
     assert L.specfold_resolve_sources(ctypes.byref(sh), bad, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None) == -3

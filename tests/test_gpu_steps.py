@@ -89,7 +89,7 @@ def test_gate_threshold_bit_exact_when_fed_rho():
 @pytest.mark.parametrize("B1,N,kind,p", [(3, 8, "chain", 0.7), (9, 32, "random", 0.72), (6, 20, "star", 0.5),
                                          (64, 64, "random", 0.8), (9, 32, "random", 1.0), (9, 32, "random", 0.0),
                                          (1, 17, "random", 0.5), (33, 40, "chain", 0.9),
-                                         # past one 8192-row tile: the three-pass compaction
+                                         # past 8192 rows: the look-back scan over 32768-row tiles
                                          (37, 1000, "random", 0.7), (3, 8193, "random", 0.3),
                                          (5, 8192, "random", 1.0), (64, 4096, "chain", 0.5)])
 def test_compact_and_resolve_bit_exact(B1, N, kind, p):
@@ -106,6 +106,77 @@ def test_compact_and_resolve_bit_exact(B1, N, kind, p):
     assert np.array_equal(off, off_o)
     assert np.array_equal(sb.reshape(B1, N), src_o)
     assert np.array_equal(ss.reshape(B1, N), src_slot_o)
+
+
+def _check_compaction_properties(fold_flat, rec, M, slot, off, N):
+    """Properties that fix the compaction's outputs at any size: the list holds exactly the
+    recomputed rows, ascending; row_slot is its inverse and -1 on folded rows; each branch offset
+    is the number of recomputed rows before the branch's first row."""
+    keep = fold_flat == 0
+    assert M == int(keep.sum())
+    assert np.all(np.diff(rec[:M]) > 0) and np.all(keep[rec[:M]])
+    assert np.array_equal(slot[rec[:M]], np.arange(M))
+    assert np.all(slot[~keep] == -1)
+    before = np.concatenate([[0], np.cumsum(keep)])
+    assert np.array_equal(off, before[np.arange(off.size) * N])
+
+
+def test_compact_largest_input_and_reused_workspace():
+    """2^24 rows (512 tiles): checked by the properties that fix the result; then a second call on
+    the same (now dirty) workspace with another mask, and a poisoned workspace."""
+    sh = Shape(64, 262144, 64, 4, 2, 16, 128, 0)
+    R, N = sh.n_branch * sh.block, sh.block
+    g = torch.Generator(device=DEV)
+    g.manual_seed(3)
+    ws = sf.compact_workspace(sh)
+    ws.fill_(0xFF)
+    rec = torch.empty(R, dtype=I32, device=DEV)
+    cnt = torch.empty(1, dtype=I32, device=DEV)
+    off = torch.empty(sh.n_branch + 1, dtype=I32, device=DEV)
+    slot = torch.empty(R, dtype=I32, device=DEV)
+    for p in (0.7, 0.05, 0.999):
+        f = (torch.rand(R, device=DEV, generator=g) < p).to(torch.uint8)
+        sf.compact(sh, f, rec, cnt, off, slot, ws=ws)
+        torch.cuda.synchronize()
+        M = int(cnt.item())
+        _check_compaction_properties(f.cpu().numpy(), rec.cpu().numpy(), M, slot.cpu().numpy(), off.cpu().numpy(), N)
+        assert int(ws[4:8].view(torch.int32).item()) == 0     # no tile gave up waiting
+
+
+def test_compact_in_a_graph_replays():
+    """The look-back's status words are cleared by a kernel of the call itself, so a captured
+    compaction gives the right result on every replay (masks changed between replays)."""
+    sh = Shape(37, 1000, 64, 4, 2, 16, 128, 0)
+    R, N = sh.n_branch * sh.block, sh.block
+    rng = np.random.default_rng(12)
+    f = torch.zeros(R, dtype=torch.uint8, device=DEV)
+    rec = torch.empty(R, dtype=I32, device=DEV)
+    cnt = torch.empty(1, dtype=I32, device=DEV)
+    off = torch.empty(sh.n_branch + 1, dtype=I32, device=DEV)
+    slot = torch.empty(R, dtype=I32, device=DEV)
+    ws = sf.compact_workspace(sh)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        sf.compact(sh, f, rec, cnt, off, slot, ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sf.compact(sh, f, rec, cnt, off, slot, ws=ws)
+    for k in range(4):
+        mask = random_mask(sh, rng, 0.3 + 0.2 * k)
+        f.copy_(torch.from_numpy(mask.astype(np.uint8).ravel()).to(DEV))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        rec_o, slot_o, off_o = oracle.compact(mask)
+        M = int(cnt.item())
+        assert M == rec_o.size
+        assert np.array_equal(rec.cpu().numpy()[:M], rec_o)
+        assert np.array_equal(slot.cpu().numpy(), slot_o)
+        assert np.array_equal(off.cpu().numpy(), off_o)
+    del graph
 
 
 def _oracle_steps(case, delta):
