@@ -172,6 +172,8 @@ def main():
 
     st_f = stage_times(wl.delta)
     st_d = stage_times(0.0)
+    print("[bench] per-launch us, folded: " + ", ".join(f"{k} {v:.2f}" for k, v in st_f.items()),
+          file=sys.stderr, flush=True)
 
     M = results[wl.delta]["M"]
     fold = results[wl.delta]["fold"].reshape(sh.n_branch, sh.block)
