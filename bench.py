@@ -53,6 +53,10 @@ def parse():
     ap.add_argument("--stage-calls", type=int, default=30, help="eager calls timed per launch with events")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration runs)")
+    ap.add_argument("--counters", type=int, default=0,
+                    help="hardware-counter runs: after the eager reference calls, run this many folded and "
+                         "then as many dense layer steps (cold weights), the flat gate and compaction once "
+                         "each and a 256 MiB device copy, print the dispatch plan and exit (no timing)")
     ap.add_argument("--layers", type=int, default=0, help="stack workloads: layers (default: the workload's)")
     ap.add_argument("--stack-steps", type=int, default=0, help="stack workloads: steps (default: the workload's)")
     ap.add_argument("--no-gate-flat", action="store_true", help="skip the large flat gate/compaction timing")
@@ -128,6 +132,26 @@ def main():
         torch.cuda.synchronize()
         results[delta] = {"H_out": H_out.clone(), "fold": stats["fold"].cpu().numpy().copy(),
                           "M": int(stats["rec_count"].item())}
+
+    if args.counters > 0:
+        # fixed dispatch sequence for rocprofv3 --pmc passes: the counters are read per dispatch,
+        # and the plan tells which dispatch is which
+        plan = []
+        for delta in (wl.delta, 0.0):
+            for k in range(args.counters):
+                step(delta, 1 + k % (n_copies - 1))
+                torch.cuda.synchronize()
+            plan.append({"delta": delta, "steps": args.counters, "launches_per_step": len(sf.stage_names()),
+                         "M": results[delta]["M"]})
+        flat = gate_flat_leg(torch, sf, dev, once=True)
+        n = (256 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).uniform_()
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"counters_plan": plan, "stage_names": sf.stage_names(), "flat": flat,
+                          "copy_bytes": 4 * n, "workload": args.workload}), flush=True)
+        return
 
     # ---------------------------------------------------------------- graph-timed throughput
     # exactly K = --steps layer steps per graph replay; consecutive steps read consecutive weight
@@ -500,9 +524,10 @@ def graph_time(torch, fns, reps, warmup_s=0.5):
     return statistics.median(time_graph(torch, fns, rounds=5, warmup_s=warmup_s, reps=max(1, reps)))
 
 
-def gate_flat_leg(torch, sf, dev):
+def gate_flat_leg(torch, sf, dev, once=False):
     """Gate and compaction alone on a large flattened input, as bandwidth evidence: 9 branches of
-    16384 positions at D = 1536 (453 MB of H) for the gate; 64 x 262144 rows for the compaction."""
+    16384 positions at D = 1536 (453 MB of H) for the gate; 64 x 262144 rows for the compaction.
+    once: one eager call of each, untimed (counter runs); returns their sizes."""
     from synth import Shape
     sh = Shape(9, 16384, 1536, 12, 2, 128, 8960, 0)
     R, D = sh.rows, sh.hidden
@@ -510,8 +535,11 @@ def gate_flat_leg(torch, sf, dev):
     H = torch.randn((R, D), device=dev).to(torch.bfloat16)
     rho = torch.empty(R, device=dev)
     fold = torch.empty(R, dtype=torch.uint8, device=dev)
+    if once:
+        sf.gate(sh, parent, H, 0.1, rho, fold)
+        torch.cuda.synchronize()
     # 8 back-to-back calls per graph replay, so the replay's own launch is not in the figure
-    ms = graph_time(torch, [lambda: sf.gate(sh, parent, H, 0.1, rho, fold)] * 8, reps=10) / 8
+    ms = 0.0 if once else graph_time(torch, [lambda: sf.gate(sh, parent, H, 0.1, rho, fold)] * 8, reps=10) / 8
     # algorithmic bytes: every row of H read once (a parent row serves all its children), rho and
     # fold written
     gbytes = R * D * 2 + R * 5
@@ -524,6 +552,12 @@ def gate_flat_leg(torch, sf, dev):
     branch_off = torch.empty(sc.n_branch + 1, dtype=torch.int32, device=dev)
     row_slot = torch.empty(Rc, dtype=torch.int32, device=dev)
     cws = sf.compact_workspace(sc, dev)
+    if once:
+        sf.compact(sc, fold_c, rec_rows, rec_count, branch_off, row_slot, ws=cws)
+        torch.cuda.synchronize()
+        return {"gate": {"rows": R, "hidden": D, "bytes": R * D * 2 + R * 5},
+                "compact": {"rows": Rc, "M": int(rec_count.item()),
+                            "bytes": Rc + 4 * Rc + 4 * int(rec_count.item()) + 4 * (sc.n_branch + 1)}}
     ms_c = graph_time(torch, [lambda: sf.compact(sc, fold_c, rec_rows, rec_count, branch_off, row_slot, ws=cws)] * 8,
                       reps=10) / 8
     M = int(rec_count.item())
