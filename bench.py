@@ -840,30 +840,39 @@ def tree_bench(args, wl):
     st = {"fold": torch.zeros(R, dtype=torch.uint8, device=dev), "rec_count": torch.zeros(1, dtype=torch.int32, device=dev)}
     print(f"[bench] tree sweep ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     points = []
+    n_steps = 4                                   # verification steps per tree shape (new draws each)
     for kind in wl.tree_sweep:
-        parent = tree_of(kind, sh.n_branch, wl.base_seed, 0)
+        parents, Hs = [], []
+        for s in range(n_steps):
+            parent = tree_of(kind, sh.n_branch, wl.base_seed, s)
+            inp = step_inputs(sh, wl.base_seed, s, child_law=wl.child_law, parent=parent)
+            parents.append(parent)
+            Hs.append(to_dev(bf16_round(inp["H"].astype(np.float32)).reshape(R, D)))
         depth = np.zeros(sh.n_branch, dtype=np.int64)
         for i in range(1, sh.n_branch):
-            depth[i] = depth[parent[i]] + 1
-        inp = step_inputs(sh, wl.base_seed, 0, child_law=wl.child_law, parent=parent)
-        H_host = bf16_round(inp["H"].astype(np.float32))
-        H = to_dev(H_host.reshape(R, D))
+            depth[i] = depth[parents[0][i]] + 1
         res = {}
         for delta in (wl.delta, 0.0):
-            sf.verify_layer(sh, parent, lws[0], pf, None, H, delta, y, ws, stats=st)
-            torch.cuda.synchronize()
-            M = int(st["rec_count"].item())
-            ff = float(st["fold"].cpu().numpy().reshape(sh.n_branch, sh.block)[1:].mean())
+            Ms, ffs = [], []
+            for s in range(n_steps):
+                sf.verify_layer(sh, parents[s], lws[0], pf, None, Hs[s], delta, y, ws, stats=st)
+                torch.cuda.synchronize()
+                Ms.append(int(st["rec_count"].item()))
+                ffs.append(float(st["fold"].cpu().numpy().reshape(sh.n_branch, sh.block)[1:].mean()))
             reps = max(1, args.steps // (4 * n_copies))
-            ms = graph_time(torch, [lambda k=k, delta=delta: sf.verify_layer(sh, parent, lws[k], pf, None, H, delta, y, ws)
+            ms = graph_time(torch, [lambda k=k, delta=delta: sf.verify_layer(sh, parents[k % n_steps], lws[k], pf, None,
+                                                                            Hs[k % n_steps], delta, y, ws)
                                     for k in range(n_copies)], reps=reps) / n_copies
-            res[delta] = (ms, M, ff)
-        sf.verify_layer(sh, parent, lws[0], pf, None, H, wl.delta, y, ws, stats=st)
-        torch.cuda.synchronize()
-        finite = bool(torch.isfinite(y.float()).all().item())
-        (msf, M, ff), (msd, _, _) = res[wl.delta], res[0.0]
-        points.append({"tree": kind, "parent": parent.tolist(), "max_depth": int(depth.max()),
-                       "rec_rows": M, "fold_fraction_drafts": round(ff, 4), "us": round(msf * 1e3, 2),
+            res[delta] = (ms, float(np.mean(Ms)), float(np.mean(ffs)), ffs)
+        finite = True
+        for s in range(n_steps):
+            sf.verify_layer(sh, parents[s], lws[0], pf, None, Hs[s], wl.delta, y, ws)
+            torch.cuda.synchronize()
+            finite = finite and bool(torch.isfinite(y.float()).all().item())
+        (msf, M, ff, ffs), (msd, _, _, _) = res[wl.delta], res[0.0]
+        points.append({"tree": kind, "parent_step0": parents[0].tolist(), "max_depth_step0": int(depth.max()),
+                       "rec_rows_mean": round(M, 1), "fold_fraction_drafts": round(ff, 4),
+                       "fold_fraction_per_step": [round(v, 4) for v in ffs], "us": round(msf * 1e3, 2),
                        "dense_us": round(msd * 1e3, 2), "branch_tokens_per_s": round(R / (msf * 1e-3), 1),
                        "speedup_vs_dense": round(msd / msf, 4), "finite_output": finite})
         print(f"[bench] tree {kind} done", file=sys.stderr, flush=True)

@@ -32,6 +32,20 @@ _T_TOKENS = 13
 LOGNORMAL_MU = -3.2335
 LOGNORMAL_SIGMA = 1.2003
 
+# One-token drafts (the draft-shape sweep, [SpecFold summary, §D.2]: seven one-token sibling
+# drafts at depth 1 through parent-extending chains).  Main's block has 17 of its 32 positions
+# committed (the parent of the summary's Figure 6 example); every draft unmasks exactly one
+# position its parent still has masked and inherits the parent's committed tokens.  The
+# parent-child divergence concentrates at the positions that are still masked ([SpecFold
+# summary, §3.1 and §4.4]): there r is log-normal with P(r <= 0.1) = 0.20, at committed
+# positions with P(r <= 0.1) = 0.85 (both with the sigma above).  A draft deeper in the tree
+# has fewer masked positions, so the fold fraction depends on the tree's shape: about 0.54 for
+# seven siblings of main and 0.60 averaged over a seven-deep chain, inside the 0.52-0.67 range
+# the summary reports across drafting shapes.
+UNMASK1_COMMITTED = 17
+UNMASK1_MU_COMMITTED = -3.5466
+UNMASK1_MU_MASKED = -1.2924
+
 
 @dataclass(frozen=True)
 class Shape:
@@ -96,12 +110,15 @@ WORKLOADS: dict[str, Workload] = {
     # one layer at 1.5B-class shape, B = 8 drafts, prefix 512
     "layer-1.5b": Workload("layer-1.5b", Shape(9, 32, 1536, 12, 2, 128, 8960, 512), 1, 0.1),
     # 28-layer stack at 1.5B-class shape, prefix 2048, 8 steps with a new tree each step.  The
-    # attention projections and the down projection are drawn with std 0.04: then a folded
+    # attention projections and the down projection are drawn with std 0.0375: then a folded
     # position's branch-specific attention output moves its residual away from the parent's
     # layer after layer, so the per-branch divergence accumulates and positions leave the fold
-    # set as the stack deepens (with std 0.02 every layer's fold set is the first layer's)
+    # set as the stack deepens (0.71 of draft rows fold at the first layer, 0.67 at the last, 0.68
+    # over all 28 layers -- near the 72 % of cells over all layers that the SpecFold summary, §3.1,
+    # profiles).  With std 0.02 (or 0.03) every layer's fold set is the first layer's; with 0.04
+    # the fold fraction falls to 0.23 by the last layer.
     "stack-1.5b": Workload("stack-1.5b", Shape(9, 32, 1536, 12, 2, 128, 8960, 2048), 2, 0.1,
-                           layers=28, steps=8, weight_std=(0.04, 0.04, 0.02, 0.04)),
+                           layers=28, steps=8, weight_std=(0.0375, 0.0375, 0.02, 0.0375)),
     # 28-layer stack at 7B-class shape, prefix 2048
     "stack-7b": Workload("stack-7b", Shape(9, 32, 3584, 28, 4, 128, 18944, 2048), 3, 0.1,
                          layers=28),
@@ -111,7 +128,9 @@ WORKLOADS: dict[str, Workload] = {
                           delta_sweep=(0.0, 0.01, 0.1, 0.2, 0.3, 0.5, 0.7)),
     # one layer at 1.5B-class shape with B = 7 drafts, swept over the draft tree's shape: seven
     # siblings of main (depth 1), random trees of depth <= 2, 3, 4, and a 7-deep chain
+    # one-token drafts (child law "unmask1")
     "draft-shapes-1.5b": Workload("draft-shapes-1.5b", Shape(8, 32, 1536, 12, 2, 128, 8960, 512), 5, 0.1,
+                                  child_law="unmask1",
                                   tree_sweep=("star", "depth2", "depth3", "depth4", "chain")),
 }
 
@@ -287,7 +306,8 @@ def step_inputs(shape: Shape, base_seed: int, step: int, tree: str = "random",
     Returns ``{"parent": int32[B+1], "H": float64[B+1, N, D], "r": float64[B+1, N],
     "unmasked": bool[B+1, N]}``; ``r`` is the drawn relative distance of each draft row
     (NaN for main and for unmasked rows).  Children are built in branch order from the
-    (already built) parent block.
+    (already built) parent block.  With ``child_law="unmask1"`` the result also holds
+    ``"committed": bool[B+1, N]`` (each branch's committed positions).
     """
     B1, N = shape.n_branch, shape.block
     if parent is None:
@@ -298,8 +318,21 @@ def step_inputs(shape: Shape, base_seed: int, step: int, tree: str = "random",
     H[0] = main_hidden(shape, base_seed, step)
     r_all = np.full((B1, N), np.nan)
     unm_all = np.zeros((B1, N), dtype=bool)
+    committed = None
+    if child_law == "unmask1":
+        committed = np.zeros((B1, N), dtype=bool)
+        committed[0, rng.choice(N, size=min(UNMASK1_COMMITTED, N), replace=False)] = True
     for i in range(1, B1):
-        if child_law == "tiny":
+        if child_law == "unmask1":
+            p = parent[i]
+            masked = np.flatnonzero(~committed[p])
+            u = int(masked[rng.integers(masked.size)]) if masked.size else int(rng.integers(N))
+            unmasked = np.zeros(N, dtype=bool)
+            unmasked[u] = True
+            committed[i] = committed[p] | unmasked
+            r = np.where(committed[p], rng.lognormal(UNMASK1_MU_COMMITTED, LOGNORMAL_SIGMA, N),
+                         rng.lognormal(UNMASK1_MU_MASKED, LOGNORMAL_SIGMA, N))
+        elif child_law == "tiny":
             small = rng.random(N) < 0.7
             r = np.where(small, rng.uniform(0.01, 0.08, N), rng.uniform(0.15, 1.0, N))
             unmasked = np.zeros(N, dtype=bool)
@@ -311,7 +344,10 @@ def step_inputs(shape: Shape, base_seed: int, step: int, tree: str = "random",
         H[i] = child_hidden(H[parent[i]], r, unmasked, rng)
         r_all[i] = np.where(unmasked, np.nan, r)
         unm_all[i] = unmasked
-    return {"parent": parent, "H": H, "r": r_all, "unmasked": unm_all}
+    out = {"parent": parent, "H": H, "r": r_all, "unmasked": unm_all}
+    if committed is not None:
+        out["committed"] = committed
+    return out
 
 
 def expected_fold_fraction(delta: float, n_block: int = 32) -> float:

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
-from synth import WORKLOADS, parent_tree, step_inputs
+from synth import WORKLOADS, parent_tree, step_inputs, tree_of
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "gate_cases.json")
 
@@ -89,6 +89,48 @@ def test_generator_fold_fraction_matches_profile():
         _, fold = oracle.gate(inp["H"], inp["parent"], 0.1)
         fr.append(fold[1:].mean())
     assert 0.62 < np.mean(fr) < 0.82
+
+
+def test_one_token_drafts_structure_and_closed_form():
+    """The draft-shape sweep's law: every draft unmasks exactly one position its parent still
+    had masked and keeps the parent's committed positions (so the committed sets nest along the
+    tree); at layer 0 the gate's rho equals the drawn r on every other row."""
+    wl = WORKLOADS["draft-shapes-1.5b"]
+    sh = wl.shape
+    for kind in wl.tree_sweep:
+        par = tree_of(kind, sh.n_branch, wl.base_seed, 0)
+        inp = step_inputs(sh, wl.base_seed, 0, child_law=wl.child_law, parent=par)
+        com, unm = inp["committed"], inp["unmasked"]
+        assert com[0].sum() == 17 and not unm[0].any()
+        for i in range(1, sh.n_branch):
+            p = par[i]
+            assert unm[i].sum() == 1
+            u = int(np.flatnonzero(unm[i])[0])
+            assert not com[p, u]
+            assert np.array_equal(com[i], com[p] | unm[i])
+        rho, _ = oracle.gate(inp["H"], par, wl.delta)
+        known = np.isfinite(inp["r"])
+        np.testing.assert_allclose(rho[known], inp["r"][known], rtol=1e-12)
+        assert np.all((rho[unm] > 0.9) & (rho[unm] < 2.0))
+
+
+def test_one_token_drafts_fold_fraction_depends_on_the_tree():
+    """Averaged over steps, the layer-0 fold fraction of one-token drafts lies in the 0.52-0.67
+    range the SpecFold summary (§D.2) reports across drafting shapes, and deeper trees (fewer
+    masked positions per draft) fold more than seven siblings of main."""
+    wl = WORKLOADS["draft-shapes-1.5b"]
+    sh = wl.shape
+    mean = {}
+    for kind in wl.tree_sweep:
+        fr = []
+        for step in range(12):
+            par = tree_of(kind, sh.n_branch, wl.base_seed, step)
+            inp = step_inputs(sh, wl.base_seed, step, child_law=wl.child_law, parent=par)
+            _, fold = oracle.gate(inp["H"], par, wl.delta)
+            fr.append(fold[1:].mean())
+        mean[kind] = float(np.mean(fr))
+        assert 0.52 <= mean[kind] <= 0.67, (kind, mean[kind])
+    assert mean["chain"] > mean["star"] + 0.03
 
 
 # ------------------------------------------------------------------ compaction
