@@ -119,9 +119,12 @@ WORKLOADS: dict[str, Workload] = {
     # the fold fraction falls to 0.23 by the last layer.
     "stack-1.5b": Workload("stack-1.5b", Shape(9, 32, 1536, 12, 2, 128, 8960, 2048), 2, 0.1,
                            layers=28, steps=8, weight_std=(0.0375, 0.0375, 0.02, 0.0375)),
-    # 28-layer stack at 7B-class shape, prefix 2048
+    # 28-layer stack at 7B-class shape, prefix 2048; attention and down projections drawn with
+    # std 0.0279, where the fold fraction falls slowly as at the 1.5B shape (0.73 of draft rows
+    # at the first layer, 0.64 at the last, 0.67 over the stack; 0.0275 keeps nearly the first
+    # layer's fold set, 0.029 drives it to 0.21)
     "stack-7b": Workload("stack-7b", Shape(9, 32, 3584, 28, 4, 128, 18944, 2048), 3, 0.1,
-                         layers=28),
+                         layers=28, weight_std=(0.0279, 0.0279, 0.02, 0.0279)),
     # one layer at 14B-class shape, prefix 4096, swept over B and delta
     "sweep-14b": Workload("sweep-14b", Shape(9, 32, 5120, 40, 8, 128, 13824, 4096), 4, 0.1,
                           branch_sweep=(2, 4, 6, 8),

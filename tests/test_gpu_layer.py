@@ -144,12 +144,14 @@ def test_stack_28_layers_regates_and_matches_oracle():
         assert f[-1][1:].mean() <= f[0][1:].mean() - 0.2
 
 
-def test_layer_7b_shape():
+@pytest.mark.parametrize("layer", [0, 13, 27])
+def test_layer_7b_shape(layer):
+    """Layers of the 7B-shape stack (each with its own seeded weights and prefix cache)."""
     wl = WORKLOADS["stack-7b"]
-    case = LayerCase(wl.shape, wl.base_seed, layer=13)
+    case = LayerCase(wl.shape, wl.base_seed, layer=layer)
     res = case.run(wl.delta)
     _, err = case.check(wl.delta, res)
-    print(f"7b layer 13: rel L2 {err:.2e}")
+    print(f"7b layer {layer}: rel L2 {err:.2e}")
 
 
 @pytest.mark.parametrize("B", [2, 8])
