@@ -38,15 +38,19 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200,
-                    help="steps per timed graph replay (exactly this many; the median of --rounds replays is reported)")
+    ap.add_argument("--steps", type=int, default=0,
+                    help="steps per timed graph replay (exactly this many; the median of --rounds replays is "
+                         "reported); a step is one verification pass through the workload's layers (default: "
+                         "16 for the 28-layer stacks, 200 for single layers)")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--rounds", type=int, default=5, help="timed replays of the K-step graph (median reported)")
-    ap.add_argument("--no-stack", action="store_true",
-                    help="layer workloads: skip the 28-layer stack leg (stack-1.5b) of the default line")
     ap.add_argument("--warmup-seconds", type=float, default=1.0,
                     help="keep replaying (untimed) at least this long before timing, so clocks have ramped")
-    ap.add_argument("--workload", default="layer-1.5b")
+    ap.add_argument("--workload", default="stack-1.5b",
+                    help="stack-1.5b (default: the 28-layer 1.5B-shape stack, with the single 1.5B layer as a "
+                         "sub-object), stack-7b, layer-1.5b, sweep-14b, draft-shapes-1.5b")
+    ap.add_argument("--no-layer", action="store_true",
+                    help="stack-1.5b: skip the single-layer (layer-1.5b) sub-object of the default line")
     ap.add_argument("--regime", choices=["cold", "warm"], default="cold")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -72,6 +76,65 @@ def parse():
     return ap.parse_args()
 
 
+# Per-kernel fractions of the vendor peaks (event-timed launches): MFMA for the contractions
+# (GEMMs, attention), HBM for every kernel.  Bytes are what each launch must move (weights,
+# activations, outputs, prefix cache), not split-K partials or chunk states; the epilogue kernels
+# have no algorithmic bytes of their own beyond the rows they write.  Cold, a contraction of
+# intensity I = flops/bytes cannot exceed I * 8 TB/s of MFMA work, i.e. a fraction
+# mfma_cap_cold = min(1, I * HBM peak / MFMA peak) of the MFMA peak.
+def kernel_work(sh, name, m):
+    """(flops, bytes) of one launch of stage `name` of a layer of shape sh with m recompute rows."""
+    R, D, F = sh.rows, sh.hidden, sh.ffn
+    d, Hq, Hkv, P, N = sh.head_dim, sh.n_q_heads, sh.n_kv_heads, sh.prefix_len, sh.block
+    Nq, Do = (Hq + 2 * Hkv) * d, Hq * d
+    table = {
+        "gate_rmsnorm": (0, 2 * R * D + 2 * D + 2 * R * D + 9 * R),
+        "qkv_gemm_compact_resolve": (2 * m * Nq * D, 2 * Nq * D + 2 * m * D + 2 * m * Nq),
+        "qkv_rope_epilogue": (0, 2 * m * Nq),
+        "attention": (4 * d * Hq * (P * m + N * R), 4 * P * Hkv * d + 2 * m * Nq + 2 * R * Do),
+        "oproj_gemm": (2 * R * Do * D, 2 * Do * D + 2 * R * Do + 2 * R * D),
+        "oproj_residual_rmsnorm": (0, 2 * R * D + 4 * R * D),
+        "gate_up_swiglu_gemm": (2 * m * 2 * F * D, 2 * 2 * F * D + 2 * m * D + 2 * m * F),
+        "down_gemm": (2 * m * F * D, 2 * F * D + 2 * m * F + 2 * m * D),
+        "down_inherit_epilogue": (0, 4 * R * D),
+    }
+    return table.get(name)
+
+
+def kernel_pct(sh, st, m):
+    """Per-stage event-timed microseconds -> fractions of the vendor peaks (the two attention
+    launches are reported together)."""
+    st = dict(st)
+    attn = sum(v for k, v in st.items() if k.startswith("attn"))
+    st = {k: v for k, v in st.items() if not k.startswith("attn")}
+    st["attention"] = attn
+    out_ = {}
+    for k, us in st.items():
+        w_ = kernel_work(sh, k, m)
+        if w_ is None or us <= 0:
+            continue
+        flops, byts = w_
+        sec = us * 1e-6
+        row = {"us": round(us, 2), "hbm_frac": round(byts / sec / (HBM_PEAK_GBS * 1e9), 4), "bytes": byts}
+        if flops:
+            row["mfma_frac"] = round(flops / sec / (BF16_PEAK_TFLOPS * 1e12), 4)
+            row["mfma_cap_cold"] = round(min(1.0, flops / byts * HBM_PEAK_GBS * 1e9 / (BF16_PEAK_TFLOPS * 1e12)), 4)
+        out_[k] = row
+    return out_
+
+
+def layer_roof_us(sh, m):
+    """Whole-layer roofline time at the vendor peaks: sum over the contractions and the gate of
+    max(bytes / BW, flops / MFMA) (the epilogues' rows are written by the kernels they follow in
+    a fused design)."""
+    t = 0.0
+    for k in ("gate_rmsnorm", "qkv_gemm_compact_resolve", "attention", "oproj_gemm", "gate_up_swiglu_gemm",
+              "down_gemm"):
+        flops, byts = kernel_work(sh, k, m)
+        t += max(flops / (BF16_PEAK_TFLOPS * 1e12), byts / (HBM_PEAK_GBS * 1e9))
+    return t * 1e6
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -79,19 +142,29 @@ def main():
               "this build has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
-    import torch
-
-    from sparse_layer_rho_amd import specfold as sf
-    from synth import WORKLOADS, bf16_round, layer_weights, prefix_kv, step_inputs
+    from synth import WORKLOADS
 
     wl = WORKLOADS[args.workload]
+    if args.steps <= 0:
+        args.steps = 16 if (wl.layers > 1 or args.layers > 1) else 200
     if wl.layers > 1 or args.layers > 1:
         return stack_bench(args, wl)
     if wl.branch_sweep:
         return sweep_bench(args, wl)
     if wl.tree_sweep:
         return tree_bench(args, wl)
+    return layer_main(args, wl)
+
+
+def layer_main(args, wl, emit=True):
+    """One layer (layer-1.5b): cold and warm, folded and dense, per-launch event timing, the flat
+    gate and compaction; prints the line (emit) and returns it."""
+    import numpy as np
+    import torch
+
+    from sparse_layer_rho_amd import specfold as sf
+    from synth import bf16_round, layer_weights, prefix_kv, step_inputs
+
     sh = wl.shape
     R, D, F = sh.rows, sh.hidden, sh.ffn
     dev = torch.device("cuda:0")
@@ -109,7 +182,7 @@ def main():
     w0 = {k: to_dev(v) for k, v in w_host.items()}
     pk, pv = to_dev(pk_h), to_dev(pv_h)
     H_in = to_dev(H_host.reshape(R, D))
-    print(f"[bench] inputs ready in {time.time() - t0:.1f}s: {args.workload}, R={R}, "
+    print(f"[bench] inputs ready in {time.time() - t0:.1f}s: {wl.name}, R={R}, "
           f"weights {sh.weight_bytes_bf16() / 1e6:.1f} MB/layer", file=sys.stderr, flush=True)
 
     # weight copies for the cold regime: enough of them to overflow the 256 MB cache
@@ -150,7 +223,7 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"counters_plan": plan, "stage_names": sf.stage_names(), "flat": flat,
-                          "copy_bytes": 4 * n, "workload": args.workload}), flush=True)
+                          "copy_bytes": 4 * n, "workload": wl.name}), flush=True)
         return
 
     # ---------------------------------------------------------------- graph-timed throughput
@@ -215,66 +288,14 @@ def main():
                 "traffic": measured_traffic(), "avg_us": round(gu_us, 2), "bytes_per_launch": gu_bytes,
                 "tflops": round(2 * M * 2 * F * D / (gu_us * 1e-6) / 1e12, 1)}
 
-    # per-kernel fractions of the vendor peaks (folded step, event-timed launches): MFMA for the
-    # contractions (GEMMs, attention), HBM for every kernel.  Bytes are what each step must move
-    # (weights, activations, outputs, prefix cache), not split-K partials or chunk states; the
-    # epilogue kernels have no algorithmic bytes of their own beyond the rows they write.  Cold,
-    # a contraction of intensity I = flops/bytes cannot exceed I * 8 TB/s of MFMA work, i.e. a
-    # fraction mfma_cap_cold = min(1, I * HBM peak / MFMA peak) of the MFMA peak.
-    def kernel_work(name, m):
-        d, Hq, Hkv, P, N = sh.head_dim, sh.n_q_heads, sh.n_kv_heads, sh.prefix_len, sh.block
-        Nq, Do = (Hq + 2 * Hkv) * d, Hq * d
-        table = {
-            "gate_rmsnorm": (0, 2 * R * D + 2 * D + 2 * R * D + 9 * R),
-            "qkv_gemm_compact_resolve": (2 * m * Nq * D, 2 * Nq * D + 2 * m * D + 2 * m * Nq),
-            "qkv_rope_epilogue": (0, 2 * m * Nq),
-            "attention": (4 * d * Hq * (P * m + N * R), 4 * P * Hkv * d + 2 * m * Nq + 2 * R * Do),
-            "oproj_gemm": (2 * R * Do * D, 2 * Do * D + 2 * R * Do + 2 * R * D),
-            "oproj_residual_rmsnorm": (0, 2 * R * D + 4 * R * D),
-            "gate_up_swiglu_gemm": (2 * m * 2 * F * D, 2 * 2 * F * D + 2 * m * D + 2 * m * F),
-            "down_gemm": (2 * m * F * D, 2 * F * D + 2 * m * F + 2 * m * D),
-            "down_inherit_epilogue": (0, 4 * R * D),
-        }
-        return table.get(name)
-
-    def kernel_pct(st, m):
-        st = dict(st)
-        attn = sum(v for k, v in st.items() if k.startswith("attn"))
-        st = {k: v for k, v in st.items() if not k.startswith("attn")}
-        st["attention"] = attn
-        out_ = {}
-        for k, us in st.items():
-            w_ = kernel_work(k, m)
-            if w_ is None:
-                continue
-            flops, byts = w_
-            sec = us * 1e-6
-            row = {"us": round(us, 2), "hbm_frac": round(byts / sec / (HBM_PEAK_GBS * 1e9), 4), "bytes": byts}
-            if flops:
-                row["mfma_frac"] = round(flops / sec / (BF16_PEAK_TFLOPS * 1e12), 4)
-                row["mfma_cap_cold"] = round(min(1.0, flops / byts * HBM_PEAK_GBS * 1e9 / (BF16_PEAK_TFLOPS * 1e12)), 4)
-            out_[k] = row
-        return out_
-
-    # whole-layer roofline at the vendor peaks: sum over the contractions and the gate of
-    # max(bytes / BW, flops / MFMA) (the epilogues' rows are written by the kernels they follow in
-    # a fused design)
-    def layer_roof_us(m):
-        t = 0.0
-        for k in ("gate_rmsnorm", "qkv_gemm_compact_resolve", "attention", "oproj_gemm", "gate_up_swiglu_gemm",
-                  "down_gemm"):
-            flops, byts = kernel_work(k, m)
-            t += max(flops / (BF16_PEAK_TFLOPS * 1e12), byts / (HBM_PEAK_GBS * 1e9))
-        return t * 1e6
-
     def regime(f, d_):
         return {"value": round(f["branch_tokens_per_s"], 1), "ms_per_step": round(f["ms_per_step"], 5),
                 "round_ms_per_step": f["round_ms_per_step"],
                 "dense_value": round(d_["branch_tokens_per_s"], 1), "dense_ms_per_step": round(d_["ms_per_step"], 5),
                 "dense_round_ms_per_step": d_["round_ms_per_step"],
                 "speedup_vs_dense": round(d_["ms_per_step"] / f["ms_per_step"], 4),
-                "layer_roofline_frac": {"folded": round(layer_roof_us(M) / (f["ms_per_step"] * 1e3), 4),
-                                        "dense": round(layer_roof_us(R) / (d_["ms_per_step"] * 1e3), 4)}}
+                "layer_roofline_frac": {"folded": round(layer_roof_us(sh, M) / (f["ms_per_step"] * 1e3), 4),
+                                        "dense": round(layer_roof_us(sh, R) / (d_["ms_per_step"] * 1e3), 4)}}
 
     out = {
         "metric": METRIC,
@@ -289,7 +310,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded random weights, prefix KV and parent-linked draft hidden states)",
-        "config": {"workload": args.workload, "hidden": D, "n_q_heads": sh.n_q_heads, "n_kv_heads": sh.n_kv_heads,
+        "config": {"workload": wl.name, "hidden": D, "n_q_heads": sh.n_q_heads, "n_kv_heads": sh.n_kv_heads,
                    "head_dim": sh.head_dim, "ffn": F, "block": sh.block, "drafts": sh.n_branch - 1,
                    "prefix": sh.prefix_len, "delta": wl.delta, "rows": R, "regime": args.regime,
                    "weight_copies": n_copies if args.regime == "cold" else 1,
@@ -300,19 +321,15 @@ def main():
                   "rec_rows": results[0.0]["M"]},
         "fold_fraction_drafts": round(fold_frac, 4),
         "rec_rows": M,
-        "layer_roofline_frac": {"folded": round(layer_roof_us(M) / (folded["ms_per_step"] * 1e3), 4),
-                                "dense": round(layer_roof_us(R) / (dense["ms_per_step"] * 1e3), 4)},
+        "layer_roofline_frac": {"folded": round(layer_roof_us(sh, M) / (folded["ms_per_step"] * 1e3), 4),
+                                "dense": round(layer_roof_us(sh, R) / (dense["ms_per_step"] * 1e3), 4)},
         "regimes": {"cold": regime(cold_f, cold_d), "warm": regime(warm_f, warm_d)},
         "roofline": roofline,
-        "kernel_frac_of_peak": kernel_pct(st_f, M),
-        "kernel_frac_of_peak_dense": kernel_pct(st_d, R),
+        "kernel_frac_of_peak": kernel_pct(sh, st_f, M),
+        "kernel_frac_of_peak_dense": kernel_pct(sh, st_d, R),
         "stages_us": {"folded": {k: round(v, 2) for k, v in st_f.items()},
                       "dense": {k: round(v, 2) for k, v in st_d.items()}},
     }
-
-    if not args.no_stack and args.workload == "layer-1.5b":
-        # the 28-layer stack at the same model shape (prefix 2048, 8 steps with a new tree each)
-        out["stack"] = stack_measure(torch, sf, WORKLOADS["stack-1.5b"], 0, 0, args, dev)
 
     if not args.no_gate_flat:
         out["gate_flat"] = gate_flat_leg(torch, sf, dev)
@@ -335,7 +352,9 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"], out["verified"] = cpu_baseline_leg(
             sh, wl, parent, H_host, w_host, pk_h, pv_h, results[wl.delta], args.cpu_seconds)
-    print(json.dumps(out), flush=True)
+    if emit:
+        print(json.dumps(out), flush=True)
+    return out
 
 
 def serialized_leg(torch, sf, sh, lws, pf, H_in, H_dense, dense, args):
@@ -466,13 +485,13 @@ def correction_leg(torch, sf, sh, wl, parent, H_in, w, pk, pv, args):
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gate_up_swiglu_gemm_layer-1.5b_traffic.md")
 
 
-def measured_traffic():
-    """HBM bytes per launch of the gate/up GEMM from the committed counter record (FETCH_SIZE +
+def measured_traffic(record=None):
+    """HBM bytes per launch of the gate/up GEMM from a committed counter record (FETCH_SIZE +
     WRITE_SIZE, calibrated by a copy of known size), or None when the record is missing or was
     taken for a different version of the GEMM sources."""
     import hashlib
     try:
-        text = open(TRAFFIC_RECORD).read()
+        text = open(record or TRAFFIC_RECORD).read()
         rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
     except (OSError, IndexError, ValueError):
         return None
@@ -574,10 +593,12 @@ def gate_flat_leg(torch, sf, dev, once=False):
                         "hbm_frac": round(cbytes / (ms_c * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
 
 
-def stack_measure(torch, sf, wl, layers, steps, args, dev, with_head=False):
-    """A full verification pass through an L-layer stack, S steps with a new draft tree each step:
-    per-branch residual streams carried across layers, every layer re-gating on its own input.
-    One graph holds the S steps; the median of --rounds timed replays is reported."""
+def stack_measure(torch, sf, wl, layers, steps, args, dev, with_head=False, keep=False):
+    """Verification passes through an L-layer stack: per-branch residual streams carried across
+    layers, every layer re-gating on its own input.  S input steps (a new draft tree and new
+    hidden states each); one graph holds exactly K = --steps passes, pass k on input k % S; the
+    median of --rounds timed replays is reported, after at least --warmup untimed passes.
+    keep: also return the device objects (for the per-launch timing and the CPU baseline)."""
     import numpy as np
 
     from synth import bf16_round, device_layer, step_inputs
@@ -586,6 +607,7 @@ def stack_measure(torch, sf, wl, layers, steps, args, dev, with_head=False):
     R, D = sh.rows, sh.hidden
     L = layers if layers > 1 else wl.layers
     S = steps if steps > 0 else max(1, wl.steps)
+    K = max(1, args.steps)
     t0 = time.time()
     # every layer's weights and prefix cache drawn on the device (synth.device_layer)
     layer_list = [device_layer(torch, sh, 1000 * wl.base_seed + l, dev, wl.weight_std) for l in range(L)]
@@ -597,7 +619,7 @@ def stack_measure(torch, sf, wl, layers, steps, args, dev, with_head=False):
         Hs = bf16_round(inp["H"].astype(np.float32))
         steps_in.append((inp["parent"], torch.from_numpy(Hs.reshape(R, D)).to(dev).to(torch.bfloat16)))
     torch.cuda.synchronize()
-    print(f"[bench] stack ready in {time.time() - t0:.1f}s: {wl.name}, {L} layers, {S} steps, "
+    print(f"[bench] stack ready in {time.time() - t0:.1f}s: {wl.name}, {L} layers, {S} input steps, "
           f"{L * sh.weight_bytes_bf16() / 1e9:.2f} GB of weights", file=sys.stderr, flush=True)
 
     ws = sf.new_workspace(sh)
@@ -607,13 +629,14 @@ def stack_measure(torch, sf, wl, layers, steps, args, dev, with_head=False):
     fold = torch.zeros((L, Rp), dtype=torch.uint8, device=dev)
     cnt = torch.zeros((L, 4), dtype=torch.int32, device=dev)
 
-    def run_step(s, delta):
+    def run_step(s, delta, stats=True, traces=None):
         parent, H0 = steps_in[s]
         x = H0
         for l in range(L):
             y = buf[l % 2]
             sf.verify_layer(sh, parent, lws[l], pfs[l], None, x, delta, y, ws,
-                            stats={"fold": fold[l, :R], "rec_count": cnt[l, :1]})
+                            stats={"fold": fold[l, :R], "rec_count": cnt[l, :1]} if stats else None,
+                            trace=traces[l].trace if traces else None)
             x = y
         return x
 
@@ -626,22 +649,23 @@ def stack_measure(torch, sf, wl, layers, steps, args, dev, with_head=False):
             outs.append(x.clone())
             Ms.append(cnt[:, 0].cpu().numpy().copy())
             ff.append(fold[:, :R].cpu().numpy().reshape(L, sh.n_branch, sh.block)[:, 1:].mean(axis=(1, 2)))
-        last = outs[-1]
+        last = outs[(K - 1) % S]
 
         def check(last=last, delta=delta):
             if not torch.equal(buf[(L - 1) % 2].view(torch.int16), last.view(torch.int16)):
                 raise RuntimeError(f"stack graph replay differs from the eager pass (delta {delta})")
-        ms = time_graph(torch, [lambda s=s, delta=delta: run_step(s, delta) for s in range(S)], rounds=args.rounds,
-                        warmup_s=args.warmup_seconds, check=check)
+        ms = time_graph(torch, [lambda k=k, delta=delta: run_step(k % S, delta) for k in range(K)],
+                        rounds=args.rounds, warmup_replays=-(-args.warmup // K), warmup_s=args.warmup_seconds,
+                        check=check)
         med = float(np.median(ms))
-        res[delta] = {"ms_per_step": med / S, "round_ms_per_step": [round(x / S, 5) for x in ms],
+        res[delta] = {"ms_per_step": med / K, "round_ms_per_step": [round(x / K, 5) for x in ms],
                       "M": np.mean(Ms, axis=0), "fold": np.mean(ff, axis=0),
                       "finite": all(bool(torch.isfinite(o.float()).all().item()) for o in outs)}
-        print(f"[bench] stack delta {delta}: {med / S:.3f} ms per step", file=sys.stderr, flush=True)
+        print(f"[bench] stack delta {delta}: {med / K:.3f} ms per step", file=sys.stderr, flush=True)
 
     f, d = res[wl.delta], res[0.0]
     out = {
-        "workload": wl.name, "layers": L, "steps": S,
+        "workload": wl.name, "layers": L, "steps": K, "input_steps": S,
         "value": round(R / (f["ms_per_step"] * 1e-3), 1), "unit": "branch-tokens/s",
         "ms_per_step": round(f["ms_per_step"], 5), "round_ms_per_step": f["round_ms_per_step"],
         "dense_value": round(R / (d["ms_per_step"] * 1e-3), 1), "dense_ms_per_step": round(d["ms_per_step"], 5),
@@ -650,35 +674,242 @@ def stack_measure(torch, sf, wl, layers, steps, args, dev, with_head=False):
         "us_per_layer": {"folded": round(1e3 * f["ms_per_step"] / L, 2), "dense": round(1e3 * d["ms_per_step"] / L, 2)},
         "rec_rows_mean": round(float(np.mean(f["M"])), 1),
         "rec_rows_per_layer": [round(float(v), 1) for v in f["M"]],
+        "fold_fraction_drafts": round(float(np.mean(f["fold"])), 4),
         "fold_fraction_drafts_per_layer": [round(float(v), 4) for v in f["fold"]],
         "finite_output": bool(f["finite"] and d["finite"]),
-        "config": {"hidden": D, "n_q_heads": sh.n_q_heads, "n_kv_heads": sh.n_kv_heads, "ffn": sh.ffn,
-                   "block": sh.block, "drafts": sh.n_branch - 1, "prefix": sh.prefix_len, "delta": wl.delta,
-                   "rows": R, "weight_std": list(wl.weight_std),
-                   "timing": f"HIP graph of the {S} steps x {L} layers, median of {args.rounds} event-timed replays"},
+        "config": {"hidden": D, "n_q_heads": sh.n_q_heads, "n_kv_heads": sh.n_kv_heads, "head_dim": sh.head_dim,
+                   "ffn": sh.ffn, "block": sh.block, "drafts": sh.n_branch - 1, "prefix": sh.prefix_len,
+                   "delta": wl.delta, "rows": R, "layers": L, "input_steps": S, "weight_std": list(wl.weight_std),
+                   "regime": f"cold by size ({L * sh.weight_bytes_bf16() / 1e9:.2f} GB of weights per pass)",
+                   "timing": f"HIP graph of exactly {K} passes through the {L} layers (input step k % {S}), "
+                             f"median of {args.rounds} event-timed replays"},
     }
     if with_head:
         out["pass_with_head"] = pass_leg(torch, sf, sh, wl, args, [(p, None, H) for p, H in steps_in], lws, pfs, ws,
                                          buf, fold, cnt, L, S, dev)
-    return out
+    if not keep:
+        return out
+    ctx = {"sh": sh, "L": L, "S": S, "layer_list": layer_list, "lws": lws, "pfs": pfs, "steps_in": steps_in,
+           "ws": ws, "buf": buf, "fold": fold, "cnt": cnt, "run_step": run_step, "M": {wl.delta: f["M"], 0.0: d["M"]}}
+    return out, ctx
+
+
+def stack_stage_times(torch, sf, ctx, delta, n_steps=3):
+    """Event-timed duration of every launch of every layer over n_steps eager passes, each traced
+    pass queued behind an untraced one (so no layer's first launch starts on an idle GPU).
+    Returns per-layer stage dicts (microseconds, mean over the passes) and per-layer M."""
+    import numpy as np
+
+    L, S = ctx["L"], ctx["S"]
+    timers = [sf.StageTimer() for _ in range(L)]
+    acc = [None] * L
+    Ms = []
+    n = min(n_steps, S)
+    for s in range(n):
+        ctx["run_step"]((s + 1) % S, delta, stats=False)
+        ctx["run_step"](s, delta, stats=True, traces=timers)
+        torch.cuda.synchronize()
+        Ms.append(ctx["cnt"][:, 0].cpu().numpy().copy())
+        for l in range(L):
+            t = timers[l].elapsed_ms()
+            acc[l] = t if acc[l] is None else {k: acc[l][k] + t[k] for k in t}
+    for tm in timers:
+        tm.close()
+    per_layer = [{k: 1e3 * v / n for k, v in a.items()} for a in acc]
+    return per_layer, np.mean(Ms, axis=0)
 
 
 def stack_bench(args, wl):
-    """--workload stack-*: the stack's own JSON line."""
+    """Stack workloads (the default, stack-1.5b, and stack-7b): the line's throughput is the
+    stack's; the dominant kernel's roofline and the per-launch fractions come from event timing of
+    every launch of every layer; stack-1.5b also carries the single layer (layer-1.5b) as a
+    sub-object, the flat gate and compaction, and the CPU oracle on sampled layers."""
+    import copy
+
+    import numpy as np
     import torch
 
     from sparse_layer_rho_amd import specfold as sf
+    from synth import WORKLOADS
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    st = stack_measure(torch, sf, wl, args.layers, args.stack_steps, args, dev, with_head=args.with_head)
-    out = {"metric": METRIC, "value": st["value"], "unit": "branch-tokens/s", "n_gpus": 1, "steps": st["steps"],
-           "ms_per_step": st["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "bf16",
-           "data": "synthetic (seeded random weights and prefix KV per layer, parent-linked draft hidden states per step)",
-           "config": {"workload": args.workload, **st["config"], "layers": st["layers"], "parallelism": "single GPU"},
-           "speedup_vs_dense": st["speedup_vs_dense"], "stack": st}
+    if args.counters > 0:
+        return stack_counters(torch, sf, wl, args, dev)
+    st, ctx = stack_measure(torch, sf, wl, args.layers, args.stack_steps, args, dev, with_head=args.with_head,
+                            keep=True)
+    sh, L = ctx["sh"], ctx["L"]
+    D, F = sh.hidden, sh.ffn
+    per_f, M_f = stack_stage_times(torch, sf, ctx, wl.delta)
+    per_d, M_d = stack_stage_times(torch, sf, ctx, 0.0)
+    mean_stage = lambda per: {k: float(np.mean([p[k] for p in per])) for k in per[0]}
+    st_f, st_d = mean_stage(per_f), mean_stage(per_d)
+    print("[bench] stack per-launch us (mean over layers), folded: " +
+          ", ".join(f"{k} {v:.2f}" for k, v in st_f.items()), file=sys.stderr, flush=True)
+
+    # dominant kernel: the FFN gate/up projection, every launch of the traced passes
+    gu_bytes = [2 * (2 * F * D) + 2 * m * D + 2 * m * F for m in M_f]
+    gu_us = [p["gate_up_swiglu_gemm"] for p in per_f]
+    achieved = float(np.sum(gu_bytes)) / (float(np.sum(gu_us)) * 1e-6) / 1e9
+    roofline = {"kernel": "gate_up_swiglu_gemm", "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(stack_traffic_record(wl.name)),
+                "avg_us": round(float(np.mean(gu_us)), 2), "bytes_per_launch": round(float(np.mean(gu_bytes))),
+                "launches": f"{L} layers x 3 passes, event-timed on the launch stream",
+                "tflops": round(2 * float(np.mean(M_f)) * 2 * F * D / (float(np.mean(gu_us)) * 1e-6) / 1e12, 1)}
+    Mm_f, Mm_d = float(np.mean(M_f)), float(np.mean(M_d))
+    roof_f = sum(layer_roof_us(sh, m) for m in M_f)
+    roof_d = sum(layer_roof_us(sh, m) for m in M_d)
+    out = {
+        "metric": METRIC, "value": st["value"], "unit": "branch-tokens/s", "n_gpus": 1, "steps": st["steps"],
+        "warmup": args.warmup, "ms_per_step": st["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded random weights and prefix KV per layer, parent-linked draft hidden states per step)",
+        "config": {"workload": wl.name, **st["config"], "parallelism": "single GPU"},
+        "speedup_vs_dense": st["speedup_vs_dense"],
+        "dense": {"value": st["dense_value"], "ms_per_step": st["dense_ms_per_step"]},
+        "fold_fraction_drafts": st["fold_fraction_drafts"], "rec_rows_mean": st["rec_rows_mean"],
+        "layer_roofline_frac": {"folded": round(roof_f / (st["ms_per_step"] * 1e3), 4),
+                                "dense": round(roof_d / (st["dense_ms_per_step"] * 1e3), 4)},
+        "roofline": roofline,
+        "kernel_frac_of_peak": kernel_pct(sh, st_f, Mm_f),
+        "kernel_frac_of_peak_dense": kernel_pct(sh, st_d, Mm_d),
+        "stages_us_mean_over_layers": {"folded": {k: round(v, 2) for k, v in st_f.items()},
+                                       "dense": {k: round(v, 2) for k, v in st_d.items()}},
+        "stack": st,
+    }
+    if wl.name == "stack-1.5b" and not args.no_layer:
+        a = copy.copy(args)
+        a.no_cpu_baseline, a.no_gate_flat, a.steps = True, True, 200
+        out["layer"] = layer_main(a, WORKLOADS["layer-1.5b"], emit=False)
+    if not args.no_gate_flat and wl.name == "stack-1.5b":
+        out["gate_flat"] = gate_flat_leg(torch, sf, dev)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"], out["verified"] = stack_cpu_baseline(torch, sf, ctx, wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def stack_traffic_record(name):
+    return os.path.join(ROOT, "profiles", f"gate_up_swiglu_gemm_{name}_traffic.md")
+
+
+def stack_counters(torch, sf, wl, args, dev):
+    """Counter runs of a stack: N folded then N dense passes through its layers (one per input
+    step), then a 256 MiB device copy for calibration; prints the dispatch plan (no timing)."""
+    a = argparse.Namespace(**vars(args))
+    a.steps, a.rounds, a.warmup, a.warmup_seconds = 1, 1, 0, 0.0
+    n = args.counters
+    # stack_measure's eager passes and one-replay timing come first; the plan starts after them
+    st, ctx = stack_measure(torch, sf, wl, args.layers, n, a, dev, keep=True)
+    torch.cuda.synchronize()
+    plan = []
+    for delta in (wl.delta, 0.0):
+        for s in range(n):
+            ctx["run_step"](s, delta)
+            torch.cuda.synchronize()
+        plan.append({"delta": delta, "passes": n, "layers": ctx["L"], "launches_per_layer": len(sf.stage_names()),
+                     "M_per_layer": [round(float(v), 1) for v in ctx["M"][delta]]})
+    nb = (256 << 20) // 4
+    x = torch.empty(nb, dtype=torch.float32, device=dev).uniform_()
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"counters_plan": plan, "stage_names": sf.stage_names(), "copy_bytes": 4 * nb,
+                      "workload": wl.name}), flush=True)
+
+
+def stack_cpu_baseline(torch, sf, ctx, wl, seconds):
+    """The CPU oracle on a bounded sample of the stack: the first, middle and last layers of the
+    first input step, each teacher-forced on the GPU's own input of that layer and checked
+    against the GPU's output (mask exact outside |rho - delta| < 1e-4, relative L2 <= 2e-2).
+    The stack rate is the sampled layers' mean time times the layer count.  Timings are the
+    median of up to 3 passes after one warm-up: with the BLAS threads the host gives this
+    process, with one thread (first sampled layer), and the dense pass (delta 0)."""
+    import contextlib
+    import platform
+    import statistics
+
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    import oracle
+
+    sh, L = ctx["sh"], ctx["L"]
+    R, D = sh.rows, sh.hidden
+    sample = sorted({0, L // 2, L - 1})
+    parent, H0 = ctx["steps_in"][0]
+    host = lambda t: t.float().cpu().numpy().astype(np.float64)
+    # the GPU's input and output of every sampled layer (one eager folded pass)
+    ins, outs, folds = {}, {}, {}
+    x = H0
+    for l in range(L):
+        y = ctx["buf"][l % 2]
+        st = {"fold": ctx["fold"][l, :R], "rec_count": ctx["cnt"][l, :1]}
+        if l in sample:
+            ins[l] = host(x).reshape(sh.n_branch, sh.block, D)
+        sf.verify_layer(sh, parent, ctx["lws"][l], ctx["pfs"][l], None, x, wl.delta, y, ctx["ws"], stats=st)
+        torch.cuda.synchronize()
+        if l in sample:
+            outs[l] = host(y).reshape(sh.n_branch, sh.block, D)
+            folds[l] = ctx["fold"][l, :R].cpu().numpy().reshape(sh.n_branch, sh.block).astype(bool)
+        x = y
+    checks, ok = [], True
+    wsd = {}
+    for l in sample:
+        w, pk, pv = ctx["layer_list"][l]
+        wsd[l] = ({k: host(v) for k, v in w.items()}, host(pk), host(pv))
+        wh, pkh, pvh = wsd[l]
+        rho_o, fold_o = oracle.gate(ins[l], parent, wl.delta)
+        band = np.abs(rho_o - wl.delta) < 1e-4
+        mask_ok = bool(np.array_equal(folds[l][~band], fold_o[~band]))
+        ref = oracle.verify_layer(ins[l], parent, wh, pkh, pvh, wl.delta, sh, fold=folds[l])
+        err = float(np.linalg.norm(outs[l] - ref["H_out"]) / np.linalg.norm(ref["H_out"]))
+        checks.append({"layer": l, "rel_l2": round(err, 6), "mask_match_outside_band": mask_ok})
+        ok = ok and mask_ok and err <= 2e-2
+
+    def timed(delta, limit, layers):
+        ctx_ = threadpool_limits(limits=limit) if limit else contextlib.nullcontext()
+        per = []
+        with ctx_:
+            threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+            for l in layers:
+                wh, pkh, pvh = wsd[l]
+                t0 = time.perf_counter()
+                oracle.verify_layer(ins[l], parent, wh, pkh, pvh, delta, sh)       # warm-up
+                first = time.perf_counter() - t0
+                n = 3 if 3 * first * len(layers) <= seconds else 1
+                ts = []
+                for _ in range(n):
+                    t0 = time.perf_counter()
+                    oracle.verify_layer(ins[l], parent, wh, pkh, pvh, delta, sh)
+                    ts.append(time.perf_counter() - t0)
+                per.append(statistics.median(ts))
+        return float(np.mean(per)), threads
+
+    t_all, threads = timed(wl.delta, None, sample)
+    t_one, _ = timed(wl.delta, 1, sample[:1])
+    t_dense, _ = timed(0.0, None, sample)
+    model = platform.processor() or ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = sorted({f"{p.get('internal_api')} {p.get('version')}" for p in threadpool_info()
+                   if p.get("user_api") == "blas"})
+    cpu = {"value": round(R / (t_all * L), 1), "unit": "branch-tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"float64 oracle on layers {sample} of the first input step ({R} rows, delta {wl.delta}), "
+                     f"teacher-forced on the GPU's layer inputs, {threads} BLAS threads; the stack rate is their "
+                     f"mean time per layer ({t_all:.3f} s) times {L} layers",
+           "seconds_per_layer": round(t_all, 4),
+           "one_thread": {"value": round(R / (t_one * L), 1), "seconds_per_layer": round(t_one, 4),
+                          "layers": sample[:1]},
+           "dense_delta0": {"value": round(R / (t_dense * L), 1), "seconds_per_layer": round(t_dense, 4),
+                            "speedup_of_folding": round(t_dense / t_all, 4)},
+           "cpu_model": model, "host_cpus_available": len(os.sched_getaffinity(0)), "blas": blas}
+    return cpu, {"ok": bool(ok), "layers": checks}
 
 
 def pass_leg(torch, sf, sh, wl, args, steps, lws, pfs, ws, buf, fold, cnt, L, S, dev):
