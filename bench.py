@@ -694,17 +694,18 @@ def stack_measure(torch, sf, wl, layers, steps, args, dev, with_head=False, keep
     return out, ctx
 
 
-def stack_stage_times(torch, sf, ctx, delta, n_steps=3):
-    """Event-timed duration of every launch of every layer over n_steps eager passes, each traced
-    pass queued behind an untraced one (so no layer's first launch starts on an idle GPU).
-    Returns per-layer stage dicts (microseconds, mean over the passes) and per-layer M."""
+def stack_stage_times(torch, sf, ctx, delta, n_steps=0):
+    """Event-timed duration of every launch of every layer over n_steps eager passes (default:
+    one per input step, the mix the timed graphs run), each traced pass queued behind an
+    untraced one (so no layer's first launch starts on an idle GPU).  Returns per-layer stage
+    dicts (microseconds, mean over the passes) and per-layer M."""
     import numpy as np
 
     L, S = ctx["L"], ctx["S"]
     timers = [sf.StageTimer() for _ in range(L)]
     acc = [None] * L
     Ms = []
-    n = min(n_steps, S)
+    n = min(n_steps, S) if n_steps > 0 else S
     for s in range(n):
         ctx["run_step"]((s + 1) % S, delta, stats=False)
         ctx["run_step"](s, delta, stats=True, traces=timers)
@@ -755,7 +756,7 @@ def stack_bench(args, wl):
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(stack_traffic_record(wl.name)),
                 "avg_us": round(float(np.mean(gu_us)), 2), "bytes_per_launch": round(float(np.mean(gu_bytes))),
-                "launches": f"{L} layers x 3 passes, event-timed on the launch stream",
+                "launches": f"{L} layers x {ctx['S']} passes (one per input step), event-timed on the launch stream",
                 "tflops": round(2 * float(np.mean(M_f)) * 2 * F * D / (float(np.mean(gu_us)) * 1e-6) / 1e12, 1)}
     Mm_f, Mm_d = float(np.mean(M_f)), float(np.mean(M_d))
     roof_f = sum(layer_roof_us(sh, m) for m in M_f)
