@@ -785,9 +785,46 @@ def stack_bench(args, wl):
         out["layer"] = layer_main(a, WORKLOADS["layer-1.5b"], emit=False)
     if not args.no_gate_flat and wl.name == "stack-1.5b":
         out["gate_flat"] = gate_flat_leg(torch, sf, dev)
+    if wl.name == "stack-1.5b":
+        pk = measured_peaks(torch, dev)
+        out["measured_peaks"] = pk
+        out["roofline"]["frac_of_measured_copy_rate"] = round(roofline["achieved"] / pk["hbm_copy_gbs"], 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"], out["verified"] = stack_cpu_baseline(torch, sf, ctx, wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def measured_peaks(torch, dev):
+    """Achievable rates on this machine from library kernels, as context for the vendor peaks: a
+    1 GiB device copy (HBM read + write) and a 8192^3 bf16 matrix product (hipBLASLt); each the
+    best of 5 event-timed runs after a warm-up.  (torch's reductions read more slowly than the
+    library's own gate kernel does, so they are no read-bandwidth reference.)"""
+    def best(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return min(ts)
+    n = (1 << 30) // 4
+    x = torch.empty(n, dtype=torch.float32, device=dev).uniform_()
+    y = torch.empty_like(x)
+    t_copy = best(lambda: y.copy_(x))
+    del x, y
+    m = 8192
+    a_ = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    b_ = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    t_mm = best(lambda: torch.matmul(a_, b_))
+    del a_, b_
+    return {"hbm_copy_gbs": round(2 * (1 << 30) / t_copy / 1e9, 1),
+            "bf16_matmul_tflops": round(2 * m ** 3 / t_mm / 1e12, 1),
+            "how": "best of 5 event-timed runs: torch 1 GiB device copy (bytes read + written), "
+                   "torch.matmul 8192^3 bf16 (hipBLASLt)"}
 
 
 def stack_traffic_record(name):
