@@ -48,3 +48,23 @@ def test_traffic_record_is_used_only_for_the_sources_it_was_taken_on(tmp_path, m
     # as does a missing or unreadable record
     rec_path.write_text("no record here")
     assert bench.measured_traffic() is None
+
+
+def test_default_line_is_the_layer_stack(monkeypatch):
+    """The metric is branch-tokens/s per layer stack: with no arguments bench.py measures the
+    28-layer 1.5B-shape stack (its single layer rides along as a sub-object)."""
+    monkeypatch.setattr(sys, "argv", ["bench.py"])
+    args = bench.parse()
+    from synth import WORKLOADS
+    wl = WORKLOADS[args.workload]
+    assert args.workload == "stack-1.5b" and wl.layers == 28 and wl.steps == 8
+    assert wl.shape.prefix_len == 2048 and wl.shape.hidden == 1536 and not args.no_layer
+
+
+def test_committed_traffic_records_match_the_current_gemm_sources():
+    """Both committed gate/up records (single layer, stack) were taken on these GEMM sources, so
+    the line reports their traffic; they sit within 10 % of the algorithmic bytes."""
+    for path in (bench.TRAFFIC_RECORD, bench.stack_traffic_record("stack-1.5b")):
+        rec = _record(open(path).read())
+        assert bench.measured_traffic(path) == rec["traffic_bytes"]
+        assert 5.7e7 < rec["traffic_bytes"] < 6.4e7
