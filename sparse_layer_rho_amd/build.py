@@ -30,6 +30,14 @@ FLAGS = [
 ]
 
 
+# per-source additions: the attention kernels keep their MFMA accumulators in ordinary VGPRs
+# (the softmax rescales them between products; in accumulation registers every rescale would
+# copy them out and back)
+FILE_FLAGS = {
+    "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -57,7 +65,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
 
     def compile_one(src_obj):
         src, obj = src_obj
-        cmd = [hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         _run(cmd)

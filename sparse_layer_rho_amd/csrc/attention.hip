@@ -35,6 +35,7 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kStageKeys = 128;                 // prefix keys per LDS stage
+constexpr float kLazy = 8.f;                    // softmax reference slack, log2 units
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -57,6 +58,47 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, ui
 
 // this wave's buffer loads (register and LDS) are complete
 __device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// 2^x with the hardware instruction (no rescaling of results below 2^-126: softmax weights
+// that small are below the fp32 resolution of the running sum anyway)
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// two floats -> two bf16, round to nearest even, with gfx950's v_cvt_pk_bf16_f32
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2_t));
+}
+
+__device__ __forceinline__ uint4 cvt_bf16x8(const float* f) {
+    return make_uint4(cvt_bf16x2(f[0], f[1]), cvt_bf16x2(f[2], f[3]), cvt_bf16x2(f[4], f[5]),
+                      cvt_bf16x2(f[6], f[7]));
+}
+
+// ds_read_b128 as inline asm: the compiler can neither hoist a wait above the rest of a batch
+// nor reuse a batch's registers before it lands, so all of a block's key fragments are in
+// flight together (left to itself it keeps two in flight); kf_wait<N> supplies the wait
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_u8*)(p)));
+}
+
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+
+// at most N of this wave's LDS reads outstanding; the fragments of `v` are used only after it
+template <int N, int C>
+__device__ __forceinline__ void kf_wait(u32x4 (&v)[C]) {
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(N) : "memory");
+#pragma unroll
+    for (int i = 0; i < C; ++i) asm volatile("" : "+v"(v[i]));
+}
 
 // Request NKEYS rows of K and V into sK / sV (swizzled as above).  row_off(row, k_or_v) gives
 // the element offset of a key row's first dimension, or -1 for a missing key (the host keeps
@@ -94,24 +136,57 @@ __device__ __forceinline__ void attend_block(const uint8_t* sK, const uint8_t* s
     const int g4 = lane >> 4, l16 = lane & 15;
     // Branch-free: rows past nk hold zeros (their loads were out of range), their scores are
     // masked below and their P entries are zero, so all fragment reads can be issued at once.
-    uint4 kf[4][T::KS];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-        const int r = kt * 16 + l16;
-#pragma unroll
-        for (int s = 0; s < T::KS; ++s) {
-            const int c = 4 * s + g4;
-            kf[kt][s] = (8 * c < HD) ? *reinterpret_cast<const uint4*>(sK + r * T::RB + ((c ^ T::fk(r)) << 4))
-                                     : make_uint4(0, 0, 0, 0);
-        }
-    }
     f32x4 sc[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (HD % 32 == 0) {
+        // every 32-wide k-step lies inside the row: the 4 KS reads of one k-step differ in
+        // their key tile only (fk depends on the row's low bits, the same in every tile), so
+        // they take immediate offsets; k-step s is waited for with the later ones in flight
+        u32x4 kf[T::KS][4];
 #pragma unroll
-    for (int s = 0; s < T::KS; ++s)
+        for (int s = 0; s < T::KS; ++s) {
+            const int c = 4 * s + g4;
+            const uint32_t a = lds_addr(sK) + l16 * T::RB + ((c ^ T::fk(l16)) << 4);
+            kf[s][0] = lds_read16<0>(a);
+            kf[s][1] = lds_read16<16 * T::RB>(a);
+            kf[s][2] = lds_read16<32 * T::RB>(a);
+            kf[s][3] = lds_read16<48 * T::RB>(a);
+        }
+        auto step = [&](int s) {
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) sc[kt] = mfma16x16x32(kf[kt][s], qf[s], sc[kt]);
+            for (int kt = 0; kt < 4; ++kt)
+                sc[kt] = mfma16x16x32(__builtin_bit_cast(uint4, kf[s][kt]), qf[s], sc[kt]);
+            __builtin_amdgcn_sched_barrier(0);    // k-step s's MFMAs stay ahead of the next wait
+        };
+        if constexpr (T::KS == 4) {
+            kf_wait<12>(kf[0]); step(0);
+            kf_wait<8>(kf[1]); step(1);
+            kf_wait<4>(kf[2]); step(2);
+            kf_wait<0>(kf[3]); step(3);
+        } else if constexpr (T::KS == 2) {
+            kf_wait<4>(kf[0]); step(0);
+            kf_wait<0>(kf[1]); step(1);
+        } else {
+            kf_wait<0>(kf[0]); step(0);
+        }
+    } else {
+        uint4 kf[4][T::KS];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            const int r = kt * 16 + l16;
+#pragma unroll
+            for (int s = 0; s < T::KS; ++s) {
+                const int c = 4 * s + g4;
+                kf[kt][s] = (8 * c < HD) ? *reinterpret_cast<const uint4*>(sK + r * T::RB + ((c ^ T::fk(r)) << 4))
+                                         : make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < T::KS; ++s)
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) sc[kt] = mfma16x16x32(kf[kt][s], qf[s], sc[kt]);
+    }
     // lane holds S^T[key = 16kt + 4*g4 + i][query l16]
     float bmax = kNegInf;
 #pragma unroll
@@ -125,21 +200,30 @@ __device__ __forceinline__ void attend_block(const uint8_t* sK, const uint8_t* s
         }
     bmax = fmaxf(bmax, __shfl_xor(bmax, 16, kWave));
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32, kWave));
-    const float new_m = fmaxf(run_m, bmax);
-    const float alpha = (run_m == kNegInf) ? 0.f : exp2f(run_m - new_m);
+    // The reference maximum run_m moves only when a score passes it by more than kLazy (log2
+    // units).  The state (run_m, run_l, o) is exact for any reference, and below that margin
+    // every weight exp2(s - run_m) <= 2^kLazy stays far inside fp32 and bf16, so most blocks
+    // skip rescaling o; the rescale runs when any query of the wave moves its reference.
+    const bool grow = bmax > run_m + kLazy;
+    const float new_m = grow ? bmax : run_m;
     float psum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float e = (sc[kt][i] == kNegInf) ? 0.f : exp2f(sc[kt][i] - new_m);
+            const float e = (sc[kt][i] == kNegInf) ? 0.f : fast_exp2(sc[kt][i] - new_m);
             sc[kt][i] = e;
             psum += e;
         }
-    run_l = run_l * alpha + psum;
-    run_m = new_m;
+    const bool rescale = grow && run_m != kNegInf;     // a state of zeros needs no rescale
+    if (__ballot(rescale) != 0) {                      // wave-uniform
+        const float alpha = rescale ? fast_exp2(run_m - new_m) : 1.f;
+        run_l *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < T::DT; ++dt) o[dt] *= alpha;
+        for (int dt = 0; dt < T::DT; ++dt) o[dt] *= alpha;
+    }
+    run_l += psum;
+    run_m = new_m;
     // O^T += V^T P^T over two 32-key steps; slot 8*g4 + i <-> key 32u + 4*g4 + i and
     // slot 8*g4 + 4 + i <-> key 32u + 16 + 4*g4 + i on both operands.  The A operand (V^T,
     // rows = dimensions) comes from two transposed reads of 4 keys each: lane p of the group
@@ -149,7 +233,7 @@ __device__ __forceinline__ void attend_block(const uint8_t* sK, const uint8_t* s
     for (int u = 0; u < 2; ++u) {
         const float pf[8] = {sc[2 * u][0], sc[2 * u][1], sc[2 * u][2], sc[2 * u][3],
                              sc[2 * u + 1][0], sc[2 * u + 1][1], sc[2 * u + 1][2], sc[2 * u + 1][3]};
-        const uint4 pb = pack8(pf);
+        const uint4 pb = cvt_bf16x8(pf);
         const int r0 = 32 * u + 4 * g4 + pr, r1 = r0 + 16;
         uint2 lo[T::DT], hi[T::DT];
 #pragma unroll
