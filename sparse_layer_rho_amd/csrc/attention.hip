@@ -59,6 +59,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, ui
 // this wave's buffer loads (register and LDS) are complete
 __device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// at most N of this wave's vector-memory operations are outstanding (gfx9 s_waitcnt: vmcnt
+// bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+template <int N>
+__device__ __forceinline__ void vm_wait_le_states() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // 2^x with the hardware instruction (no rescaling of results below 2^-126: softmax weights
 // that small are below the fp32 resolution of the running sum anyway)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -103,24 +111,45 @@ __device__ __forceinline__ void kf_wait(u32x4 (&v)[C]) {
 // Request NKEYS rows of K and V into sK / sV (swizzled as above).  row_off(row, k_or_v) gives
 // the element offset of a key row's first dimension, or -1 for a missing key (the host keeps
 // every view under 1 GB, so offsets fit in 32 bits).  Load i of the
-// NKEYS*CH/64 per tensor is issued by wave i % NW (NW waves in the workgroup).
-template <int HD, int NKEYS, int NW, typename RowOff>
+// NKEYS*CH/64 per tensor is issued by wave i % NW (NW waves in the workgroup).  OFFS_FIRST:
+// every offset is formed before the first load -- for a row_off that reads LDS, which the
+// compiler would otherwise re-read after each load into LDS (one round trip per load).
+template <int HD, int NKEYS, int NW, bool OFFS_FIRST, typename RowOff>
 __device__ __forceinline__ void request_rows(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
                                              uint8_t* sK, uint8_t* sV, RowOff row_off) {
     using T = AttnTile<HD>;
     constexpr int kLoads = NKEYS * T::CH / 64;
+    constexpr int kPer = (kLoads + NW - 1) / NW;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-#pragma unroll
-    for (int t = 0; t < (kLoads + NW - 1) / NW; ++t) {
+    auto offsets = [&](int t, uint32_t& ok_, uint32_t& ov) {
         const int i = wave + NW * t;
-        if (i >= kLoads) break;                    // wave-uniform
         const int q = i * 64 + lane;
         const int row = q / T::CH, pos = q % T::CH;
-        const int ek = row_off(row, 0), ev = row_off(row, 1);
-        const uint32_t ok_ = ek < 0 ? kOob : static_cast<uint32_t>((ek + 8 * (pos ^ T::fk(row))) * 2);
-        const uint32_t ov = ev < 0 ? kOob : static_cast<uint32_t>((ev + 8 * (pos ^ T::fv(row))) * 2);
-        dma16(rk, sK + i * 1024, ok_);
-        dma16(rv, sV + i * 1024, ov);
+        const int ek = i < kLoads ? row_off(row, 0) : -1, ev = i < kLoads ? row_off(row, 1) : -1;
+        ok_ = ek < 0 ? kOob : static_cast<uint32_t>((ek + 8 * (pos ^ T::fk(row))) * 2);
+        ov = ev < 0 ? kOob : static_cast<uint32_t>((ev + 8 * (pos ^ T::fv(row))) * 2);
+    };
+    if constexpr (OFFS_FIRST) {
+        uint32_t ok_[kPer], ov[kPer];
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) offsets(t, ok_[t], ov[t]);
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) {
+            const int i = wave + NW * t;
+            if (i >= kLoads) break;                // wave-uniform
+            dma16(rk, sK + i * 1024, ok_[t]);
+            dma16(rv, sV + i * 1024, ov[t]);
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) {
+            const int i = wave + NW * t;
+            if (i >= kLoads) break;                // wave-uniform
+            uint32_t ok_, ov;
+            offsets(t, ok_, ov);
+            dma16(rk, sK + i * 1024, ok_);
+            dma16(rv, sV + i * 1024, ov);
+        }
     }
 }
 
@@ -303,7 +332,7 @@ __global__ __launch_bounds__(128 * QT) void attn_prefix_kernel(const AttnArgs a)
     const int vst = static_cast<int>(a.pv_st), vbase = g * static_cast<int>(a.pv_sh);
     auto request_stage = [&](int kb, int buf) {
         uint8_t* sK = smem + buf * 2 * kStageBytes;
-        request_rows<HD, kStageKeys, 2 * QT>(rk, rv, sK, sK + kStageBytes, [&](int row, int which) -> int {
+        request_rows<HD, kStageKeys, 2 * QT, false>(rk, rv, sK, sK + kStageBytes, [&](int row, int which) -> int {
             const int key = kb + row;
             return key >= key1 ? -1 : (which == 0 ? key * kst + kbase : key * vst + vbase);
         });
@@ -395,7 +424,7 @@ __global__ __launch_bounds__(64) void attn_block_kernel(const AttnArgs a) {
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_c, rows_bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_c, rows_bytes);
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q_c, static_cast<uint32_t>(static_cast<size_t>(a.m_cap) * a.Hq * HD * 2));
-    request_rows<HD, 64, 1>(rk, rv, sK, sV, [&](int row, int) -> int {
+    request_rows<HD, 64, 1, true>(rk, rv, sK, sV, [&](int row, int) -> int {
         const int s = row < N ? sSlot[row] : -1;
         return s < 0 ? -1 : (s * a.Hkv + g) * HD;
     });
@@ -429,8 +458,13 @@ __global__ __launch_bounds__(64) void attn_block_kernel(const AttnArgs a) {
                 co[b][dt] = buf_loadf4(ro, ok ? (base * HD + dt * 16 + 4 * (lane >> 4)) * 4 : kOob);
         }
     };
+    // the states are requested last, so waiting until only they are outstanding means the
+    // keys (in LDS) and the query have landed; the block part runs while the states arrive
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
     load_states(0);
-    vm_drain();
+    __builtin_amdgcn_sched_barrier(0);
+    vm_wait_le_states<kBatch * (1 + T::DT)>();
     __syncthreads();
     if (!active) return;
 
@@ -464,7 +498,7 @@ __global__ __launch_bounds__(64) void attn_block_kernel(const AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < T::DT; ++dt) {
         const f32x4 v = o[dt] * invL;
-        *reinterpret_cast<uint2*>(dst + dt * 16) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        *reinterpret_cast<uint2*>(dst + dt * 16) = make_uint2(cvt_bf16x2(v[0], v[1]), cvt_bf16x2(v[2], v[3]));
     }
     if (a.lse && (lane >> 4) == 0)
         a.lse[static_cast<size_t>(row) * a.Hq + h] = bad ? __builtin_nanf("") : (run_m + log2f(run_l)) * 0.69314718055994531f;
