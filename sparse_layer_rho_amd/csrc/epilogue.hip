@@ -24,16 +24,28 @@ __device__ __forceinline__ int clamp_m(const int32_t* m_count, int cap) {
     return M < 0 ? 0 : (M > cap ? cap : M);
 }
 
-// sum over splits s < S, in ascending order, of the float4 at byte offset base + s * stride
+// the float4s at byte offset base + s * stride for splits s < S (zeros past S) ...
 template <int SPL>
-__device__ __forceinline__ f32x4 sum_splits(__amdgpu_buffer_rsrc_t r, uint32_t base, uint32_t stride, int S) {
-    f32x4 v[SPL];
+__device__ __forceinline__ void load_splits(f32x4 (&v)[SPL], __amdgpu_buffer_rsrc_t r, uint32_t base, uint32_t stride,
+                                            int S) {
 #pragma unroll
     for (int s = 0; s < SPL; ++s) v[s] = buf_loadf4(r, s < S ? base + s * stride : kOob);
+}
+
+// ... and their sum in ascending split order
+template <int SPL>
+__device__ __forceinline__ f32x4 add_splits(const f32x4 (&v)[SPL]) {
     f32x4 acc = v[0];
 #pragma unroll
     for (int s = 1; s < SPL; ++s) acc += v[s];
     return acc;
+}
+
+template <int SPL>
+__device__ __forceinline__ f32x4 sum_splits(__amdgpu_buffer_rsrc_t r, uint32_t base, uint32_t stride, int S) {
+    f32x4 v[SPL];
+    load_splits<SPL>(v, r, base, stride, S);
+    return add_splits<SPL>(v);
 }
 
 __device__ __forceinline__ void unpack4(const uint2 v, float* f) {
@@ -54,8 +66,6 @@ __global__ __launch_bounds__(1024) void qkv_epilogue_kernel(const QkvEpiArgs a) 
     const int heads = a.Hq + 2 * a.Hkv, half = a.hd >> 1, q4 = a.hd >> 3;
     const int u = threadIdx.x;
     if (m >= clamp_m(a.m_count, a.m_cap) || u >= heads * q4) return;
-    const int row = a.rec_rows[m];
-    const bool ok = row >= 0 && row < a.R;
     const int nq = heads * a.hd;
     const int hh = u / q4, j0 = (u - hh * q4) * 4;
     const int c1 = hh * a.hd + j0;
@@ -63,14 +73,25 @@ __global__ __launch_bounds__(1024) void qkv_epilogue_kernel(const QkvEpiArgs a) 
         make_rsrc(a.part, static_cast<uint32_t>(static_cast<size_t>(a.splits) * a.m_cap * nq * 4));
     const uint32_t stride = static_cast<uint32_t>(a.m_cap) * nq * 4;
     const uint32_t base = (static_cast<uint32_t>(m) * nq + c1) * 4;
-    // the rotation angles (P + n) theta^(-2j/d), formed in double, are computed before the
-    // partial sums so the frequency table is read in the same round trip as the partials
+    // one round trip: the slot's row, the frequency table and the partials are all requested
+    // before any of them is used (the scheduling barrier keeps the compiler from waiting for
+    // the row before it issues the rest)
+    const int row = a.rec_rows[m];
+    double inv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) inv[e] = a.inv_freq[j0 + e];
+    f32x4 p1[SPL], p2[SPL];
+    load_splits<SPL>(p1, rP, base, stride, a.splits);
+    load_splits<SPL>(p2, rP, base + half * 4, stride, a.splits);
+    __builtin_amdgcn_sched_barrier(0);
+    const bool ok = row >= 0 && row < a.R;
+    // the rotation angles (P + n) theta^(-2j/d), formed in double
     const double pos = static_cast<double>(a.P + (ok ? row % a.N : 0));
     double ang[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ang[e] = pos * a.inv_freq[j0 + e];
-    f32x4 x1 = sum_splits<SPL>(rP, base, stride, a.splits);
-    f32x4 x2 = sum_splits<SPL>(rP, base + half * 4, stride, a.splits);
+    for (int e = 0; e < 4; ++e) ang[e] = pos * inv[e];
+    f32x4 x1 = add_splits<SPL>(p1);
+    f32x4 x2 = add_splits<SPL>(p2);
     if (!ok) x1 = x2 = f32x4{1.f, 1.f, 1.f, 1.f} * __builtin_nanf("");
     float y1[4], y2[4];
     if (hh < a.Hq + a.Hkv) {
@@ -144,7 +165,8 @@ __global__ __launch_bounds__(1024) void oproj_epilogue_kernel(const float* __res
     if ((tid & 63) == 0) s_ss[tid >> 6] = ss;
     __syncthreads();
     float tot = 0.f;
-    for (int w = 0; w < (B >> 6); ++w) tot += s_ss[w];
+#pragma unroll
+    for (int w = 0; w < 16; ++w) tot += w < (B >> 6) ? s_ss[w] : 0.f;   // one LDS round trip
     const float inv = 1.0f / sqrtf(tot / static_cast<float>(D) + eps);
 #pragma unroll
     for (int k = 0; k < MAXU; ++k) {
@@ -171,40 +193,45 @@ __global__ __launch_bounds__(1024) void down_epilogue_kernel(const float* __rest
     __shared__ int s_rows[kMaxBranches];
     __shared__ int s_cnt;
     const int b = blockIdx.x, tid = threadIdx.x, B = blockDim.x;
-    const int M = clamp_m(m_count, m_cap);
     const int R = nb * N;
     const int D4 = D >> 2;
-    if (b < R) {
-        const int sb = src_slot[b];
-        if (sb < 0 || sb >= M) {
-            const float nan = __builtin_nanf("");
-            for (int c4 = tid; c4 < D4; c4 += B)
-                *reinterpret_cast<uint2*>(H_out + static_cast<size_t>(b) * D + 4 * c4) =
-                    make_uint2(pack_bf16x2(nan, nan), pack_bf16x2(nan, nan));
-        }
+    // first round trip: the recompute count, this row's source slot and this slot's row
+    const int M = clamp_m(m_count, m_cap);
+    const int sb = b < R ? src_slot[b] : 0;
+    const int row = b < m_cap ? rec_rows[b] : -1;
+    if (b < R && (sb < 0 || sb >= M)) {
+        const float nan = __builtin_nanf("");
+        for (int c4 = tid; c4 < D4; c4 += B)
+            *reinterpret_cast<uint2*>(H_out + static_cast<size_t>(b) * D + 4 * c4) =
+                make_uint2(pack_bf16x2(nan, nan), pack_bf16x2(nan, nan));
     }
-    if (b >= M) return;
-    const int row = rec_rows[b];
-    if (row < 0 || row >= R) return;
+    if (b >= M || row < 0 || row >= R) return;
     const int n = row % N;
-    if (tid == 0) s_cnt = 0;
-    __syncthreads();
-    if (tid < nb) {
-        const int r = tid * N + n;
-        if (src_slot[r] == b) s_rows[atomicAdd(&s_cnt, 1)] = r;
-    }
+    // second round trip: the slot's partials and the source slots of every row at position n
     const __amdgpu_buffer_rsrc_t rP = make_rsrc(part, static_cast<uint32_t>(static_cast<size_t>(splits) * m_cap * D * 4));
     const __amdgpu_buffer_rsrc_t rH = make_rsrc(h_mid, static_cast<uint32_t>(static_cast<size_t>(R) * D * 2));
     const uint32_t stride = static_cast<uint32_t>(m_cap) * D * 4;
-    f32x4 f[MAXU];
+    const int cand = tid < nb ? src_slot[tid * N + n] : -1;   // first, so it is waited for alone
+    f32x4 pv[MAXU][SPL];
 #pragma unroll
     for (int k = 0; k < MAXU; ++k) {
         const int u = tid + k * B;
-        f[k] = sum_splits<SPL>(rP, u < D4 ? (static_cast<uint32_t>(b) * D + 4 * u) * 4 : kOob, stride, splits);
+        load_splits<SPL>(pv[k], rP, u < D4 ? (static_cast<uint32_t>(b) * D + 4 * u) * 4 : kOob, stride, splits);
     }
+    if (tid == 0) s_cnt = 0;
     __syncthreads();
-    const int cnt = s_cnt;
+    if (cand == b) s_rows[atomicAdd(&s_cnt, 1)] = tid * N + n;
+    f32x4 f[MAXU];
+#pragma unroll
+    for (int k = 0; k < MAXU; ++k) f[k] = add_splits<SPL>(pv[k]);
+    __syncthreads();
+    const int cnt = __builtin_amdgcn_readfirstlane(s_cnt);      // uniform: scalar loop control
     for (int t0 = 0; t0 < cnt; t0 += kBatch) {
+        // the batch's rows from LDS in one round trip (indices clamped, so no read depends on a
+        // branch), then their residual rows in one more
+        int rows[kBatch];
+#pragma unroll
+        for (int t = 0; t < kBatch; ++t) rows[t] = s_rows[min(t0 + t, cnt - 1)];
         uint2 hv[kBatch][MAXU];
 #pragma unroll
         for (int t = 0; t < kBatch; ++t)
@@ -212,7 +239,7 @@ __global__ __launch_bounds__(1024) void down_epilogue_kernel(const float* __rest
             for (int k = 0; k < MAXU; ++k) {
                 const int u = tid + k * B;
                 const bool valid = t0 + t < cnt && u < D4;
-                hv[t][k] = buf_load8(rH, valid ? (static_cast<uint32_t>(s_rows[valid ? t0 + t : 0]) * D + 4 * u) * 2 : kOob);
+                hv[t][k] = buf_load8(rH, valid ? (static_cast<uint32_t>(rows[t]) * D + 4 * u) * 2 : kOob);
             }
 #pragma unroll
         for (int t = 0; t < kBatch; ++t)
@@ -224,7 +251,7 @@ __global__ __launch_bounds__(1024) void down_epilogue_kernel(const float* __rest
                 unpack4(hv[t][k], h);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) h[e] += f[k][e];
-                *reinterpret_cast<uint2*>(H_out + static_cast<size_t>(s_rows[t0 + t]) * D + 4 * u) = pack4(h);
+                *reinterpret_cast<uint2*>(H_out + static_cast<size_t>(rows[t]) * D + 4 * u) = pack4(h);
             }
     }
 }
