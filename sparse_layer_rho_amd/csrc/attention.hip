@@ -28,6 +28,7 @@
 // query's statistics and the P V product O^T = V^T P^T takes P straight from registers
 // (the key order inside a 32-key step is permuted identically on both operands).
 #include "kernels.h"
+#include "lanes.h"
 
 namespace specfold {
 
@@ -227,8 +228,7 @@ __device__ __forceinline__ void attend_block(const uint8_t* sK, const uint8_t* s
             sc[kt][i] = v;
             bmax = fmaxf(bmax, v);
         }
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16, kWave));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, kWave));
+    bmax = max_rows4(bmax);                        // over the query's four lanes
     // The reference maximum run_m moves only when a score passes it by more than kLazy (log2
     // units).  The state (run_m, run_l, o) is exact for any reference, and below that margin
     // every weight exp2(s - run_m) <= 2^kLazy stays far inside fp32 and bf16, so most blocks
@@ -384,8 +384,7 @@ __global__ __launch_bounds__(128 * QT) void attn_prefix_kernel(const AttnArgs a)
             for (int e = 0; e < 4; ++e) o[dt][e] = o[dt][e] * w0 + xs[(dt * 4 + e) * 64] * w1;
         run_m = nm;
     }
-    run_l += __shfl_xor(run_l, 16, kWave);
-    run_l += __shfl_xor(run_l, 32, kWave);
+    run_l = sum_rows4(run_l);
     if (!qvalid) return;
     const size_t base = (static_cast<size_t>(chunk) * a.m_cap + m) * a.Hq + h;
     if ((lane >> 4) == 0)
@@ -473,8 +472,7 @@ __global__ __launch_bounds__(64) void attn_block_kernel(const AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < T::DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     attend_block<HD>(sK, sV, N, qf, a.scale_log2, run_m, run_l, o);
-    run_l += __shfl_xor(run_l, 16, kWave);
-    run_l += __shfl_xor(run_l, 32, kWave);
+    run_l = sum_rows4(run_l);
 
     // merge the prefix chunk states in ascending chunk order by online log-sum-exp rescaling
     for (int c0 = 0; c0 < a.n_chunks; c0 += kBatch) {

@@ -14,6 +14,7 @@
 // partials, rounded up; splits past the last read zeros) before it adds anything, so a kernel
 // costs one memory round trip instead of one per split.
 #include "kernels.h"
+#include "lanes.h"
 
 namespace specfold {
 
@@ -161,7 +162,7 @@ __global__ __launch_bounds__(1024) void oproj_epilogue_kernel(const float* __res
         }
     }
     if (!xn) return;
-    ss = wave_sum(ss);
+    ss = wave_sum_dpp(ss);
     if ((tid & 63) == 0) s_ss[tid >> 6] = ss;
     __syncthreads();
     float tot = 0.f;

@@ -4,7 +4,7 @@
 // rho = |H_i[n] - H_p[n]| / |H_p[n]| and the row folds when rho <= delta; main rows bypass
 // the gate [SpecFold summary, App. B].  One 64-lane wave owns one row: the lanes stream the
 // child and parent rows in 16-byte chunks (coalesced), accumulate in fp32 and reduce with
-// cross-lane shuffles.  The same loads give the row's sum of squares, i.e. its RMSNorm scale,
+// DPP lane moves.  The same loads give the row's sum of squares, i.e. its RMSNorm scale,
 // and -- when asked -- the normalised row the QKV projection consumes (RMSNorm weight applied,
 // rounded to bf16), so the layer input is read from HBM once.
 //
@@ -17,6 +17,7 @@
 // (at most n_branch steps; branch 0 always terminates) -- rows are independent, so one
 // order-free launch covers all branches.
 #include "kernels.h"
+#include "lanes.h"
 
 namespace specfold {
 
@@ -109,9 +110,9 @@ __device__ __forceinline__ void gate_finish(const GateParams& p, int row, int la
             b += yv[e] * yv[e];
         }
     }
-    a = wave_sum(a);
-    b = wave_sum(b);
-    ss = wave_sum(ss);
+    a = wave_sum_dpp(a);
+    b = wave_sum_dpp(b);
+    ss = wave_sum_dpp(ss);
     const float inv = 1.0f / sqrtf(ss / static_cast<float>(p.D) + p.eps);
     if (lane == 0) {
         float r = 0.f;
