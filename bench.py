@@ -796,8 +796,9 @@ def stack_bench(args, wl):
 
 def measured_peaks(torch, dev):
     """Achievable rates on this machine from library kernels, as context for the vendor peaks: a
-    1 GiB device copy (HBM read + write) and a 8192^3 bf16 matrix product (hipBLASLt); each the
-    best of 5 event-timed runs after a warm-up.  (torch's reductions read more slowly than the
+    1 GiB device copy (HBM read + write), copies within a 128 MiB working set (last-level
+    cache) and a 8192^3 bf16 matrix product (hipBLASLt); each the best of 5 event-timed runs
+    after a warm-up.  (torch's reductions read more slowly than the
     library's own gate kernel does, so they are no read-bandwidth reference.)"""
     def best(fn, reps=5):
         fn()
@@ -816,14 +817,27 @@ def measured_peaks(torch, dev):
     y = torch.empty_like(x)
     t_copy = best(lambda: y.copy_(x))
     del x, y
+    # the same with a 128 MiB working set (two 64 MiB buffers), copied 8 times back to back:
+    # after the first copy both stay in the 256 MB last-level cache (MALL)
+    n2 = (64 << 20) // 4
+    x2 = torch.empty(n2, dtype=torch.float32, device=dev).uniform_()
+    y2 = torch.empty_like(x2)
+
+    def copies():
+        for _ in range(8):
+            y2.copy_(x2)
+    t_mall = best(copies) / 8
+    del x2, y2
     m = 8192
     a_ = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
     b_ = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
     t_mm = best(lambda: torch.matmul(a_, b_))
     del a_, b_
     return {"hbm_copy_gbs": round(2 * (1 << 30) / t_copy / 1e9, 1),
+            "mall_copy_gbs": round(2 * (64 << 20) / t_mall / 1e9, 1),
             "bf16_matmul_tflops": round(2 * m ** 3 / t_mm / 1e12, 1),
-            "how": "best of 5 event-timed runs: torch 1 GiB device copy (bytes read + written), "
+            "how": "best of 5 event-timed runs: torch 1 GiB device copy (bytes read + written); "
+                   "the mean of 8 back-to-back 64 MiB copies between two cache-resident buffers; "
                    "torch.matmul 8192^3 bf16 (hipBLASLt)"}
 
 
