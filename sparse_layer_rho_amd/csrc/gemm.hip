@@ -118,13 +118,26 @@ __device__ __forceinline__ void block_barrier() {
 
 // Compact the recompute rows (fold == 0) of R rows into s_rows (ascending), 256 threads.
 // Returns M.  When publish, also writes the global list, offsets, row_slot and fold sources.
-__device__ int compact_in_lds(const GemmArgs& p, int32_t* s_rows, int* s_tot, bool publish) {
+// The flags of the first kPre * 256 rows are requested in one batch (one memory round trip
+// instead of one per 256 rows) and kept in LDS (s_fold), with the parent map, so the source
+// walks of the publishing workgroup read no global memory.
+__device__ int compact_in_lds(const GemmArgs& p, int32_t* s_rows, uint8_t* s_fold, int* s_tot, bool publish) {
+    constexpr int kPre = 4;
+    __shared__ int s_par[kMaxBranches];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int R = p.fc_R, N = p.fc_N;
+    if (publish && tid < p.fc_nb) s_par[tid] = p.fc_par.p[tid];
+    uint8_t pre[kPre];
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+        const int r = k * 256 + tid;
+        pre[k] = r < R ? p.fc_fold[r] : 1;
+    }
     int base = 0;
-    for (int r0 = 0; r0 < R; r0 += 256) {
+    auto step = [&](int r0, uint8_t f) {
         const int r = r0 + tid;
-        const bool rec = (r < R) && (p.fc_fold[r] == 0);
+        const bool rec = (r < R) && (f == 0);
+        if (r < R) s_fold[r] = f;
         const uint64_t m = __ballot(rec);
         const int excl = __popcll(m & ((1ull << lane) - 1ull));
         if (lane == 0) s_tot[wave] = __popcll(m);
@@ -140,7 +153,11 @@ __device__ int compact_in_lds(const GemmArgs& p, int32_t* s_rows, int* s_tot, bo
         }
         base += t0 + t1 + t2 + t3;
         __syncthreads();
-    }
+    };
+#pragma unroll
+    for (int k = 0; k < kPre; ++k)
+        if (k * 256 < R) step(k * 256, pre[k]);
+    for (int r0 = kPre * 256; r0 < R; r0 += 256) step(r0, r0 + tid < R ? p.fc_fold[r0 + tid] : 1);
     if (publish) {
         if (tid == 0) {
             p.fc_rec_count[0] = base;
@@ -152,7 +169,7 @@ __device__ int compact_in_lds(const GemmArgs& p, int32_t* s_rows, int* s_tot, bo
         for (int r = tid; r < R; r += 256) {
             const int i = r / N, n = r - i * N;
             int j = i;
-            for (int s = 0; s < p.fc_nb && j > 0 && p.fc_fold[j * N + n] != 0; ++s) j = p.fc_par.p[j];
+            for (int s = 0; s < p.fc_nb && j > 0 && s_fold[j * N + n] != 0; ++s) j = s_par[j];
             const int src_row = j * N + n;
             int lo = 0, hi = base;                   // first slot with s_rows[slot] >= src_row
             while (lo < hi) {
@@ -441,7 +458,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
     int32_t* s_rows = reinterpret_cast<int32_t*>(smem + T::LDS);
     int M;
     if (p.fc_fold != nullptr) {
-        M = compact_in_lds(p, s_rows, s_tot, blockIdx.x == 0 && blockIdx.y == 0);   // (group 0, chunk 0)
+        uint8_t* s_fold = reinterpret_cast<uint8_t*>(s_rows + p.fc_R);
+        M = compact_in_lds(p, s_rows, s_fold, s_tot, blockIdx.x == 0 && blockIdx.y == 0);   // (group 0, chunk 0)
     } else {
         M = p.m_count ? p.m_count[0] : p.m_fixed;
     }
@@ -505,7 +523,8 @@ hipError_t launch_shape(GemmArgs a, const GemmCfg& c, int splits, hipStream_t st
     a.min_chunks = c.min_chunks;
     a.m_chunks = (a.m_cap + T::MP - 1) / T::MP;
     if (a.m_chunks < 1) a.m_chunks = 1;
-    const size_t lds = static_cast<size_t>(T::LDS) + (a.fc_fold ? static_cast<size_t>(a.fc_R) * 4 : 0);
+    // the fused compaction's row list (4 bytes per row) and flags (1 byte per row)
+    const size_t lds = static_cast<size_t>(T::LDS) + (a.fc_fold ? static_cast<size_t>(a.fc_R) * 5 : 0);
     auto kern = gemm_kernel<NTW, WN, TM, KSUB, NBW, NBA, EPI>;
     static std::atomic<size_t> cap{0};
     hipError_t e = raise_lds_cap(reinterpret_cast<const void*>(kern), lds, cap);
