@@ -299,15 +299,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int M, const 
                   static_cast<uint32_t>(wlk[q] * 2);
     }
     const int alk = ((lane & 7) ^ ((lane >> 3) & 7)) * 8;
+    // the rows' sources first, every lookup of the wave issued before any is used (a clamped
+    // index keeps them unconditional), then the offsets: one round trip for a row list in
+    // memory instead of one per load
+    int src[QA];
 #pragma unroll
     for (int q = 0; q < QA; ++q) {
         const int m = (q * 4 + wave) * 8 + (lane >> 3);
-        uint32_t o = kOobRow;
-        if (m < mrows) {
-            const int src = fused ? s_rows[m0 + m] : (p.a_rows ? p.a_rows[m0 + m] : m0 + m);
-            if (src >= 0 && src < p.a_row_limit) o = static_cast<uint32_t>(static_cast<size_t>(src) * p.lda * 2);
-        }
-        aoff[q] = o + static_cast<uint32_t>(alk * 2);
+        const int mc = m0 + (m < mrows ? m : 0);
+        src[q] = fused ? s_rows[mc] : (p.a_rows ? p.a_rows[mc] : mc);
+    }
+#pragma unroll
+    for (int q = 0; q < QA; ++q) {
+        const int m = (q * 4 + wave) * 8 + (lane >> 3);
+        const bool ok = m < mrows && src[q] >= 0 && src[q] < p.a_row_limit;
+        aoff[q] = (ok ? static_cast<uint32_t>(static_cast<size_t>(src[q]) * p.lda * 2) : kOobRow) +
+                  static_cast<uint32_t>(alk * 2);
     }
     uint8_t* const wring = smem;
     uint8_t* const aring = smem + NBW * T::WSLOT;
