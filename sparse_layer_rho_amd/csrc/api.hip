@@ -332,8 +332,9 @@ hipError_t run_qkv(const Dims& d, const Layout& L, const uint16_t* xn, const int
 hipError_t run_attention(const Dims& d, const Layout& L, const uint16_t* q_c, const uint16_t* k_c,
                          const uint16_t* v_c, const int32_t* rec_count, const int32_t* src_slot,
                          const specfold_prefix_kv* pf, uint16_t* attn, float* lse, void* ws,
-                         hipStream_t st, Tracer* tr) {
+                         hipStream_t st, Tracer* tr, int plan_rows = 0) {
     AttnArgs a{};
+    a.plan_rows = plan_rows;
     a.q_c = q_c; a.k_c = k_c; a.v_c = v_c; a.m_count = rec_count; a.m_cap = d.R; a.src_slot = src_slot;
     a.nb = d.nb; a.N = d.N; a.Hq = d.Hq; a.Hkv = d.Hkv; a.hd = d.hd; a.P = d.P;
     if (d.P > 0) {
@@ -457,8 +458,10 @@ int launch_layer(const Dims& d, const Layout& L, const ParentMap& par, const spe
     uint16_t* xn2 = at<uint16_t>(ws, L.xn2);
     if ((he = run_qkv(d, L, g.xn, rec_rows, rec_count, w->w_qkv, q_c, k_c, v_c, ws, st, &tr, &fc)) != hipSuccess)
         return hip_status(he);
-    if ((he = run_attention(d, L, q_c, k_c, v_c, rec_count, src_slot, prefix, attn, nullptr, ws, st, &tr)) !=
-        hipSuccess)
+    // a threshold that folds only exact copies (delta <= 0, or NaN) leaves every row recomputing
+    const int plan_rows = delta > 0.0f ? (d.R + 1) / 2 : d.R;
+    if ((he = run_attention(d, L, q_c, k_c, v_c, rec_count, src_slot, prefix, attn, nullptr, ws, st, &tr,
+                            plan_rows)) != hipSuccess)
         return hip_status(he);
     if ((he = run_out_proj(d, L, attn, H_in, w->w_o, h_mid, w->ln2, xn2, ws, st, &tr)) != hipSuccess)
         return hip_status(he);

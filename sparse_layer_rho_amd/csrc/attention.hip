@@ -522,14 +522,17 @@ hipError_t launch_prefix_qt(const AttnArgs& a, hipStream_t st) {
 // CU read each block from LDS); four once two would need a second round, where sharing each
 // K/V stage over more queries pays.  A chunk of one stage leaves room for two workgroups per
 // CU, a longer one (two stage buffers) for one.  The recompute count is known on the device
-// only; the tiles are sized for half the rows recomputing.  Measured: the 7B layer at P = 2048
+// only; the tiles are planned for plan_rows recompute rows (the layer passes all rows when its
+// threshold folds nothing but exact copies, else half of them, the pages' fold ratios being
+// 0.5-0.7).  Measured: the 7B layer at P = 2048
 // (M = 100, 352 busy two-tile workgroups) 28.3 against 18.9 us with four; the 1.5B layer at
 // P = 2048 (M = 108, 168 busy) 14.0 against 15.5.
 template <int HD>
 hipError_t launch_prefix_hd(const AttnArgs& a, hipStream_t st) {
     const int G = a.Hq / a.Hkv;
     const long slots = a.chunk_len > kStageKeys ? 256 : 512;
-    const long busy2 = static_cast<long>(a.n_chunks) * a.Hkv * ((((a.m_cap + 1) / 2) * G + 31) / 32);
+    const int rows = a.plan_rows > 0 ? (a.plan_rows < a.m_cap ? a.plan_rows : a.m_cap) : (a.m_cap + 1) / 2;
+    const long busy2 = static_cast<long>(a.n_chunks) * a.Hkv * ((rows * G + 31) / 32);
     return busy2 <= slots ? launch_prefix_qt<HD, 2>(a, st) : launch_prefix_qt<HD, 4>(a, st);
 }
 

@@ -151,6 +151,7 @@ struct AttnArgs {
     uint16_t* attn;          // [R][Hq*hd]
     float* lse;              // nullable [R][Hq]
     float scale_log2;        // log2(e) / sqrt(hd)
+    int plan_rows;           // recompute rows the prefix tiles are planned for (0: half of m_cap)
 };
 hipError_t launch_attn_prefix(const AttnArgs& a, hipStream_t st);
 // rows kernels either side of the stack
