@@ -51,6 +51,23 @@ def test_draft_tree_shapes_match_oracle(kind):
     print(f"{kind}: rel L2 {err:.2e}, M = {res['rec_count']} of {case.shape.rows}")
 
 
+def test_stack_shape_layer_dense_and_folded_match_oracle():
+    """One layer of the 28-layer stack's shape (P = 2048, 512-key prefix chunks) at delta = 0,
+    where every row recomputes and the prefix tiles are planned for all rows (four query tiles
+    per workgroup), and at the stack's delta (two); the main branch's output is the same bits
+    either way, since tile plans change no sums."""
+    wl = WORKLOADS["stack-1.5b"]
+    case = LayerCase.workload("stack-1.5b")
+    dense = case.run(0.0)
+    assert dense["rec_count"] == case.shape.rows
+    case.check(0.0, dense)
+    folded = case.run(wl.delta)
+    assert folded["rec_count"] < case.shape.rows
+    case.check(wl.delta, folded)
+    N = case.shape.block
+    assert np.array_equal(dense["H_out_bits"][:N], folded["H_out_bits"][:N])
+
+
 def test_delta_zero_is_dense_per_branch():
     wl = WORKLOADS["tiny"]
     case = LayerCase.workload("tiny")
