@@ -98,11 +98,12 @@ __global__ __launch_bounds__(1024) void qkv_epilogue_kernel(const QkvEpiArgs a) 
     if (hh < a.Hq + a.Hkv) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            // angle reduced to [-pi, pi]
-            const double twopi = 6.283185307179586476925286766559;
-            const float red = static_cast<float>(ang[e] - twopi * rint(ang[e] / twopi));
-            float sn, cs;
-            sincosf(red, &sn, &cs);
+            // the angle in revolutions, reduced to [-1/2, 1/2] in double, then the hardware
+            // sine and cosine, which take revolutions (absolute error near 2^-20, far below the
+            // bf16 rounding of the rotated values)
+            const double rev = ang[e] * 0.15915494309189533577;     // 1 / (2 pi)
+            const float red = static_cast<float>(rev - rint(rev));
+            const float sn = __builtin_amdgcn_sinf(red), cs = __builtin_amdgcn_cosf(red);
             y1[e] = x1[e] * cs - x2[e] * sn;
             y2[e] = x2[e] * cs + x1[e] * sn;
         }

@@ -412,11 +412,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int M, const 
             for (int j = 0; j < NTW; j += 2) {
                 const int col = c0 + (wn * (NTW / 2) + j / 2) * 16 + 4 * (lane >> 4);
                 if (col >= c1) continue;
+                // silu(g) * up = g * up / (1 + e^-g), with the hardware exp2 and reciprocal
+                // (about 1 ulp each in fp32, far below the bf16 rounding of the result)
                 float o[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const float gt = acc[i][j][q], up = acc[i][j + 1][q];
-                    o[q] = gt / (1.0f + expf(-gt)) * up;
+                    const float e = __builtin_amdgcn_exp2f(gt * -1.4426950408889634f);
+                    o[q] = gt * __builtin_amdgcn_rcpf(1.0f + e) * up;
                 }
                 *reinterpret_cast<uint2*>(p.act + static_cast<size_t>(m0 + m) * p.F + col) =
                     make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
