@@ -183,8 +183,10 @@ __global__ __launch_bounds__(1024) void oproj_epilogue_kernel(const float* __res
     }
 }
 
-// workgroup b: reduces slot b (when b < M) into every row that inherits from it; also writes
-// NaN into row b when row b's source slot is invalid
+// workgroup (b, part): reduces slot b (when b < M) into every row that inherits from it, over
+// the part-th of the gridDim.y ranges of column quads; also writes NaN into those columns of row
+// b when row b's source slot is invalid.  The parts spread each slot's split partials (its
+// largest input) over several CUs.
 template <int SPL, int MAXU>
 __global__ __launch_bounds__(1024) void down_epilogue_kernel(const float* __restrict__ part, int splits, int m_cap,
                                                              const int32_t* m_count, const int32_t* rec_rows,
@@ -197,13 +199,15 @@ __global__ __launch_bounds__(1024) void down_epilogue_kernel(const float* __rest
     const int b = blockIdx.x, tid = threadIdx.x, B = blockDim.x;
     const int R = nb * N;
     const int D4 = D >> 2;
+    const int QP = (D4 + static_cast<int>(gridDim.y) - 1) / static_cast<int>(gridDim.y);
+    const int u0 = static_cast<int>(blockIdx.y) * QP, u1 = min(D4, u0 + QP);   // this part's quads
     // first round trip: the recompute count, this row's source slot and this slot's row
     const int M = clamp_m(m_count, m_cap);
     const int sb = b < R ? src_slot[b] : 0;
     const int row = b < m_cap ? rec_rows[b] : -1;
     if (b < R && (sb < 0 || sb >= M)) {
         const float nan = __builtin_nanf("");
-        for (int c4 = tid; c4 < D4; c4 += B)
+        for (int c4 = u0 + tid; c4 < u1; c4 += B)
             *reinterpret_cast<uint2*>(H_out + static_cast<size_t>(b) * D + 4 * c4) =
                 make_uint2(pack_bf16x2(nan, nan), pack_bf16x2(nan, nan));
     }
@@ -217,8 +221,8 @@ __global__ __launch_bounds__(1024) void down_epilogue_kernel(const float* __rest
     f32x4 pv[MAXU][SPL];
 #pragma unroll
     for (int k = 0; k < MAXU; ++k) {
-        const int u = tid + k * B;
-        load_splits<SPL>(pv[k], rP, u < D4 ? (static_cast<uint32_t>(b) * D + 4 * u) * 4 : kOob, stride, splits);
+        const int u = u0 + tid + k * B;
+        load_splits<SPL>(pv[k], rP, u < u1 ? (static_cast<uint32_t>(b) * D + 4 * u) * 4 : kOob, stride, splits);
     }
     if (tid == 0) s_cnt = 0;
     __syncthreads();
@@ -239,16 +243,16 @@ __global__ __launch_bounds__(1024) void down_epilogue_kernel(const float* __rest
         for (int t = 0; t < kBatch; ++t)
 #pragma unroll
             for (int k = 0; k < MAXU; ++k) {
-                const int u = tid + k * B;
-                const bool valid = t0 + t < cnt && u < D4;
+                const int u = u0 + tid + k * B;
+                const bool valid = t0 + t < cnt && u < u1;
                 hv[t][k] = buf_load8(rH, valid ? (static_cast<uint32_t>(rows[t]) * D + 4 * u) * 2 : kOob);
             }
 #pragma unroll
         for (int t = 0; t < kBatch; ++t)
 #pragma unroll
             for (int k = 0; k < MAXU; ++k) {
-                const int u = tid + k * B;
-                if (t0 + t >= cnt || u >= D4) continue;
+                const int u = u0 + tid + k * B;
+                if (t0 + t >= cnt || u >= u1) continue;
                 float h[4];
                 unpack4(hv[t][k], h);
 #pragma unroll
@@ -311,10 +315,12 @@ hipError_t launch_down_epilogue(const float* part, int splits, int m_cap, const 
                                 const uint16_t* h_mid, uint16_t* H_out, hipStream_t st) {
     const int R = nb * N;
     if (R <= 0) return hipSuccess;
-    const int D4 = D >> 2, block = quad_block(D4);
-    const int per = (D4 + block - 1) / block;
+    // column parts of at most 128 quads (512 columns): three at D = 1536, seven at 3584
+    const int D4 = D >> 2, parts = (D4 + 127) / 128;
+    const int qp = (D4 + parts - 1) / parts, block = quad_block(qp);
+    const int per = (qp + block - 1) / block;
     if (per > 2) return hipErrorInvalidValue;
-    const dim3 grid(R > m_cap ? R : m_cap);
+    const dim3 grid(R > m_cap ? R : m_cap, parts);
     return with_spl(splits, [&](auto spl) {
         constexpr int SPL = decltype(spl)::value;
         if (per == 1)
