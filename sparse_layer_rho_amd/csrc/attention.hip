@@ -52,9 +52,10 @@ struct AttnTile {
     static __device__ __forceinline__ int fv(int r) { return (2 * r) & (CH - 1); }
 };
 
-// 16 bytes per lane, global -> LDS: lane l's bytes land at lds + 16 l (lds is wave-uniform)
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds), 16, voff, 0, 0, 0);
+// 16 bytes per lane, global -> LDS: lane l's bytes land at lds + 16 l (lds is wave-uniform);
+// the address is voff (per lane) + soff (wave-uniform)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff = 0) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds), 16, voff, soff, 0, 0);
 }
 
 // this wave's buffer loads (register and LDS) are complete
@@ -111,99 +112,95 @@ __device__ __forceinline__ void kf_wait(u32x4 (&v)[C]) {
 
 // Request NKEYS rows of K and V into sK / sV (swizzled as above).  row_off(row, k_or_v) gives
 // the element offset of a key row's first dimension, or -1 for a missing key (the host keeps
-// every view under 1 GB, so offsets fit in 32 bits).  Load i of the
-// NKEYS*CH/64 per tensor is issued by wave i % NW (NW waves in the workgroup).  OFFS_FIRST:
-// every offset is formed before the first load -- for a row_off that reads LDS, which the
-// compiler would otherwise re-read after each load into LDS (one round trip per load).
-template <int HD, int NKEYS, int NW, bool OFFS_FIRST, typename RowOff>
+// every view under 1 GB, so offsets fit in 32 bits).  Load i of the NKEYS*CH/64 per tensor is
+// issued by wave i % NW (NW waves in the workgroup).  Every offset is formed before the first
+// load: for a row_off that reads LDS, the compiler would otherwise re-read it after each load
+// into LDS (one round trip per load).
+template <int HD, int NKEYS, int NW, typename RowOff>
 __device__ __forceinline__ void request_rows(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
                                              uint8_t* sK, uint8_t* sV, RowOff row_off) {
     using T = AttnTile<HD>;
     constexpr int kLoads = NKEYS * T::CH / 64;
     constexpr int kPer = (kLoads + NW - 1) / NW;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    auto offsets = [&](int t, uint32_t& ok_, uint32_t& ov) {
+    uint32_t ok_[kPer], ov[kPer];
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) {
         const int i = wave + NW * t;
         const int q = i * 64 + lane;
         const int row = q / T::CH, pos = q % T::CH;
         const int ek = i < kLoads ? row_off(row, 0) : -1, ev = i < kLoads ? row_off(row, 1) : -1;
-        ok_ = ek < 0 ? kOob : static_cast<uint32_t>((ek + 8 * (pos ^ T::fk(row))) * 2);
-        ov = ev < 0 ? kOob : static_cast<uint32_t>((ev + 8 * (pos ^ T::fv(row))) * 2);
-    };
-    if constexpr (OFFS_FIRST) {
-        uint32_t ok_[kPer], ov[kPer];
+        ok_[t] = ek < 0 ? kOob : static_cast<uint32_t>((ek + 8 * (pos ^ T::fk(row))) * 2);
+        ov[t] = ev < 0 ? kOob : static_cast<uint32_t>((ev + 8 * (pos ^ T::fv(row))) * 2);
+    }
 #pragma unroll
-        for (int t = 0; t < kPer; ++t) offsets(t, ok_[t], ov[t]);
-#pragma unroll
-        for (int t = 0; t < kPer; ++t) {
-            const int i = wave + NW * t;
-            if (i >= kLoads) break;                // wave-uniform
-            dma16(rk, sK + i * 1024, ok_[t]);
-            dma16(rv, sV + i * 1024, ov[t]);
-        }
-    } else {
-#pragma unroll
-        for (int t = 0; t < kPer; ++t) {
-            const int i = wave + NW * t;
-            if (i >= kLoads) break;                // wave-uniform
-            uint32_t ok_, ov;
-            offsets(t, ok_, ov);
-            dma16(rk, sK + i * 1024, ok_);
-            dma16(rv, sV + i * 1024, ov);
-        }
+    for (int t = 0; t < kPer; ++t) {
+        const int i = wave + NW * t;
+        if (i >= kLoads) break;                    // wave-uniform
+        dma16(rk, sK + i * 1024, ok_[t]);
+        dma16(rv, sV + i * 1024, ov[t]);
     }
 }
 
-// One 64-key block of online softmax for the wave's 16 queries; sK / sV point at the block's
-// first row (a multiple of 16 rows into the stage, so the swizzles line up).
-// qf: B operand (query lane&15, d = 32s + 8*(lane>>4)); nk valid keys.
-template <int HD>
+// One block of 16 * NKT keys (NKT = 2 or 4) of online softmax for the wave's NQ tiles of 16
+// queries; sK / sV point at the block's first row (a multiple of 16 rows into the stage, so
+// the swizzles line up).  Every key and value fragment read from LDS serves all NQ tiles.
+// qf[q]: B operand of query tile q (query lane&15, d = 32s + 8*(lane>>4)); nk valid keys.
+template <int HD, int NKT, int NQ>
 __device__ __forceinline__ void attend_block(const uint8_t* sK, const uint8_t* sV, int nk,
-                                             const uint4 (&qf)[AttnTile<HD>::KS], float scale_log2,
-                                             float& run_m, float& run_l, f32x4 (&o)[AttnTile<HD>::DT]) {
+                                             const uint4 (&qf)[NQ][AttnTile<HD>::KS], float scale_log2,
+                                             float (&run_m)[NQ], float (&run_l)[NQ],
+                                             f32x4 (&o)[NQ][AttnTile<HD>::DT]) {
     using T = AttnTile<HD>;
+    static_assert(NKT == 2 || NKT == 4, "blocks of 32 or 64 keys");
     const int lane = threadIdx.x & 63;
     const int g4 = lane >> 4, l16 = lane & 15;
     // Branch-free: rows past nk hold zeros (their loads were out of range), their scores are
     // masked below and their P entries are zero, so all fragment reads can be issued at once.
-    f32x4 sc[4];
+    f32x4 sc[NQ][NKT];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) sc[q][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (HD % 32 == 0) {
-        // every 32-wide k-step lies inside the row: the 4 KS reads of one k-step differ in
+        // every 32-wide k-step lies inside the row: the NKT reads of one k-step differ in
         // their key tile only (fk depends on the row's low bits, the same in every tile), so
         // they take immediate offsets; k-step s is waited for with the later ones in flight
-        u32x4 kf[T::KS][4];
+        u32x4 kf[T::KS][NKT];
 #pragma unroll
         for (int s = 0; s < T::KS; ++s) {
             const int c = 4 * s + g4;
             const uint32_t a = lds_addr(sK) + l16 * T::RB + ((c ^ T::fk(l16)) << 4);
             kf[s][0] = lds_read16<0>(a);
             kf[s][1] = lds_read16<16 * T::RB>(a);
-            kf[s][2] = lds_read16<32 * T::RB>(a);
-            kf[s][3] = lds_read16<48 * T::RB>(a);
+            if constexpr (NKT == 4) {
+                kf[s][2] = lds_read16<32 * T::RB>(a);
+                kf[s][3] = lds_read16<48 * T::RB>(a);
+            }
         }
         auto step = [&](int s) {
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
-                sc[kt] = mfma16x16x32(__builtin_bit_cast(uint4, kf[s][kt]), qf[s], sc[kt]);
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int q = 0; q < NQ; ++q)
+                    sc[q][kt] = mfma16x16x32(__builtin_bit_cast(uint4, kf[s][kt]), qf[q][s], sc[q][kt]);
             __builtin_amdgcn_sched_barrier(0);    // k-step s's MFMAs stay ahead of the next wait
         };
         if constexpr (T::KS == 4) {
-            kf_wait<12>(kf[0]); step(0);
-            kf_wait<8>(kf[1]); step(1);
-            kf_wait<4>(kf[2]); step(2);
+            kf_wait<3 * NKT>(kf[0]); step(0);
+            kf_wait<2 * NKT>(kf[1]); step(1);
+            kf_wait<NKT>(kf[2]); step(2);
             kf_wait<0>(kf[3]); step(3);
         } else if constexpr (T::KS == 2) {
-            kf_wait<4>(kf[0]); step(0);
+            kf_wait<NKT>(kf[0]); step(0);
             kf_wait<0>(kf[1]); step(1);
         } else {
             kf_wait<0>(kf[0]); step(0);
         }
     } else {
-        uint4 kf[4][T::KS];
+        uint4 kf[NKT][T::KS];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
+        for (int kt = 0; kt < NKT; ++kt) {
             const int r = kt * 16 + l16;
 #pragma unroll
             for (int s = 0; s < T::KS; ++s) {
@@ -215,54 +212,67 @@ __device__ __forceinline__ void attend_block(const uint8_t* sK, const uint8_t* s
 #pragma unroll
         for (int s = 0; s < T::KS; ++s)
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) sc[kt] = mfma16x16x32(kf[kt][s], qf[s], sc[kt]);
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) sc[q][kt] = mfma16x16x32(kf[kt][s], qf[q][s], sc[q][kt]);
     }
-    // lane holds S^T[key = 16kt + 4*g4 + i][query l16]
-    float bmax = kNegInf;
+    // lane holds S^T[key = 16kt + 4*g4 + i][query l16] of each query tile.  The reference
+    // maximum run_m moves only when a score passes it by more than kLazy (log2 units).  The
+    // state (run_m, run_l, o) is exact for any reference, and below that margin every weight
+    // exp2(s - run_m) <= 2^kLazy stays far inside fp32 and bf16, so most blocks skip rescaling
+    // o; the rescale runs when any query of the wave moves its reference.
+    float alpha[NQ];
+    bool rescale_any = false;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int q = 0; q < NQ; ++q) {
+        float bmax = kNegInf;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = kt * 16 + 4 * g4 + i;
-            const float v = (key < nk) ? sc[kt][i] * scale_log2 : kNegInf;
-            sc[kt][i] = v;
-            bmax = fmaxf(bmax, v);
-        }
-    bmax = max_rows4(bmax);                        // over the query's four lanes
-    // The reference maximum run_m moves only when a score passes it by more than kLazy (log2
-    // units).  The state (run_m, run_l, o) is exact for any reference, and below that margin
-    // every weight exp2(s - run_m) <= 2^kLazy stays far inside fp32 and bf16, so most blocks
-    // skip rescaling o; the rescale runs when any query of the wave moves its reference.
-    const bool grow = bmax > run_m + kLazy;
-    const float new_m = grow ? bmax : run_m;
-    float psum = 0.f;
+        for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+            for (int i = 0; i < 4; ++i) {
+                const int key = kt * 16 + 4 * g4 + i;
+                const float v = (key < nk) ? sc[q][kt][i] * scale_log2 : kNegInf;
+                sc[q][kt][i] = v;
+                bmax = fmaxf(bmax, v);
+            }
+        bmax = max_rows4(bmax);                    // over the query's four lanes
+        const bool grow = bmax > run_m[q] + kLazy;
+        const float new_m = grow ? bmax : run_m[q];
+        float psum = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float e = (sc[kt][i] == kNegInf) ? 0.f : fast_exp2(sc[kt][i] - new_m);
-            sc[kt][i] = e;
-            psum += e;
-        }
-    const bool rescale = grow && run_m != kNegInf;     // a state of zeros needs no rescale
-    if (__ballot(rescale) != 0) {                      // wave-uniform
-        const float alpha = rescale ? fast_exp2(run_m - new_m) : 1.f;
-        run_l *= alpha;
+        for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-        for (int dt = 0; dt < T::DT; ++dt) o[dt] *= alpha;
+            for (int i = 0; i < 4; ++i) {
+                const float e = (sc[q][kt][i] == kNegInf) ? 0.f : fast_exp2(sc[q][kt][i] - new_m);
+                sc[q][kt][i] = e;
+                psum += e;
+            }
+        const bool rescale = grow && run_m[q] != kNegInf;   // a state of zeros needs no rescale
+        alpha[q] = rescale ? fast_exp2(run_m[q] - new_m) : 1.f;
+        rescale_any = rescale_any || rescale;
+        run_l[q] = run_l[q] * alpha[q] + psum;
+        run_m[q] = new_m;
     }
-    run_l += psum;
-    run_m = new_m;
-    // O^T += V^T P^T over two 32-key steps; slot 8*g4 + i <-> key 32u + 4*g4 + i and
+    if (__ballot(rescale_any) != 0) {              // wave-uniform
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+#pragma unroll
+            for (int dt = 0; dt < T::DT; ++dt) o[q][dt] *= alpha[q];
+    }
+    // O^T += V^T P^T over 32-key steps; slot 8*g4 + i <-> key 32u + 4*g4 + i and
     // slot 8*g4 + 4 + i <-> key 32u + 16 + 4*g4 + i on both operands.  The A operand (V^T,
     // rows = dimensions) comes from two transposed reads of 4 keys each: lane p of the group
     // names key row 4*g4 + p/4 (+16), dimensions 16dt + 4(p%4)..+3.
     const int pr = l16 >> 2, pc = l16 & 3;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const float pf[8] = {sc[2 * u][0], sc[2 * u][1], sc[2 * u][2], sc[2 * u][3],
-                             sc[2 * u + 1][0], sc[2 * u + 1][1], sc[2 * u + 1][2], sc[2 * u + 1][3]};
-        const uint4 pb = cvt_bf16x8(pf);
+    for (int u = 0; u < NKT / 2; ++u) {
+        uint4 pb[NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const float pf[8] = {sc[q][2 * u][0], sc[q][2 * u][1], sc[q][2 * u][2], sc[q][2 * u][3],
+                                 sc[q][2 * u + 1][0], sc[q][2 * u + 1][1], sc[q][2 * u + 1][2], sc[q][2 * u + 1][3]};
+            pb[q] = cvt_bf16x8(pf);
+        }
         const int r0 = 32 * u + 4 * g4 + pr, r1 = r0 + 16;
         uint2 lo[T::DT], hi[T::DT];
 #pragma unroll
@@ -275,7 +285,9 @@ __device__ __forceinline__ void attend_block(const uint8_t* sK, const uint8_t* s
         }
 #pragma unroll
         for (int dt = 0; dt < T::DT; ++dt)
-            o[dt] = mfma16x16x32(make_uint4(lo[dt].x, lo[dt].y, hi[dt].x, hi[dt].y), pb, o[dt]);
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                o[q][dt] = mfma16x16x32(make_uint4(lo[dt].x, lo[dt].y, hi[dt].x, hi[dt].y), pb[q], o[q][dt]);
     }
 }
 
@@ -303,9 +315,9 @@ __device__ __forceinline__ uint32_t view_bytes(int P, int Hkv, int64_t st, int64
 // grid: x = prefix chunk * Hkv + KV group, y = group of QT 16-query tiles of (slot,
 // head-in-group) queries, so the groups below the recompute count are dispatched first.
 // 2 QT waves: wave w takes query tile w % QT and, of every stage, the 64-key half w / QT; the
-// two halves' states are merged through LDS at the end.  (Every wave reads
-// a whole 64-key block from LDS, so few waves per CU keep the LDS port from saturating.)  Dynamic LDS: one stage of kStageKeys rows of K and V, or two when
-// a chunk spans several stages.
+// two halves' states are merged through LDS at the end.  (Every wave reads a whole 64-key block
+// from LDS, so few waves per CU keep the LDS port from saturating.)  Dynamic LDS: one stage of
+// kStageKeys rows of K and V, or two when a chunk spans several stages.
 template <int HD, int QT>
 __global__ __launch_bounds__(128 * QT) void attn_prefix_kernel(const AttnArgs a) {
     using T = AttnTile<HD>;
@@ -319,7 +331,7 @@ __global__ __launch_bounds__(128 * QT) void attn_prefix_kernel(const AttnArgs a)
     if (q0 >= nq) return;
     const int key0 = chunk * a.chunk_len;
     const int key1 = min(a.P, key0 + a.chunk_len);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int qw = wave % QT, half = wave / QT;
     const int qi = q0 + qw * 16 + (lane & 15);
     const bool qvalid = qi < nq;
@@ -330,21 +342,49 @@ __global__ __launch_bounds__(128 * QT) void attn_prefix_kernel(const AttnArgs a)
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.pv, view_bytes(a.P, a.Hkv, a.pv_st, a.pv_sh, HD));
     const int kst = static_cast<int>(a.pk_st), kbase = g * static_cast<int>(a.pk_sh);
     const int vst = static_cast<int>(a.pv_st), vbase = g * static_cast<int>(a.pv_sh);
+    // Stage requests: load i (1 KB, kRpl key rows) of a stage is issued by wave i % NW.  A
+    // wave's loads are kRpl * NW rows apart, a multiple of the swizzle period, so the lane's
+    // row within its load and its swizzled chunk are the same in every load: the lane offsets
+    // are formed once and each load adds a wave-uniform key offset (no per-load arithmetic).
+    // Only a stage that runs past the chunk's end masks rows, per lane.
+    constexpr int NW = 2 * QT, kRpl = 64 / T::CH, kLoads = kStageKeys / kRpl;
+    constexpr int kPer = (kLoads + NW - 1) / NW;
+    static_assert((NW * kRpl) % T::CH == 0, "a wave's loads keep the lane's swizzle");
+    const int lrow = wave * kRpl + lane / T::CH, pos = lane % T::CH;
+    const uint32_t koff = static_cast<uint32_t>((lrow * kst + kbase + 8 * (pos ^ T::fk(lrow))) * 2);
+    const uint32_t voff = static_cast<uint32_t>((lrow * vst + vbase + 8 * (pos ^ T::fv(lrow))) * 2);
     auto request_stage = [&](int kb, int buf) {
         uint8_t* sK = smem + buf * 2 * kStageBytes;
-        request_rows<HD, kStageKeys, 2 * QT, false>(rk, rv, sK, sK + kStageBytes, [&](int row, int which) -> int {
-            const int key = kb + row;
-            return key >= key1 ? -1 : (which == 0 ? key * kst + kbase : key * vst + vbase);
-        });
+        uint8_t* sV = sK + kStageBytes;
+        if (kb + kStageKeys <= key1) {             // wave-uniform: every row of the stage is a key
+#pragma unroll
+            for (int t = 0; t < kPer; ++t) {
+                const int i = wave + NW * t;
+                if (kLoads % NW != 0 && i >= kLoads) break;
+                const int r0 = kb + NW * kRpl * t;
+                dma16(rk, sK + i * 1024, koff, static_cast<uint32_t>(r0 * kst * 2));
+                dma16(rv, sV + i * 1024, voff, static_cast<uint32_t>(r0 * vst * 2));
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < kPer; ++t) {
+                const int i = wave + NW * t;
+                if (kLoads % NW != 0 && i >= kLoads) break;
+                const int r0 = kb + NW * kRpl * t;
+                const bool ok = r0 + lrow < key1;
+                dma16(rk, sK + i * 1024, ok ? koff + static_cast<uint32_t>(r0 * kst * 2) : kOob);
+                dma16(rv, sV + i * 1024, ok ? voff + static_cast<uint32_t>(r0 * vst * 2) : kOob);
+            }
+        }
     };
     request_stage(key0, 0);
-    uint4 qf[T::KS];
-    load_query<HD>(rq, qvalid ? static_cast<uint32_t>((m * a.Hq + h) * HD * 2) : kOob, qf);
+    uint4 qf[1][T::KS];
+    load_query<HD>(rq, qvalid ? static_cast<uint32_t>((m * a.Hq + h) * HD * 2) : kOob, qf[0]);
 
-    float run_m = kNegInf, run_l = 0.f;
-    f32x4 o[T::DT];
+    float run_m[1] = {kNegInf}, run_l[1] = {0.f};
+    f32x4 o[1][T::DT];
 #pragma unroll
-    for (int dt = 0; dt < T::DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < T::DT; ++dt) o[0][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     int buf = 0;
     for (int kb = key0; kb < key1; kb += kStageKeys) {
@@ -354,8 +394,8 @@ __global__ __launch_bounds__(128 * QT) void attn_prefix_kernel(const AttnArgs a)
         const uint8_t* sK = smem + buf * 2 * kStageBytes;
         const int sb = 64 * half, nst = min(kStageKeys, key1 - kb);
         if (sb < nst)                              // wave-uniform
-            attend_block<HD>(sK + sb * T::RB, sK + kStageBytes + sb * T::RB, min(64, nst - sb), qf,
-                             a.scale_log2, run_m, run_l, o);
+            attend_block<HD, 4, 1>(sK + sb * T::RB, sK + kStageBytes + sb * T::RB, min(64, nst - sb), qf,
+                                   a.scale_log2, run_m, run_l, o);
         __syncthreads();                           // this buffer is consumed
         buf ^= 1;
     }
@@ -366,43 +406,44 @@ __global__ __launch_bounds__(128 * QT) void attn_prefix_kernel(const AttnArgs a)
 #pragma unroll
         for (int dt = 0; dt < T::DT; ++dt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) xs[(dt * 4 + e) * 64] = o[dt][e];
-        xs[T::DT * 4 * 64] = run_m;
-        xs[(T::DT * 4 + 1) * 64] = run_l;
+            for (int e = 0; e < 4; ++e) xs[(dt * 4 + e) * 64] = o[0][dt][e];
+        xs[T::DT * 4 * 64] = run_m[0];
+        xs[(T::DT * 4 + 1) * 64] = run_l[0];
     }
     __syncthreads();
     if (half == 1) return;
+    float rm = run_m[0], rl = run_l[0];
     {
         const float m1 = xs[T::DT * 4 * 64], l1 = xs[(T::DT * 4 + 1) * 64];
-        const float nm = fmaxf(run_m, m1);
-        const float w0 = run_m == kNegInf ? 0.f : exp2f(run_m - nm);
+        const float nm = fmaxf(rm, m1);
+        const float w0 = rm == kNegInf ? 0.f : exp2f(rm - nm);
         const float w1 = m1 == kNegInf ? 0.f : exp2f(m1 - nm);
-        run_l = run_l * w0 + l1 * w1;
+        rl = rl * w0 + l1 * w1;
 #pragma unroll
         for (int dt = 0; dt < T::DT; ++dt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[dt][e] = o[dt][e] * w0 + xs[(dt * 4 + e) * 64] * w1;
-        run_m = nm;
+            for (int e = 0; e < 4; ++e) o[0][dt][e] = o[0][dt][e] * w0 + xs[(dt * 4 + e) * 64] * w1;
+        rm = nm;
     }
-    run_l = sum_rows4(run_l);
+    rl = sum_rows4(rl);
     if (!qvalid) return;
     const size_t base = (static_cast<size_t>(chunk) * a.m_cap + m) * a.Hq + h;
     if ((lane >> 4) == 0)
-        *reinterpret_cast<float2*>(a.part_ml + 2 * base) = make_float2(run_m, run_l);
+        *reinterpret_cast<float2*>(a.part_ml + 2 * base) = make_float2(rm, rl);
     float* po = a.part_o + base * HD + 4 * (lane >> 4);
 #pragma unroll
-    for (int dt = 0; dt < T::DT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[dt];
+    for (int dt = 0; dt < T::DT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[0][dt];
 }
 
 // grid: x = branch, y = KV group, z = query tile (16 positions x 1 head).  One wave per
 // workgroup: the chunk states a tile merges are its largest input, and single-wave workgroups
 // spread them over as many CUs as there are tiles.
-template <int HD>
+template <int HD, int NKT>
 __global__ __launch_bounds__(64) void attn_block_kernel(const AttnArgs a) {
     using T = AttnTile<HD>;
     constexpr int kBatch = 4;                      // prefix chunk states loaded per round trip
-    __shared__ __align__(16) uint8_t sK[64 * T::RB];
-    __shared__ __align__(16) uint8_t sV[64 * T::RB];
+    __shared__ __align__(16) uint8_t sK[16 * NKT * T::RB];
+    __shared__ __align__(16) uint8_t sV[16 * NKT * T::RB];
     __shared__ int sSlot[64];
     const int G = a.Hq / a.Hkv, N = a.N;
     const int i = blockIdx.x, g = blockIdx.y;
@@ -423,7 +464,7 @@ __global__ __launch_bounds__(64) void attn_block_kernel(const AttnArgs a) {
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k_c, rows_bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v_c, rows_bytes);
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q_c, static_cast<uint32_t>(static_cast<size_t>(a.m_cap) * a.Hq * HD * 2));
-    request_rows<HD, 64, 1, true>(rk, rv, sK, sV, [&](int row, int) -> int {
+    request_rows<HD, 16 * NKT, 1>(rk, rv, sK, sV, [&](int row, int) -> int {
         const int s = row < N ? sSlot[row] : -1;
         return s < 0 ? -1 : (s * a.Hkv + g) * HD;
     });
@@ -434,8 +475,8 @@ __global__ __launch_bounds__(64) void attn_block_kernel(const AttnArgs a) {
     const int n = nt * 16 + (lane & 15);
     const bool nvalid = active && n < N;
     const int qslot = nvalid ? sSlot[n] : -1;
-    uint4 qf[T::KS];
-    load_query<HD>(rq, qslot >= 0 ? static_cast<uint32_t>((qslot * a.Hq + h) * HD * 2) : kOob, qf);
+    uint4 qf[1][T::KS];
+    load_query<HD>(rq, qslot >= 0 ? static_cast<uint32_t>((qslot * a.Hq + h) * HD * 2) : kOob, qf[0]);
 
     // prefix chunk states of the source slot: the first batch is requested now, so it arrives
     // with the block's keys
@@ -467,12 +508,15 @@ __global__ __launch_bounds__(64) void attn_block_kernel(const AttnArgs a) {
     __syncthreads();
     if (!active) return;
 
-    float run_m = kNegInf, run_l = 0.f;
+    float bm[1] = {kNegInf}, bl[1] = {0.f};
+    f32x4 bo[1][T::DT];
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt) bo[0][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    attend_block<HD, NKT, 1>(sK, sV, N, qf, a.scale_log2, bm, bl, bo);
+    float run_m = bm[0], run_l = sum_rows4(bl[0]);
     f32x4 o[T::DT];
 #pragma unroll
-    for (int dt = 0; dt < T::DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    attend_block<HD>(sK, sV, N, qf, a.scale_log2, run_m, run_l, o);
-    run_l = sum_rows4(run_l);
+    for (int dt = 0; dt < T::DT; ++dt) o[dt] = bo[0][dt];
 
     // merge the prefix chunk states in ascending chunk order by online log-sum-exp rescaling
     for (int c0 = 0; c0 < a.n_chunks; c0 += kBatch) {
@@ -536,6 +580,13 @@ hipError_t launch_prefix_hd(const AttnArgs& a, hipStream_t st) {
     return busy2 <= slots ? launch_prefix_qt<HD, 2>(a, st) : launch_prefix_qt<HD, 4>(a, st);
 }
 
+template <int HD>
+void launch_block_hd(const AttnArgs& a, dim3 grid, hipStream_t st) {
+    // blocks of up to 32 positions take the 32-key form (no MFMAs or fragment reads on padding)
+    if (a.N <= 32) hipLaunchKernelGGL((attn_block_kernel<HD, 2>), grid, dim3(64), 0, st, a);
+    else hipLaunchKernelGGL((attn_block_kernel<HD, 4>), grid, dim3(64), 0, st, a);
+}
+
 }  // namespace
 
 hipError_t launch_attn_prefix(const AttnArgs& a, hipStream_t st) {
@@ -551,13 +602,14 @@ hipError_t launch_attn_prefix(const AttnArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_attn_block(const AttnArgs& a, hipStream_t st) {
+    if (a.N > 64) return hipErrorInvalidValue;
     const int G = a.Hq / a.Hkv;
     const dim3 grid(a.nb, a.Hkv, G * ((a.N + 15) / 16));
     switch (a.hd) {
-        case 16: hipLaunchKernelGGL(attn_block_kernel<16>, grid, dim3(64), 0, st, a); break;
-        case 32: hipLaunchKernelGGL(attn_block_kernel<32>, grid, dim3(64), 0, st, a); break;
-        case 64: hipLaunchKernelGGL(attn_block_kernel<64>, grid, dim3(64), 0, st, a); break;
-        case 128: hipLaunchKernelGGL(attn_block_kernel<128>, grid, dim3(64), 0, st, a); break;
+        case 16: launch_block_hd<16>(a, grid, st); break;
+        case 32: launch_block_hd<32>(a, grid, st); break;
+        case 64: launch_block_hd<64>(a, grid, st); break;
+        case 128: launch_block_hd<128>(a, grid, st); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
