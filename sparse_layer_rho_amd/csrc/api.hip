@@ -78,7 +78,10 @@ int splits_for(GemmKind kind, int n_cols, int k) {
 //   * QKV, the recompute rows (M ~ 100 folded): 64-column groups, two 64-row chunks; 1.5B
 //     6.9 us against 7.7 with 32-column groups;
 //   * o_proj, all R rows: 128-row chunks, three at R = 288 instead of five of 64, so the weights
-//     are re-read least; 1.5B 8.5 against 9.2 us, 7B 19.7 against 28.4, 14B 35 against 51;
+//     are re-read least; 1.5B 8.5 against 9.2 us, 7B 19.7 against 28.4, 14B 35 against 51; three
+//     activation slots (two stages in flight) 9.1 against 9.4 us at 1.5B (the other
+//     projections lose with them: QKV 0.5 us, down 2-5 us, whose 80 KB rings no longer fit two
+//     workgroups per CU);
 //   * gate/up up to 128 rows (above, gemm_shapes_kernel's three shapes): weight stages of 256 bytes
 //     per row;
 //   * down: 128-row chunks; 128-column groups when a K-split spans at least 1024 elements (the
@@ -91,7 +94,7 @@ GemmCfg pick_gemm(GemmKind kind, int n_cols, int k, int max_rows) {
     c.splits = splits_for(kind, n_cols, k);
     switch (kind) {
     case GEMM_QKV: c.ntw = 4; c.tm = 1; c.ksub = 1; c.nbw = 3; c.nba = 2; break;
-    case GEMM_O: c.ntw = 4; c.tm = 2; c.ksub = 1; c.nbw = 4; c.nba = 2; break;
+    case GEMM_O: c.ntw = 4; c.tm = 2; c.ksub = 1; c.nbw = 4; c.nba = 3; break;
     case GEMM_GATE_UP: c.ntw = 4; c.tm = 1; c.ksub = 2; c.nbw = 2; c.nba = 2; break;
     case GEMM_DOWN:
         if (k / c.splits >= 1024) { c.ntw = 8; c.tm = 2; c.ksub = 1; c.nbw = 3; c.nba = 2; }

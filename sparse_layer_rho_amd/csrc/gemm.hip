@@ -253,18 +253,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int M, const 
     // columns), the last unit possibly partial, spread evenly over the groups; the last group
     // ends at ncols.  With ceil(ncols / 4) units no group is wider than the group capacity the
     // host sized the grid for (ncols <= groups * capacity, capacity a multiple of 4).
+    // (32-bit unsigned products: the launchers keep groups * units below 2^32, so no 64-bit
+    // division, a long scalar sequence, sits in every workgroup's prologue)
     const int ncols = EPI == EPI_SWIGLU ? p.F : p.Nout;
-    const int units = (ncols + 3) / 4;
-    const int c0 = static_cast<int>(static_cast<int64_t>(g) * units / p.n_groups) * 4;
-    const int c1 = min(ncols, static_cast<int>(static_cast<int64_t>(g + 1) * units / p.n_groups) * 4);
+    const uint32_t units = static_cast<uint32_t>(ncols + 3) / 4, ng = static_cast<uint32_t>(p.n_groups);
+    const int c0 = static_cast<int>(static_cast<uint32_t>(g) * units / ng) * 4;
+    const int c1 = min(ncols, static_cast<int>(static_cast<uint32_t>(g + 1) * units / ng) * 4);
 
     // K range of this split: whole units of kSplitUnit elements (a multiple of every weight
     // stage), so the split boundaries -- and with them the order in which every output's sum
     // is formed -- depend on K and the split count only, not on the tile shape or the rows
     static_assert(kSplitUnit % (KSUB * kStageK) == 0, "weight stages tile the split unit");
-    const int nun = (p.K + kSplitUnit - 1) / kSplitUnit;
-    const int u0 = static_cast<int>(static_cast<int64_t>(y) * nun / S);
-    const int u1 = static_cast<int>(static_cast<int64_t>(y + 1) * nun / S);
+    const int nun = (p.K + kSplitUnit - 1) / kSplitUnit;   // K < 2^29, S <= 32: products fit
+    const int u0 = static_cast<int>(static_cast<uint32_t>(y * nun) / static_cast<uint32_t>(S));
+    const int u1 = static_cast<int>(static_cast<uint32_t>((y + 1) * nun) / static_cast<uint32_t>(S));
     const int k_begin = u0 * kSplitUnit;
     const int k_stop = min(p.K, u1 * kSplitUnit);
     const int nws = k_stop > k_begin ? (k_stop - k_begin + KSUB * kStageK - 1) / (KSUB * kStageK) : 0;
@@ -521,6 +523,11 @@ __global__ __launch_bounds__(256) void gemm_shapes_kernel(const GemmArgs pa, con
     else SC::run(pc, M, smem);
 }
 
+// the kernels split the 4-column units over the groups with 32-bit products
+bool groups_fit(int groups, int ncols) {
+    return static_cast<uint64_t>(groups) * static_cast<uint64_t>((ncols + 3) / 4) < (uint64_t(1) << 32);
+}
+
 template <int NTW, int WN, int TM, int KSUB, int NBW, int NBA, int EPI>
 hipError_t launch_shape(GemmArgs a, const GemmCfg& c, int splits, hipStream_t st) {
     using T = Tile<NTW, WN, TM, KSUB, NBW, NBA>;
@@ -528,7 +535,7 @@ hipError_t launch_shape(GemmArgs a, const GemmCfg& c, int splits, hipStream_t st
     // epilogue takes a column count that is not a multiple of 4
     if (EPI != EPI_ARGMAX && ((EPI == EPI_SWIGLU ? a.F : a.Nout) % 4) != 0) return hipErrorInvalidValue;
     const int groups = c.groups;
-    if (groups < 1) return hipErrorInvalidValue;
+    if (groups < 1 || !groups_fit(groups, EPI == EPI_SWIGLU ? a.F : a.Nout)) return hipErrorInvalidValue;
     a.n_groups = groups;
     a.min_chunks = c.min_chunks;
     a.m_chunks = (a.m_cap + T::MP - 1) / T::MP;
@@ -552,6 +559,7 @@ hipError_t launch_shapes(GemmArgs a, const GemmCfg* c, const int* upto, hipStrea
     const int rows[3] = {upto[0], upto[1], a.m_cap};   // the most rows each shape ever sees
     int grid = 1;
     for (int i = 0; i < 3; ++i) {
+        if (c[i].groups < 1 || !groups_fit(c[i].groups, a.F)) return hipErrorInvalidValue;
         p[i].n_groups = c[i].groups;
         p[i].min_chunks = c[i].min_chunks;
         const int r = rows[i] < a.m_cap ? rows[i] : a.m_cap;
