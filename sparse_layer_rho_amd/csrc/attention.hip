@@ -314,12 +314,15 @@ __device__ __forceinline__ uint32_t view_bytes(int P, int Hkv, int64_t st, int64
 
 // grid: x = prefix chunk * Hkv + KV group, y = group of QT 16-query tiles of (slot,
 // head-in-group) queries, so the groups below the recompute count are dispatched first.
-// 2 QT waves: wave w takes query tile w % QT and, of every stage, the 64-key half w / QT; the
-// two halves' states are merged through LDS at the end.  (Every wave reads a whole 64-key block
-// from LDS, so few waves per CU keep the LDS port from saturating.)  Dynamic LDS: one stage of
-// kStageKeys rows of K and V, or two when a chunk spans several stages.
-template <int HD, int QT>
-__global__ __launch_bounds__(128 * QT) void attn_prefix_kernel(const AttnArgs a) {
+// 2 QT compute waves: wave w takes query tile w % QT and, of every stage, the 64-key half w / QT;
+// the two halves' states are merged through LDS at the end.  (Every wave reads a whole 64-key
+// block from LDS, so few waves per CU keep the LDS port from saturating.)  LW = 0: the compute
+// waves also request the stages; LW = 4 (chunks of several stages): four more waves request
+// them, so the next stage's loads are issued while the current one is multiplied rather than
+// before.  Dynamic LDS: one stage of kStageKeys rows of K and V, or two when a chunk spans
+// several stages.
+template <int HD, int QT, int LW>
+__global__ __launch_bounds__(128 * QT + 64 * LW) void attn_prefix_kernel(const AttnArgs a) {
     using T = AttnTile<HD>;
     constexpr int kStageBytes = kStageKeys * T::RB;
     extern __shared__ __align__(16) uint8_t smem[];
@@ -332,6 +335,7 @@ __global__ __launch_bounds__(128 * QT) void attn_prefix_kernel(const AttnArgs a)
     const int key0 = chunk * a.chunk_len;
     const int key1 = min(a.P, key0 + a.chunk_len);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const bool loader = LW > 0 && wave >= 2 * QT;  // wave-uniform
     const int qw = wave % QT, half = wave / QT;
     const int qi = q0 + qw * 16 + (lane & 15);
     const bool qvalid = qi < nq;
@@ -347,10 +351,11 @@ __global__ __launch_bounds__(128 * QT) void attn_prefix_kernel(const AttnArgs a)
     // row within its load and its swizzled chunk are the same in every load: the lane offsets
     // are formed once and each load adds a wave-uniform key offset (no per-load arithmetic).
     // Only a stage that runs past the chunk's end masks rows, per lane.
-    constexpr int NW = 2 * QT, kRpl = 64 / T::CH, kLoads = kStageKeys / kRpl;
+    constexpr int NW = LW > 0 ? LW : 2 * QT, kRpl = 64 / T::CH, kLoads = kStageKeys / kRpl;
     constexpr int kPer = (kLoads + NW - 1) / NW;
     static_assert((NW * kRpl) % T::CH == 0, "a wave's loads keep the lane's swizzle");
-    const int lrow = wave * kRpl + lane / T::CH, pos = lane % T::CH;
+    const int rw = LW > 0 ? wave - 2 * QT : wave;  // requesting wave index (load waves: >= 0)
+    const int lrow = rw * kRpl + lane / T::CH, pos = lane % T::CH;
     const uint32_t koff = static_cast<uint32_t>((lrow * kst + kbase + 8 * (pos ^ T::fk(lrow))) * 2);
     const uint32_t voff = static_cast<uint32_t>((lrow * vst + vbase + 8 * (pos ^ T::fv(lrow))) * 2);
     auto request_stage = [&](int kb, int buf) {
@@ -359,7 +364,7 @@ __global__ __launch_bounds__(128 * QT) void attn_prefix_kernel(const AttnArgs a)
         if (kb + kStageKeys <= key1) {             // wave-uniform: every row of the stage is a key
 #pragma unroll
             for (int t = 0; t < kPer; ++t) {
-                const int i = wave + NW * t;
+                const int i = rw + NW * t;
                 if (kLoads % NW != 0 && i >= kLoads) break;
                 const int r0 = kb + NW * kRpl * t;
                 dma16(rk, sK + i * 1024, koff, static_cast<uint32_t>(r0 * kst * 2));
@@ -368,7 +373,7 @@ __global__ __launch_bounds__(128 * QT) void attn_prefix_kernel(const AttnArgs a)
         } else {
 #pragma unroll
             for (int t = 0; t < kPer; ++t) {
-                const int i = wave + NW * t;
+                const int i = rw + NW * t;
                 if (kLoads % NW != 0 && i >= kLoads) break;
                 const int r0 = kb + NW * kRpl * t;
                 const bool ok = r0 + lrow < key1;
@@ -377,9 +382,10 @@ __global__ __launch_bounds__(128 * QT) void attn_prefix_kernel(const AttnArgs a)
             }
         }
     };
-    request_stage(key0, 0);
+    const bool requester = LW == 0 || loader;
+    if (requester) request_stage(key0, 0);
     uint4 qf[1][T::KS];
-    load_query<HD>(rq, qvalid ? static_cast<uint32_t>((m * a.Hq + h) * HD * 2) : kOob, qf[0]);
+    if (!loader) load_query<HD>(rq, qvalid ? static_cast<uint32_t>((m * a.Hq + h) * HD * 2) : kOob, qf[0]);
 
     float run_m[1] = {kNegInf}, run_l[1] = {0.f};
     f32x4 o[1][T::DT];
@@ -388,12 +394,12 @@ __global__ __launch_bounds__(128 * QT) void attn_prefix_kernel(const AttnArgs a)
 
     int buf = 0;
     for (int kb = key0; kb < key1; kb += kStageKeys) {
-        vm_drain();
+        if (requester) vm_drain();
         __syncthreads();                           // stage kb is in LDS; the other buffer is free
-        if (kb + kStageKeys < key1) request_stage(kb + kStageKeys, buf ^ 1);
+        if (requester && kb + kStageKeys < key1) request_stage(kb + kStageKeys, buf ^ 1);
         const uint8_t* sK = smem + buf * 2 * kStageBytes;
         const int sb = 64 * half, nst = min(kStageKeys, key1 - kb);
-        if (sb < nst)                              // wave-uniform
+        if (!loader && sb < nst)                   // wave-uniform
             attend_block<HD, 4, 1>(sK + sb * T::RB, sK + kStageBytes + sb * T::RB, min(64, nst - sb), qf,
                                    a.scale_log2, run_m, run_l, o);
         __syncthreads();                           // this buffer is consumed
@@ -402,7 +408,7 @@ __global__ __launch_bounds__(128 * QT) void attn_prefix_kernel(const AttnArgs a)
     // merge the second half's state into the first (per-lane partial denominators are
     // rescaled like the outputs; the rescale factor is uniform over a query's four lanes)
     float* xs = reinterpret_cast<float*>(smem) + qw * (T::DT * 4 + 2) * 64 + lane;
-    if (half == 1) {
+    if (!loader && half == 1) {
 #pragma unroll
         for (int dt = 0; dt < T::DT; ++dt)
 #pragma unroll
@@ -411,7 +417,7 @@ __global__ __launch_bounds__(128 * QT) void attn_prefix_kernel(const AttnArgs a)
         xs[(T::DT * 4 + 1) * 64] = run_l[0];
     }
     __syncthreads();
-    if (half == 1) return;
+    if (loader || half == 1) return;
     float rm = run_m[0], rl = run_l[0];
     {
         const float m1 = xs[T::DT * 4 * 64], l1 = xs[(T::DT * 4 + 1) * 64];
@@ -546,7 +552,7 @@ __global__ __launch_bounds__(64) void attn_block_kernel(const AttnArgs a) {
         a.lse[static_cast<size_t>(row) * a.Hq + h] = bad ? __builtin_nanf("") : (run_m + log2f(run_l)) * 0.69314718055994531f;
 }
 
-template <int HD, int QT>
+template <int HD, int QT, int LW>
 hipError_t launch_prefix_qt(const AttnArgs& a, hipStream_t st) {
     // one LDS stage holds the whole chunk, else two alternate
     const size_t stage = static_cast<size_t>(2) * kStageKeys * AttnTile<HD>::RB;
@@ -555,10 +561,10 @@ hipError_t launch_prefix_qt(const AttnArgs& a, hipStream_t st) {
                   "the merge exchange fits in one stage");
     const int G = a.Hq / a.Hkv;
     const dim3 grid(a.n_chunks * a.Hkv, (a.m_cap * G + 16 * QT - 1) / (16 * QT));
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_prefix_kernel<HD, QT>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_prefix_kernel<HD, QT, LW>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_prefix_kernel<HD, QT>), grid, dim3(128 * QT), lds, st, a);
+    hipLaunchKernelGGL((attn_prefix_kernel<HD, QT, LW>), grid, dim3(128 * QT + 64 * LW), lds, st, a);
     return hipGetLastError();
 }
 
@@ -577,7 +583,9 @@ hipError_t launch_prefix_hd(const AttnArgs& a, hipStream_t st) {
     const long slots = a.chunk_len > kStageKeys ? 256 : 512;
     const int rows = a.plan_rows > 0 ? (a.plan_rows < a.m_cap ? a.plan_rows : a.m_cap) : (a.m_cap + 1) / 2;
     const long busy2 = static_cast<long>(a.n_chunks) * a.Hkv * ((rows * G + 31) / 32);
-    return busy2 <= slots ? launch_prefix_qt<HD, 2>(a, st) : launch_prefix_qt<HD, 4>(a, st);
+    const bool multi = a.chunk_len > kStageKeys;
+    if (busy2 <= slots) return multi ? launch_prefix_qt<HD, 2, 4>(a, st) : launch_prefix_qt<HD, 2, 0>(a, st);
+    return multi ? launch_prefix_qt<HD, 4, 4>(a, st) : launch_prefix_qt<HD, 4, 0>(a, st);
 }
 
 template <int HD>
