@@ -60,6 +60,8 @@ enum GemmKind { GEMM_QKV, GEMM_O, GEMM_GATE_UP, GEMM_DOWN };
 // accumulation order].  The counts aim at about 512 (QKV), 768 (o_proj) and 384 (down) busy
 // workgroups with the row workgroups a 288-row layer has (2, 5 and 1 per column group), as
 // measured best on the 1.5B layer.
+constexpr int kNumCUs = 256;                        // compute units of the GPU (MI355X)
+
 int splits_for(GemmKind kind, int n_cols, int k) {
     if (kind == GEMM_GATE_UP) return 1;             // SwiGLU needs the whole sum
     const int rows = kind == GEMM_QKV ? 2 : kind == GEMM_O ? 5 : 1;
@@ -79,9 +81,10 @@ int splits_for(GemmKind kind, int n_cols, int k) {
 //     6.9 us against 7.7 with 32-column groups;
 //   * o_proj, all R rows: 128-row chunks, three at R = 288 instead of five of 64, so the weights
 //     are re-read least; 1.5B 8.5 against 9.2 us, 7B 19.7 against 28.4, 14B 35 against 51; three
-//     activation slots (two stages in flight) 9.1 against 9.4 us at 1.5B (the other
-//     projections lose with them: QKV 0.5 us, down 2-5 us, whose 80 KB rings no longer fit two
-//     workgroups per CU);
+//     activation slots (two stages in flight) when the grid fits one workgroup per CU: 1.5B 9.1
+//     against 9.4 us, but 7B (504 workgroups) 24.2 against 20.6, as the 80 KB rings no longer
+//     fit two workgroups per CU (the other projections lose with them too: QKV 0.5 us, down
+//     2-5 us);
 //   * gate/up up to 128 rows (above, gemm_shapes_kernel's three shapes): weight stages of 256 bytes
 //     per row;
 //   * down: 128-row chunks; 128-column groups when a K-split spans at least 1024 elements (the
@@ -94,7 +97,7 @@ GemmCfg pick_gemm(GemmKind kind, int n_cols, int k, int max_rows) {
     c.splits = splits_for(kind, n_cols, k);
     switch (kind) {
     case GEMM_QKV: c.ntw = 4; c.tm = 1; c.ksub = 1; c.nbw = 3; c.nba = 2; break;
-    case GEMM_O: c.ntw = 4; c.tm = 2; c.ksub = 1; c.nbw = 4; c.nba = 3; break;
+    case GEMM_O: c.ntw = 4; c.tm = 2; c.ksub = 1; c.nbw = 4; c.nba = 2; break;
     case GEMM_GATE_UP: c.ntw = 4; c.tm = 1; c.ksub = 2; c.nbw = 2; c.nba = 2; break;
     case GEMM_DOWN:
         if (k / c.splits >= 1024) { c.ntw = 8; c.tm = 2; c.ksub = 1; c.nbw = 3; c.nba = 2; }
@@ -104,6 +107,13 @@ GemmCfg pick_gemm(GemmKind kind, int n_cols, int k, int max_rows) {
     if (max_rows <= 64) { c.ntw = 2; c.wn = 2; c.tm = 2; c.ksub = 2; c.nbw = 2; c.nba = 2; }
     const int cap = gemm_group_cols(c);
     c.groups = (n_cols + cap - 1) / cap;
+    // o_proj: a third activation slot while its workgroups fit one per CU (the 80 KB rings leave
+    // no room for a second)
+    if (kind == GEMM_O && c.wn == 1) {
+        const int rows = gemm_chunk_rows(c);
+        const long wgs = static_cast<long>(c.groups) * ((max_rows + rows - 1) / rows) * c.splits;
+        c.nba = wgs <= kNumCUs ? 3 : 2;
+    }
     // the recompute-row projections keep two row workgroups per column group however small M
     // is (the split counts assume them)
     c.min_chunks = (kind == GEMM_QKV || kind == GEMM_GATE_UP) ? 2 : 1;
