@@ -29,6 +29,7 @@ struct Layout {
     GemmCfg c_qkv, c_o, c_gu, c_down;
     GemmCfg c_gu_shapes[3];      // gate/up tile shapes for up to gu_upto[0], up to gu_upto[1], and more rows
     int gu_upto[2];
+    GemmCfg c_gu_shapes_few[3];  // the same when few rows are expected to recompute (delta > 0)
     bool gu_multi;               // false: c_gu for every row count
     size_t rho, fold, inv_rms, rec_rows, rec_count, branch_off, row_slot, src_branch, src_slot;
     size_t xn1, xn2, q_c, k_c, v_c, attn, h_mid, act, gemm_part, attn_o, attn_ml;
@@ -113,6 +114,7 @@ GemmCfg pick_gemm(GemmKind kind, int n_cols, int k, int max_rows) {
         const int rows = gemm_chunk_rows(c);
         const long wgs = static_cast<long>(c.groups) * ((max_rows + rows - 1) / rows) * c.splits;
         c.nba = wgs <= kNumCUs ? 3 : 2;
+        c.lw = wgs <= kNumCUs ? 4 : 0;
     }
     // the recompute-row projections keep two row workgroups per column group however small M
     // is (the split counts assume them)
@@ -146,6 +148,20 @@ void pick_gate_up_shapes(int F, GemmCfg* c, int* upto) {
     upto[1] = k == 1 ? 256 : 128;
 }
 
+// The gate/up shapes when few rows are expected to recompute (the layer's threshold folds
+// rows): where the few-rows grid is one workgroup per CU (k = 1) and the 48-column tiles cover
+// a group, the shapes with four load waves beside the compute waves and three activation slots
+// (1.5B, M = 108-118: 19.1 against 20.2 us); otherwise those of pick_gate_up_shapes.  The
+// device still picks by M, so more rows than expected stay correct, only slower.
+void pick_gate_up_shapes_few(int F, const GemmCfg* dense, GemmCfg* c) {
+    for (int i = 0; i < 3; ++i) c[i] = dense[i];
+    const int k = (F + 256 * 64 - 1) / (256 * 64);
+    if (k != 1 || dense[0].ntw != 6) return;
+    c[0].nbw = 4; c[0].nba = 3; c[0].lw = 4;
+    c[1].nbw = 4; c[1].nba = 3; c[1].lw = 4;
+    c[2].lw = 4;
+}
+
 Layout layout_of(const Dims& d) {
     Layout L;
     // the recompute projections expect about 128 busy rows (folded M); o_proj has all R rows
@@ -153,7 +169,10 @@ Layout layout_of(const Dims& d) {
     L.c_o = pick_gemm(GEMM_O, d.D, d.Do, d.R);
     L.c_gu = pick_gemm(GEMM_GATE_UP, d.F, d.D, d.R);
     L.gu_multi = d.R > 128;
-    if (L.gu_multi) pick_gate_up_shapes(d.F, L.c_gu_shapes, L.gu_upto);
+    if (L.gu_multi) {
+        pick_gate_up_shapes(d.F, L.c_gu_shapes, L.gu_upto);
+        pick_gate_up_shapes_few(d.F, L.c_gu_shapes, L.c_gu_shapes_few);
+    }
     L.c_down = pick_gemm(GEMM_DOWN, d.D, d.F, d.R);
     L.s_qkv = L.c_qkv.splits; L.s_o = L.c_o.splits; L.s_down = L.c_down.splits;
     L.chunk_len = d.P <= 1024 ? 128 : 512;
@@ -393,13 +412,14 @@ hipError_t run_out_proj(const Dims& d, const Layout& L, const uint16_t* attn, co
 hipError_t run_ffn(const Dims& d, const Layout& L, const uint16_t* xn2, const uint16_t* h_mid,
                    const int32_t* rec_rows, const int32_t* rec_count, const int32_t* src_slot,
                    const uint16_t* w_gate_up, const uint16_t* w_down, uint16_t* H_out, void* ws, hipStream_t st,
-                   Tracer* tr) {
+                   Tracer* tr, bool few_rows = false) {
     GemmArgs g{};
     g.A = xn2; g.lda = d.D; g.a_rows = rec_rows; g.a_row_limit = d.R; g.m_count = rec_count;
     g.m_cap = d.R; g.W = w_gate_up; g.K = d.D; g.Nout = 2 * d.F;
     g.act = at<uint16_t>(ws, L.act); g.F = d.F;
     if (tr) tr->begin();
-    hipError_t e = L.gu_multi ? launch_gemm_shapes(g, L.c_gu_shapes, L.gu_upto, st) : launch_gemm(g, L.c_gu, st);
+    hipError_t e = L.gu_multi ? launch_gemm_shapes(g, few_rows ? L.c_gu_shapes_few : L.c_gu_shapes, L.gu_upto, st)
+                              : launch_gemm(g, L.c_gu, st);
     if (tr) tr->end();
     if (e != hipSuccess) return e;
     GemmArgs h{};
@@ -479,7 +499,7 @@ int launch_layer(const Dims& d, const Layout& L, const ParentMap& par, const spe
     if ((he = run_out_proj(d, L, attn, H_in, w->w_o, h_mid, w->ln2, xn2, ws, st, &tr)) != hipSuccess)
         return hip_status(he);
     if ((he = run_ffn(d, L, xn2, h_mid, rec_rows, rec_count, src_slot, w->w_gate_up, w->w_down, H_out, ws, st,
-                      &tr)) != hipSuccess)
+                      &tr, delta > 0.0f)) != hipSuccess)
         return hip_status(he);
     return SPECFOLD_OK;
 }

@@ -116,7 +116,8 @@ __device__ __forceinline__ void block_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// Compact the recompute rows (fold == 0) of R rows into s_rows (ascending), 256 threads.
+// Compact the recompute rows (fold == 0) of R rows into s_rows (ascending), on the first 256
+// threads of the workgroup (load waves, where a kernel has them, only pass the barriers).
 // Returns M.  When publish, also writes the global list, offsets, row_slot and fold sources.
 // The flags of the first kPre * 256 rows are requested in one batch (one memory round trip
 // instead of one per 256 rows) and kept in LDS (s_fold), with the parent map, so the source
@@ -125,28 +126,30 @@ __device__ int compact_in_lds(const GemmArgs& p, int32_t* s_rows, uint8_t* s_fol
     constexpr int kPre = 4;
     __shared__ int s_par[kMaxBranches];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool act = tid < 256;
     const int R = p.fc_R, N = p.fc_N;
-    if (publish && tid < p.fc_nb) s_par[tid] = p.fc_par.p[tid];
+    if (publish && act && tid < p.fc_nb) s_par[tid] = p.fc_par.p[tid];
     uint8_t pre[kPre];
 #pragma unroll
     for (int k = 0; k < kPre; ++k) {
         const int r = k * 256 + tid;
-        pre[k] = r < R ? p.fc_fold[r] : 1;
+        pre[k] = act && r < R ? p.fc_fold[r] : 1;
     }
     int base = 0;
     auto step = [&](int r0, uint8_t f) {
         const int r = r0 + tid;
-        const bool rec = (r < R) && (f == 0);
-        if (r < R) s_fold[r] = f;
+        const bool in = act && r < R;
+        const bool rec = in && (f == 0);
+        if (in) s_fold[r] = f;
         const uint64_t m = __ballot(rec);
         const int excl = __popcll(m & ((1ull << lane) - 1ull));
-        if (lane == 0) s_tot[wave] = __popcll(m);
+        if (lane == 0 && act) s_tot[wave] = __popcll(m);
         __syncthreads();
         const int t0 = s_tot[0], t1 = s_tot[1], t2 = s_tot[2], t3 = s_tot[3];
         const int woff = (wave > 0 ? t0 : 0) + (wave > 1 ? t1 : 0) + (wave > 2 ? t2 : 0);
         const int slot = base + woff + excl;
         if (rec) s_rows[slot] = r;
-        if (publish && r < R) {
+        if (publish && in) {
             p.fc_row_slot[r] = rec ? slot : -1;
             if (rec) p.fc_rec_rows[slot] = r;
             if (r % N == 0) p.fc_branch_off[r / N] = slot;
@@ -157,7 +160,7 @@ __device__ int compact_in_lds(const GemmArgs& p, int32_t* s_rows, uint8_t* s_fol
 #pragma unroll
     for (int k = 0; k < kPre; ++k)
         if (k * 256 < R) step(k * 256, pre[k]);
-    for (int r0 = kPre * 256; r0 < R; r0 += 256) step(r0, r0 + tid < R ? p.fc_fold[r0 + tid] : 1);
+    for (int r0 = kPre * 256; r0 < R; r0 += 256) step(r0, act && r0 + tid < R ? p.fc_fold[r0 + tid] : 1);
     if (publish) {
         if (tid == 0) {
             p.fc_rec_count[0] = base;
@@ -166,7 +169,7 @@ __device__ int compact_in_lds(const GemmArgs& p, int32_t* s_rows, uint8_t* s_fol
         }
         // fold sources: walk each row's chain up the parent map (branch 0 terminates);
         // slots come from the LDS list by binary search
-        for (int r = tid; r < R; r += 256) {
+        for (int r = tid; act && r < R; r += 256) {
             const int i = r / N, n = r - i * N;
             int j = i;
             for (int s = 0; s < p.fc_nb && j > 0 && s_fold[j * N + n] != 0; ++s) j = s_par[j];
@@ -216,7 +219,7 @@ struct Tile {
 
 // One workgroup's share of the product for M rows: workgroup `lin` of a launch with S K-splits
 // (smem: the rings, s_rows: the fused compaction's row list).
-template <int NTW, int WN, int TM, int KSUB, int NBW, int NBA, int EPI>
+template <int NTW, int WN, int TM, int KSUB, int NBW, int NBA, int EPI, int LW>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int M, const int lin, const int S, uint8_t* smem,
                                           const int32_t* s_rows) {
     using T = Tile<NTW, WN, TM, KSUB, NBW, NBA>;
@@ -283,40 +286,48 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int M, const 
         return col < c1 ? col : -1;
     };
 
-    // ---- ring loads (1 KB per wave each).  Weight load q of this wave fills weight-slot rows
-    // (q*4 + wave) * (1024 / WRB) + lane / WLPR; the lane takes physical chunk lane % WLPR of the
-    // row, which holds logical chunk (lane % WLPR) ^ (row & 15).  Activation load q fills slot
-    // rows (q*4 + wave)*8 + lane/8, physical chunk lane & 7 = logical chunk (lane & 7) ^ (row & 7).
+    // ---- ring loads (1 KB per wave each), issued by four waves: the compute waves themselves
+    // (LW = 0), or four load waves beside them (LW = 4: waves 4-7 only issue loads, so a stage's
+    // issue runs beside the multiplication instead of before it).  Issuing wave lw's weight load
+    // q fills weight-slot rows (q*4 + lw) * (1024 / WRB) + lane / WLPR; the lane takes physical
+    // chunk lane % WLPR of the row, which holds logical chunk (lane % WLPR) ^ (row & 15).
+    // Activation load q fills slot rows (q*4 + lw)*8 + lane/8, physical chunk lane & 7 =
+    // logical chunk (lane & 7) ^ (row & 7).
+    static_assert(LW == 0 || LW == 4, "no load waves, or four");
+    const bool issuer = LW == 0 || wave >= 4;      // wave-uniform
+    const int lw = LW == 0 ? wave : wave - 4;
     constexpr int WLPR = T::WLPR, RPL = 1024 / T::WRB;     // weight rows per load
     const __amdgpu_buffer_rsrc_t rW = make_rsrc(p.W, static_cast<uint32_t>(static_cast<size_t>(p.Nout) * p.K * 2));
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, static_cast<uint32_t>(static_cast<size_t>(p.a_row_limit) * p.lda * 2));
     uint32_t woff[QW], aoff[QA];
     int wlk[QW];                                   // logical K offset of the lane's weight chunk
-#pragma unroll
-    for (int q = 0; q < QW; ++q) {
-        const int r = (q * 4 + wave) * RPL + lane / WLPR;
-        wlk[q] = ((lane % WLPR) ^ (r & (WLPR - 1) & 15)) * 8;
-        const int gr = w_row(r);
-        woff[q] = (gr >= 0 ? static_cast<uint32_t>(static_cast<size_t>(gr) * p.K * 2) : kOobRow) +
-                  static_cast<uint32_t>(wlk[q] * 2);
-    }
     const int alk = ((lane & 7) ^ ((lane >> 3) & 7)) * 8;
-    // the rows' sources first, every lookup of the wave issued before any is used (a clamped
-    // index keeps them unconditional), then the offsets: one round trip for a row list in
-    // memory instead of one per load
-    int src[QA];
+    if (issuer) {
 #pragma unroll
-    for (int q = 0; q < QA; ++q) {
-        const int m = (q * 4 + wave) * 8 + (lane >> 3);
-        const int mc = m0 + (m < mrows ? m : 0);
-        src[q] = fused ? s_rows[mc] : (p.a_rows ? p.a_rows[mc] : mc);
-    }
+        for (int q = 0; q < QW; ++q) {
+            const int r = (q * 4 + lw) * RPL + lane / WLPR;
+            wlk[q] = ((lane % WLPR) ^ (r & (WLPR - 1) & 15)) * 8;
+            const int gr = w_row(r);
+            woff[q] = (gr >= 0 ? static_cast<uint32_t>(static_cast<size_t>(gr) * p.K * 2) : kOobRow) +
+                      static_cast<uint32_t>(wlk[q] * 2);
+        }
+        // the rows' sources first, every lookup of the wave issued before any is used (a
+        // clamped index keeps them unconditional), then the offsets: one round trip for a row
+        // list in memory instead of one per load
+        int src[QA];
 #pragma unroll
-    for (int q = 0; q < QA; ++q) {
-        const int m = (q * 4 + wave) * 8 + (lane >> 3);
-        const bool ok = m < mrows && src[q] >= 0 && src[q] < p.a_row_limit;
-        aoff[q] = (ok ? static_cast<uint32_t>(static_cast<size_t>(src[q]) * p.lda * 2) : kOobRow) +
-                  static_cast<uint32_t>(alk * 2);
+        for (int q = 0; q < QA; ++q) {
+            const int m = (q * 4 + lw) * 8 + (lane >> 3);
+            const int mc = m0 + (m < mrows ? m : 0);
+            src[q] = fused ? s_rows[mc] : (p.a_rows ? p.a_rows[mc] : mc);
+        }
+#pragma unroll
+        for (int q = 0; q < QA; ++q) {
+            const int m = (q * 4 + lw) * 8 + (lane >> 3);
+            const bool ok = m < mrows && src[q] >= 0 && src[q] < p.a_row_limit;
+            aoff[q] = (ok ? static_cast<uint32_t>(static_cast<size_t>(src[q]) * p.lda * 2) : kOobRow) +
+                      static_cast<uint32_t>(alk * 2);
+        }
     }
     uint8_t* const wring = smem;
     uint8_t* const aring = smem + NBW * T::WSLOT;
@@ -326,7 +337,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int M, const 
 #pragma unroll
         for (int q = 0; q < QW; ++q) {
             const uint32_t kb = k0 + wlk[q] < k_stop ? static_cast<uint32_t>(k0 * 2) : kOobK;
-            dma16(rW, slot + (q * 4 + wave) * 1024, woff[q] + kb);
+            dma16(rW, slot + (q * 4 + lw) * 1024, woff[q] + kb);
         }
     };
     auto issue_a = [&](int t) {                    // activation stage t -> slot t % NBA
@@ -334,8 +345,48 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int M, const 
         const int k0 = k_begin + t * kStageK;
         const uint32_t kb = k0 + alk < k_stop ? static_cast<uint32_t>(k0 * 2) : kOobK;
 #pragma unroll
-        for (int q = 0; q < QA; ++q) dma16(rA, slot + (q * 4 + wave) * 1024, aoff[q] + kb);
+        for (int q = 0; q < QA; ++q) dma16(rA, slot + (q * 4 + lw) * 1024, aoff[q] + kb);
     };
+
+    // ---- the rings.  Prologue: weight stages 0 .. LWU-1, then activation stages 0 .. LA-1.
+    // Iteration t waits for activation stage t (and with it everything requested earlier),
+    // then requests activation stage t + LA and, when t starts weight stage u, weight stage
+    // u + LWU.  Weight stage t / KSUB is always requested before activation stage t
+    // (KSUB * LWU > LA), so one wait covers both; it leaves out exactly the loads this wave
+    // issued after activation stage t: activation stages t+1 .. t+LA-1 and the weight stages
+    // requested in iterations max(0, t-LA) .. t-1.  With load waves, they wait and issue and
+    // the compute waves pass the same nst barriers (and no other in gemm_tile) and multiply.
+    constexpr int LWU = T::LWU, LA = T::LA;
+    auto issue_prologue = [&]() {
+#pragma unroll
+        for (int u = 0; u < LWU; ++u)
+            if (u < nws) issue_w(u);
+#pragma unroll
+        for (int t = 0; t < LA; ++t)
+            if (t < nst) issue_a(t);
+    };
+    auto wait_stage = [&](int t) {
+        int n_w = 0;
+        for (int i = max(0, t - LA); i < t; ++i)
+            if (i % KSUB == 0 && i / KSUB + LWU < nws) ++n_w;
+        const int n_a = max(0, min(LA - 1, nst - 1 - t));
+        vm_wait_le<(QA < QW ? QA : QW), T::MAXN>(n_a * QA + n_w * QW);
+    };
+    auto issue_next = [&](int t) {
+        if (t + LA < nst) issue_a(t + LA);
+        if (t % KSUB == 0 && t / KSUB + LWU < nws) issue_w(t / KSUB + LWU);
+    };
+    if constexpr (LW > 0) {
+        if (issuer) {
+            issue_prologue();
+            for (int t = 0; t < nst; ++t) {
+                wait_stage(t);
+                block_barrier();                   // stage t landed; the slots of t-1 are free
+                issue_next(t);
+            }
+            return;
+        }
+    }
 
     // ---- fragment reads: lane reads row fr = lane & 15 of a 16-row tile at logical chunk
     // 8j + 4kk + (lane >> 4) of compute stage j of the weight stage, k-step kk (weights: XOR row
@@ -377,31 +428,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int M, const 
 #pragma unroll
             for (int j = 0; j < NTW; ++j) acc[i][j] = mma(f1[j], f1[NTW + i], acc[i][j]);
     };
-
-    // ---- the rings.  Prologue: weight stages 0 .. LWU-1, then activation stages 0 .. LA-1.
-    // Iteration t waits for activation stage t (and with it everything requested earlier),
-    // then requests activation stage t + LA and, when t starts weight stage u, weight stage
-    // u + LWU.  Weight stage t / KSUB is always requested before activation stage t
-    // (KSUB * LWU > LA), so one wait covers both; it leaves out exactly the loads this wave
-    // issued after activation stage t: activation stages t+1 .. t+LA-1 and the weight stages
-    // requested in iterations max(0, t-LA) .. t-1.
-    constexpr int LWU = T::LWU, LA = T::LA;
-#pragma unroll
-    for (int u = 0; u < LWU; ++u)
-        if (u < nws) issue_w(u);
-#pragma unroll
-    for (int t = 0; t < LA; ++t)
-        if (t < nst) issue_a(t);
-    for (int t = 0; t < nst; ++t) {
-        int n_w = 0;
-        for (int i = max(0, t - LA); i < t; ++i)
-            if (i % KSUB == 0 && i / KSUB + LWU < nws) ++n_w;
-        const int n_a = max(0, min(LA - 1, nst - 1 - t));
-        vm_wait_le<(QA < QW ? QA : QW), T::MAXN>(n_a * QA + n_w * QW);
-        block_barrier();                           // stage t landed for every wave; slots of t-1 free
-        if (t + LA < nst) issue_a(t + LA);
-        if (t % KSUB == 0 && t / KSUB + LWU < nws) issue_w(t / KSUB + LWU);
-        compute(t);
+    if constexpr (LW > 0) {
+        for (int t = 0; t < nst; ++t) {
+            block_barrier();                       // stage t landed; the slots of t-1 are free
+            compute(t);
+        }
+    } else {
+        issue_prologue();
+        for (int t = 0; t < nst; ++t) {
+            wait_stage(t);
+            block_barrier();                       // stage t landed for every wave; slots of t-1 free
+            issue_next(t);
+            compute(t);
+        }
     }
 
     // ---- epilogue: lane holds C[row m][cols n0 + 4*(lane>>4) + q] of tile (i, j)
@@ -462,8 +501,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int M, const 
     }
 }
 
-template <int NTW, int WN, int TM, int KSUB, int NBW, int NBA, int EPI>
-__global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
+template <int NTW, int WN, int TM, int KSUB, int NBW, int NBA, int EPI, int LW>
+__global__ __launch_bounds__(256 + 64 * LW) void gemm_kernel(const GemmArgs p) {
     using T = Tile<NTW, WN, TM, KSUB, NBW, NBA>;
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ int s_tot[4];
@@ -477,7 +516,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs p) {
     }
     M = M < 0 ? 0 : (M > p.m_cap ? p.m_cap : M);
     M = __builtin_amdgcn_readfirstlane(M);
-    gemm_tile<NTW, WN, TM, KSUB, NBW, NBA, EPI>(p, M, blockIdx.x + gridDim.x * blockIdx.y, gridDim.y, smem, s_rows);
+    gemm_tile<NTW, WN, TM, KSUB, NBW, NBA, EPI, LW>(p, M, blockIdx.x + gridDim.x * blockIdx.y, gridDim.y, smem, s_rows);
 }
 
 // Raise a kernel's dynamic-LDS cap to at least `lds` bytes.  `cap` holds the cap raised so far
@@ -495,14 +534,16 @@ inline hipError_t raise_lds_cap(const void* kern, size_t lds, std::atomic<size_t
 }
 
 // A tile shape as a type, for the launch that holds several
-template <int NTW, int WN, int TM, int KSUB, int NBW, int NBA>
+template <int NTW, int WN, int TM, int KSUB, int NBW, int NBA, int LW_>
 struct Shape {
     using T = Tile<NTW, WN, TM, KSUB, NBW, NBA>;
+    static constexpr int LW = LW_;
     static bool is(const GemmCfg& c) {
-        return c.ntw == NTW && c.wn == WN && c.tm == TM && c.ksub == KSUB && c.nbw == NBW && c.nba == NBA;
+        return c.ntw == NTW && c.wn == WN && c.tm == TM && c.ksub == KSUB && c.nbw == NBW && c.nba == NBA &&
+               c.lw == LW;
     }
     static __device__ __forceinline__ void run(const GemmArgs& p, int M, uint8_t* smem) {
-        gemm_tile<NTW, WN, TM, KSUB, NBW, NBA, EPI_SWIGLU>(p, M, blockIdx.x, 1, smem, nullptr);
+        gemm_tile<NTW, WN, TM, KSUB, NBW, NBA, EPI_SWIGLU, LW>(p, M, blockIdx.x, 1, smem, nullptr);
     }
 };
 
@@ -512,7 +553,7 @@ struct Shape {
 // of its grid (the largest shape's).  The LDS is the largest shape's; p[i] carries shape i's
 // groups and chunks.
 template <class SA, class SB, class SC>
-__global__ __launch_bounds__(256) void gemm_shapes_kernel(const GemmArgs pa, const GemmArgs pb, const GemmArgs pc,
+__global__ __launch_bounds__(256 + 64 * SA::LW) void gemm_shapes_kernel(const GemmArgs pa, const GemmArgs pb, const GemmArgs pc,
                                                           const int upto_a, const int upto_b) {
     extern __shared__ __align__(16) uint8_t smem[];
     int M = pa.m_count ? pa.m_count[0] : pa.m_fixed;
@@ -528,7 +569,7 @@ bool groups_fit(int groups, int ncols) {
     return static_cast<uint64_t>(groups) * static_cast<uint64_t>((ncols + 3) / 4) < (uint64_t(1) << 32);
 }
 
-template <int NTW, int WN, int TM, int KSUB, int NBW, int NBA, int EPI>
+template <int NTW, int WN, int TM, int KSUB, int NBW, int NBA, int EPI, int LW>
 hipError_t launch_shape(GemmArgs a, const GemmCfg& c, int splits, hipStream_t st) {
     using T = Tile<NTW, WN, TM, KSUB, NBW, NBA>;
     // the partial-sum and SwiGLU epilogues store whole 4-column units; only the greedy-token
@@ -542,17 +583,18 @@ hipError_t launch_shape(GemmArgs a, const GemmCfg& c, int splits, hipStream_t st
     if (a.m_chunks < 1) a.m_chunks = 1;
     // the fused compaction's row list (4 bytes per row) and flags (1 byte per row)
     const size_t lds = static_cast<size_t>(T::LDS) + (a.fc_fold ? static_cast<size_t>(a.fc_R) * 5 : 0);
-    auto kern = gemm_kernel<NTW, WN, TM, KSUB, NBW, NBA, EPI>;
+    auto kern = gemm_kernel<NTW, WN, TM, KSUB, NBW, NBA, EPI, LW>;
     static std::atomic<size_t> cap{0};
     hipError_t e = raise_lds_cap(reinterpret_cast<const void*>(kern), lds, cap);
     if (e != hipSuccess) return e;
     const dim3 grid(((groups + 7) / 8) * 8 * a.m_chunks, splits);
-    hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, a);
+    hipLaunchKernelGGL(kern, grid, dim3(256 + 64 * LW), lds, st, a);
     return hipGetLastError();
 }
 
 template <class SA, class SB, class SC>
 hipError_t launch_shapes(GemmArgs a, const GemmCfg* c, const int* upto, hipStream_t st) {
+    static_assert(SA::LW == SB::LW && SB::LW == SC::LW, "one launch, one workgroup size");
     a.fc_fold = nullptr;
     GemmArgs p[3] = {a, a, a};
     const int mp[3] = {SA::T::MP, SB::T::MP, SC::T::MP};
@@ -575,7 +617,7 @@ hipError_t launch_shapes(GemmArgs a, const GemmCfg* c, const int* upto, hipStrea
     static std::atomic<size_t> cap{0};
     hipError_t e = raise_lds_cap(reinterpret_cast<const void*>(kern), lds, cap);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, p[0], p[1], p[2], upto[0], upto[1]);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256 + 64 * SA::LW), lds, st, p[0], p[1], p[2], upto[0], upto[1]);
     return hipGetLastError();
 }
 
@@ -595,12 +637,13 @@ size_t gemm_lds_bytes(const GemmCfg& c) {
 }
 
 hipError_t launch_gemm(const GemmArgs& a, const GemmCfg& c, hipStream_t st) {
-#define SPECFOLD_GEMM_CASE(NTW_, WN_, TM_, KS_, NBW_, NBA_)                                         \
-    if (c.ntw == NTW_ && c.wn == WN_ && c.tm == TM_ && c.ksub == KS_ && c.nbw == NBW_ && c.nba == NBA_)  \
-        return c.argmax ? (WN_ == 1 ? launch_shape<NTW_, WN_, TM_, KS_, NBW_, NBA_, EPI_ARGMAX>(a, c, 1, st)  \
+#define SPECFOLD_GEMM_CASE(NTW_, WN_, TM_, KS_, NBW_, NBA_, LW_)                                    \
+    if (c.ntw == NTW_ && c.wn == WN_ && c.tm == TM_ && c.ksub == KS_ && c.nbw == NBW_ && c.nba == NBA_ &&  \
+        c.lw == LW_)                                                                               \
+        return c.argmax ? (WN_ == 1 ? launch_shape<NTW_, WN_, TM_, KS_, NBW_, NBA_, EPI_ARGMAX, LW_>(a, c, 1, st) \
                                     : hipErrorInvalidValue)                                            \
-             : c.swiglu ? launch_shape<NTW_, WN_, TM_, KS_, NBW_, NBA_, EPI_SWIGLU>(a, c, 1, st)          \
-                        : launch_shape<NTW_, WN_, TM_, KS_, NBW_, NBA_, EPI_PARTIAL>(a, c, c.splits, st);
+             : c.swiglu ? launch_shape<NTW_, WN_, TM_, KS_, NBW_, NBA_, EPI_SWIGLU, LW_>(a, c, 1, st)     \
+                        : launch_shape<NTW_, WN_, TM_, KS_, NBW_, NBA_, EPI_PARTIAL, LW_>(a, c, c.splits, st);
     SPECFOLD_GEMM_CASES(SPECFOLD_GEMM_CASE)
 #undef SPECFOLD_GEMM_CASE
     return hipErrorInvalidValue;
@@ -610,11 +653,11 @@ hipError_t launch_gemm_shapes(const GemmArgs& a, const GemmCfg* c, const int* up
     if (a.fc_fold != nullptr || upto[0] < 0 || upto[1] < upto[0]) return hipErrorInvalidValue;
     for (int i = 0; i < 3; ++i)
         if (!c[i].swiglu || c[i].argmax) return hipErrorInvalidValue;
-#define SPECFOLD_GEMM_TRIPLE(A0, A1, A2, A3, A4, A5, B0, B1, B2, B3, B4, B5, C0, C1, C2, C3, C4, C5)      \
+#define SPECFOLD_GEMM_TRIPLE(A0, A1, A2, A3, A4, A5, B0, B1, B2, B3, B4, B5, C0, C1, C2, C3, C4, C5, LW_) \
     {                                                                                              \
-        using SA = Shape<A0, A1, A2, A3, A4, A5>;                                                  \
-        using SB = Shape<B0, B1, B2, B3, B4, B5>;                                                  \
-        using SC = Shape<C0, C1, C2, C3, C4, C5>;                                                  \
+        using SA = Shape<A0, A1, A2, A3, A4, A5, LW_>;                                             \
+        using SB = Shape<B0, B1, B2, B3, B4, B5, LW_>;                                             \
+        using SC = Shape<C0, C1, C2, C3, C4, C5, LW_>;                                             \
         if (SA::is(c[0]) && SB::is(c[1]) && SC::is(c[2])) return launch_shapes<SA, SB, SC>(a, c, upto, st); \
     }
     SPECFOLD_GEMM_TRIPLES(SPECFOLD_GEMM_TRIPLE)

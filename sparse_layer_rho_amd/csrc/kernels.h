@@ -99,20 +99,24 @@ struct GemmCfg {
     bool swiglu;
     int min_chunks;          // row workgroups per column group used at least (when there are that many)
     bool argmax;             // greedy-token epilogue (wn must be 1, no K split)
+    int lw;                  // 0, or 4 load waves beside the compute waves (one workgroup per CU)
 };
-// the (ntw, wn, tm, ksub, nbw, nba) shapes compiled
-#define SPECFOLD_GEMM_CASES(X) \
-    X(4, 1, 1, 2, 2, 2) X(4, 1, 1, 1, 3, 2) X(4, 1, 2, 1, 4, 2) X(2, 2, 2, 2, 2, 2) X(8, 1, 2, 1, 3, 2) X(4, 1, 2, 1, 4, 3)
+// the (ntw, wn, tm, ksub, nbw, nba, lw) shapes compiled
+#define SPECFOLD_GEMM_CASES(X)                                                                     \
+    X(4, 1, 1, 2, 2, 2, 0) X(4, 1, 1, 1, 3, 2, 0) X(4, 1, 2, 1, 4, 2, 0) X(2, 2, 2, 2, 2, 2, 0)         \
+    X(8, 1, 2, 1, 3, 2, 0) X(4, 1, 2, 1, 4, 3, 4)
 int gemm_chunk_rows(const GemmCfg& c);
 int gemm_group_cols(const GemmCfg& c);
 size_t gemm_lds_bytes(const GemmCfg& c);
 hipError_t launch_gemm(const GemmArgs& a, const GemmCfg& c, hipStream_t st);
 // SwiGLU projection with three tile shapes in one launch: c[0] for M <= upto[0] rows, c[1] for
 // M <= upto[1], c[2] above, chosen on the device (no fused compaction).  Every shape forms each
-// output's sum in the same order.  The (c[0] ; c[1] ; c[2]) triples compiled:
+// output's sum in the same order.  The (c[0] ; c[1] ; c[2] ; lw, the same for all three)
+// triples compiled:
 #define SPECFOLD_GEMM_TRIPLES(X)                                                                   \
-    X(6, 1, 1, 1, 3, 2, 6, 1, 2, 1, 3, 2, 8, 1, 2, 1, 3, 2)                                        \
-    X(8, 1, 1, 1, 3, 2, 8, 1, 2, 1, 3, 2, 8, 1, 2, 1, 3, 2)
+    X(6, 1, 1, 1, 3, 2, 6, 1, 2, 1, 3, 2, 8, 1, 2, 1, 3, 2, 0)                                     \
+    X(8, 1, 1, 1, 3, 2, 8, 1, 2, 1, 3, 2, 8, 1, 2, 1, 3, 2, 0)                                     \
+    X(6, 1, 1, 1, 4, 3, 6, 1, 2, 1, 4, 3, 8, 1, 2, 1, 3, 2, 4)
 hipError_t launch_gemm_shapes(const GemmArgs& a, const GemmCfg* c, const int* upto, hipStream_t st);
 
 // ------------------------------------------------------------------ GEMM epilogues
