@@ -27,6 +27,7 @@ struct Dims {
 
 struct Layout {
     GemmCfg c_qkv, c_o, c_gu, c_down;
+    GemmCfg c_down_few;          // the down projection when few rows are expected to recompute (delta > 0)
     GemmCfg c_gu_shapes[3];      // gate/up tile shapes for up to gu_upto[0], up to gu_upto[1], and more rows
     int gu_upto[2];
     GemmCfg c_gu_shapes_few[3];  // the same when few rows are expected to recompute (delta > 0)
@@ -162,6 +163,22 @@ void pick_gate_up_shapes_few(int F, const GemmCfg* dense, GemmCfg* c) {
     c[2].lw = 4;
 }
 
+// The down projection when few rows are expected to recompute (the layer's threshold folds
+// rows): where the dense plan has 64-column groups and 96-column groups times the K-splits
+// still fit one workgroup per CU, the 96-column groups -- each CU then streams its share of the
+// weights in one workgroup with one row chunk (1.5B, M = 108-115: 13.8-14.0 against
+// 15.2-15.3 us; at M = 288 the 96-column groups lose 0.3-0.6 us, so the dense plan keeps 64).
+// The split count is the dense plan's, so the choice never changes a bit.
+GemmCfg pick_down_few(const GemmCfg& dense, int n_cols) {
+    GemmCfg c = dense;
+    if (dense.ntw != 4 || dense.wn != 1 || dense.tm != 2) return c;
+    const int groups = (n_cols + 95) / 96;
+    if (static_cast<long>(groups) * dense.splits > kNumCUs) return c;
+    c.ntw = 6;
+    c.groups = groups;
+    return c;
+}
+
 Layout layout_of(const Dims& d) {
     Layout L;
     // the recompute projections expect about 128 busy rows (folded M); o_proj has all R rows
@@ -174,6 +191,7 @@ Layout layout_of(const Dims& d) {
         pick_gate_up_shapes_few(d.F, L.c_gu_shapes, L.c_gu_shapes_few);
     }
     L.c_down = pick_gemm(GEMM_DOWN, d.D, d.F, d.R);
+    L.c_down_few = pick_down_few(L.c_down, d.D);
     L.s_qkv = L.c_qkv.splits; L.s_o = L.c_o.splits; L.s_down = L.c_down.splits;
     L.chunk_len = d.P <= 1024 ? 128 : 512;
     L.n_chunks = d.P > 0 ? (d.P + L.chunk_len - 1) / L.chunk_len : 0;
@@ -427,7 +445,7 @@ hipError_t run_ffn(const Dims& d, const Layout& L, const uint16_t* xn2, const ui
     h.m_cap = d.R; h.W = w_down; h.K = d.F; h.Nout = d.D;
     h.partial = at<float>(ws, L.gemm_part);
     if (tr) tr->begin();
-    e = launch_gemm(h, L.c_down, st);
+    e = launch_gemm(h, few_rows ? L.c_down_few : L.c_down, st);
     if (tr) tr->end();
     if (e != hipSuccess) return e;
     if (tr) tr->begin();
