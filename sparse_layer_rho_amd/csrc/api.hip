@@ -168,6 +168,8 @@ void pick_gate_up_shapes_few(int F, const GemmCfg* dense, GemmCfg* c) {
 // still fit one workgroup per CU, the 96-column groups -- each CU then streams its share of the
 // weights in one workgroup with one row chunk (1.5B, M = 108-115: 13.8-14.0 against
 // 15.2-15.3 us; at M = 288 the 96-column groups lose 0.3-0.6 us, so the dense plan keeps 64).
+// Its K-splits are placed by XCD, so each XCD reads only its own columns of the activations
+// (13.4 against 13.75 us; the dense plan lost 2.6 us with it, so it keeps the plain placement).
 // The split count is the dense plan's, so the choice never changes a bit.
 GemmCfg pick_down_few(const GemmCfg& dense, int n_cols) {
     GemmCfg c = dense;
@@ -176,6 +178,7 @@ GemmCfg pick_down_few(const GemmCfg& dense, int n_cols) {
     if (static_cast<long>(groups) * dense.splits > kNumCUs) return c;
     c.ntw = 6;
     c.groups = groups;
+    c.xcd_split = true;
     return c;
 }
 

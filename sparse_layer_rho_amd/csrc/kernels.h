@@ -86,6 +86,7 @@ struct GemmArgs {
     float* arg_val;              // [group_base + n_groups][m_cap]
     int32_t* arg_idx;            // column + col_base, or -1 when the group has no candidate
     int col_base, group_base;
+    int xcd_split;               // set by the launcher from GemmCfg::xcd_split
 };
 
 // Tile shape of one launch: a workgroup covers the output columns of one of `groups` even
@@ -100,6 +101,7 @@ struct GemmCfg {
     int min_chunks;          // row workgroups per column group used at least (when there are that many)
     bool argmax;             // greedy-token epilogue (wn must be 1, no K split)
     int lw;                  // 0, or 4 load waves beside the compute waves (one workgroup per CU)
+    bool xcd_split;          // K-splits placed by XCD (partial-sum epilogue; S a multiple or divisor of 8)
 };
 // the (ntw, wn, tm, ksub, nbw, nba, lw) shapes compiled
 #define SPECFOLD_GEMM_CASES(X)                                                                     \
