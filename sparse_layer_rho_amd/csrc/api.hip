@@ -178,7 +178,7 @@ GemmCfg pick_down_few(const GemmCfg& dense, int n_cols) {
     if (static_cast<long>(groups) * dense.splits > kNumCUs) return c;
     c.ntw = 6;
     c.groups = groups;
-    c.xcd_split = true;
+    c.xcd_split = dense.splits % 8 == 0;
     return c;
 }
 

@@ -242,28 +242,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, const int M, const 
     // load some CUs twice and leave others idle).  The row workgroups of one group share
     // id % 8 and sit within 8 c_use ids of each other: they run on one XCD at about the same
     // time and the group's weights come from that XCD's L2 after the first fetched them.
-    // With xcd_split, the K-splits are placed by XCD instead (consecutive ids go round-robin to
-    // the 8 XCDs, so id % 8 names the XCD): XCD x takes the splits y = x (mod 8) of every group
-    // when S is a multiple of 8, or split x mod S of every (8/S)-th group when S divides 8.  Each
-    // XCD's L2 then fetches the activation columns of its own K ranges only, instead of all of
-    // them (8 copies of the activations crossing the fabric per launch).
+    // With xcd_split (S a multiple of 8), the K-splits are placed by XCD instead (consecutive ids
+    // go round-robin to the 8 XCDs, so id % 8 names the XCD): XCD x takes the splits y = x
+    // (mod 8) of every group, and its L2 fetches the activation columns of its own K ranges only,
+    // instead of all of them (8 copies of the activations crossing the fabric per launch).
     int y, chunk, g;
-    if (p.xcd_split && S > 1 && (S % 8 == 0 || 8 % S == 0)) {
+    if (p.xcd_split && S % 8 == 0) {
         const int x = lin & 7, j = lin >> 3;
-        if (S % 8 == 0) {
-            const int GC = p.n_groups * c_use;
-            const int ys = j / GC;
-            if (ys >= S / 8) return;
-            const int rem = j - ys * GC;
-            y = x + 8 * ys;
-            g = rem / c_use;
-            chunk = rem - g * c_use;
-        } else {
-            const int xs = 8 / S;                  // XCDs sharing a split
-            y = x % S;
-            g = (j / c_use) * xs + x / S;
-            chunk = j % c_use;
-        }
+        const int GC = p.n_groups * c_use;
+        const int ys = j / GC;
+        if (ys >= S / 8) return;
+        const int rem = j - ys * GC;
+        y = x + 8 * ys;
+        g = rem / c_use;
+        chunk = rem - g * c_use;
     } else {
         const int A = ((p.n_groups + 7) / 8) * 8 * c_use;      // busy workgroups per split
         if (lin >= S * A) return;

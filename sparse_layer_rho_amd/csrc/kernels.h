@@ -101,7 +101,7 @@ struct GemmCfg {
     int min_chunks;          // row workgroups per column group used at least (when there are that many)
     bool argmax;             // greedy-token epilogue (wn must be 1, no K split)
     int lw;                  // 0, or 4 load waves beside the compute waves (one workgroup per CU)
-    bool xcd_split;          // K-splits placed by XCD (partial-sum epilogue; S a multiple or divisor of 8)
+    bool xcd_split;          // K-splits placed by XCD (partial-sum epilogue, S a multiple of 8)
 };
 // the (ntw, wn, tm, ksub, nbw, nba, lw) shapes compiled
 #define SPECFOLD_GEMM_CASES(X)                                                                     \
