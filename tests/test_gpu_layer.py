@@ -68,6 +68,19 @@ def test_stack_shape_layer_dense_and_folded_match_oracle():
     assert np.array_equal(dense["H_out_bits"][:N], folded["H_out_bits"][:N])
 
 
+@pytest.mark.parametrize("name", ["layer-1.5b", "stack-1.5b"])
+def test_few_row_plans_match_dense_plans_bitwise(name):
+    """A positive threshold selects the plans sized for few recompute rows (gate/up tile shapes
+    with load waves, 96-column down groups with K-splits placed by XCD, prefix tiles for half the
+    rows); a threshold below every rho of these inputs folds nothing, so M = R and every row --
+    not only the main branch -- must carry the dense plans' bits: tile plans never change a sum."""
+    case = LayerCase.workload(name)
+    dense = case.run(0.0)
+    tiny = case.run(1e-30)
+    assert dense["rec_count"] == case.shape.rows and tiny["rec_count"] == case.shape.rows
+    assert np.array_equal(dense["H_out_bits"], tiny["H_out_bits"])
+
+
 def test_delta_zero_is_dense_per_branch():
     wl = WORKLOADS["tiny"]
     case = LayerCase.workload("tiny")
