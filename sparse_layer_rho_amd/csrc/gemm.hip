@@ -122,9 +122,9 @@ __device__ __forceinline__ void block_barrier() {
 // The flags of the first kPre * 256 rows are requested in one batch (one memory round trip
 // instead of one per 256 rows) and kept in LDS (s_fold), with the parent map, so the source
 // walks of the publishing workgroup read no global memory.
-__device__ int compact_in_lds(const GemmArgs& p, int32_t* s_rows, uint8_t* s_fold, int* s_tot, bool publish) {
+__device__ int compact_in_lds(const GemmArgs& p, int32_t* s_rows, uint8_t* s_fold, int* s_tot, int* s_par,
+                              bool publish) {
     constexpr int kPre = 4;
-    __shared__ int s_par[kMaxBranches];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool act = tid < 256;
     const int R = p.fc_R, N = p.fc_N;
@@ -523,12 +523,16 @@ template <int NTW, int WN, int TM, int KSUB, int NBW, int NBA, int EPI, int LW>
 __global__ __launch_bounds__(256 + 64 * LW) void gemm_kernel(const GemmArgs p) {
     using T = Tile<NTW, WN, TM, KSUB, NBW, NBA>;
     extern __shared__ __align__(16) uint8_t smem[];
-    __shared__ int s_tot[4];
+    // the fused compaction's LDS sits behind the rings in the dynamic allocation (fc_lds_bytes),
+    // so a launch without it takes the rings' bytes only: static LDS here would push an 80 KB
+    // tile just past half of a CU's 160 KB and halve the workgroups a CU holds
     int32_t* s_rows = reinterpret_cast<int32_t*>(smem + T::LDS);
     int M;
     if (p.fc_fold != nullptr) {
         uint8_t* s_fold = reinterpret_cast<uint8_t*>(s_rows + p.fc_R);
-        M = compact_in_lds(p, s_rows, s_fold, s_tot, blockIdx.x == 0 && blockIdx.y == 0);   // (group 0, chunk 0)
+        int* s_tot = reinterpret_cast<int*>(smem + T::LDS + ((static_cast<size_t>(p.fc_R) * 5 + 15) & ~size_t(15)));
+        int* s_par = s_tot + 4;
+        M = compact_in_lds(p, s_rows, s_fold, s_tot, s_par, blockIdx.x == 0 && blockIdx.y == 0);   // (group 0, chunk 0)
     } else {
         M = p.m_count ? p.m_count[0] : p.m_fixed;
     }
@@ -600,8 +604,10 @@ hipError_t launch_shape(GemmArgs a, const GemmCfg& c, int splits, hipStream_t st
     a.xcd_split = EPI == EPI_PARTIAL && c.xcd_split ? 1 : 0;
     a.m_chunks = (a.m_cap + T::MP - 1) / T::MP;
     if (a.m_chunks < 1) a.m_chunks = 1;
-    // the fused compaction's row list (4 bytes per row) and flags (1 byte per row)
-    const size_t lds = static_cast<size_t>(T::LDS) + (a.fc_fold ? static_cast<size_t>(a.fc_R) * 5 : 0);
+    // the fused compaction's row list (4 bytes per row), flags (1 byte per row), four wave totals
+    // and the parent map
+    const size_t fc_lds = a.fc_fold ? ((static_cast<size_t>(a.fc_R) * 5 + 15) & ~size_t(15)) + 4 * (4 + kMaxBranches) : 0;
+    const size_t lds = static_cast<size_t>(T::LDS) + fc_lds;
     auto kern = gemm_kernel<NTW, WN, TM, KSUB, NBW, NBA, EPI, LW>;
     static std::atomic<size_t> cap{0};
     hipError_t e = raise_lds_cap(reinterpret_cast<const void*>(kern), lds, cap);
