@@ -83,15 +83,15 @@ int splits_for(GemmKind kind, int n_cols, int k) {
 //     6.9 us against 7.7 with 32-column groups;
 //   * o_proj, all R rows: 128-row chunks, three at R = 288 instead of five of 64, so the weights
 //     are re-read least; 1.5B 8.5 against 9.2 us, 7B 19.7 against 28.4, 14B 35 against 51; three
-//     activation slots (two stages in flight) when the grid fits one workgroup per CU: 1.5B 9.1
-//     against 9.4 us, but 7B (504 workgroups) 24.2 against 20.6, as the 80 KB rings no longer
-//     fit two workgroups per CU (the other projections lose with them too: QKV 0.5 us, down
-//     2-5 us);
+//     activation slots (two stages in flight) and four load waves when the grid fits one
+//     workgroup per CU: 1.5B 9.1 against 9.4 us (7B, 504 workgroups: 20.05 against 20.08 with
+//     them, so it keeps two slots);
 //   * gate/up up to 128 rows (above, gemm_shapes_kernel's three shapes): weight stages of 256 bytes
 //     per row;
 //   * down: 128-row chunks; 128-column groups when a K-split spans at least 1024 elements (the
 //     7B and 14B shapes: 38 against 44 us at M = 108), else 64 (1.5B, 560 elements per split,
-//     where the wider tiles lose 4 us at M = 288).
+//     where the wider tiles lose 4 us at M = 288) with three activation slots (80 KB, two
+//     workgroups per CU: 1.5B dense 28.9 against 30.1-30.4 us).
 GemmCfg pick_gemm(GemmKind kind, int n_cols, int k, int max_rows) {
     GemmCfg c{};
     c.swiglu = kind == GEMM_GATE_UP;
@@ -103,7 +103,7 @@ GemmCfg pick_gemm(GemmKind kind, int n_cols, int k, int max_rows) {
     case GEMM_GATE_UP: c.ntw = 4; c.tm = 1; c.ksub = 2; c.nbw = 2; c.nba = 2; break;
     case GEMM_DOWN:
         if (k / c.splits >= 1024) { c.ntw = 8; c.tm = 2; c.ksub = 1; c.nbw = 3; c.nba = 2; }
-        else { c.ntw = 4; c.tm = 2; c.ksub = 1; c.nbw = 4; c.nba = 2; }
+        else { c.ntw = 4; c.tm = 2; c.ksub = 1; c.nbw = 4; c.nba = 3; }
         break;
     }
     if (max_rows <= 64) { c.ntw = 2; c.wn = 2; c.tm = 2; c.ksub = 2; c.nbw = 2; c.nba = 2; }
@@ -177,6 +177,7 @@ GemmCfg pick_down_few(const GemmCfg& dense, int n_cols) {
     const int groups = (n_cols + 95) / 96;
     if (static_cast<long>(groups) * dense.splits > kNumCUs) return c;
     c.ntw = 6;
+    c.nba = 2;                                    // 80 KB: two workgroups per CU above 128 rows
     c.groups = groups;
     c.xcd_split = dense.splits % 8 == 0;
     return c;

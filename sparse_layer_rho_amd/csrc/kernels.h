@@ -106,7 +106,7 @@ struct GemmCfg {
 // the (ntw, wn, tm, ksub, nbw, nba, lw) shapes compiled
 #define SPECFOLD_GEMM_CASES(X)                                                                     \
     X(4, 1, 1, 2, 2, 2, 0) X(4, 1, 1, 1, 3, 2, 0) X(4, 1, 2, 1, 4, 2, 0) X(2, 2, 2, 2, 2, 2, 0)         \
-    X(8, 1, 2, 1, 3, 2, 0) X(4, 1, 2, 1, 4, 3, 4) X(6, 1, 2, 1, 4, 2, 0)
+    X(8, 1, 2, 1, 3, 2, 0) X(4, 1, 2, 1, 4, 3, 4) X(6, 1, 2, 1, 4, 2, 0) X(4, 1, 2, 1, 4, 3, 0)
 int gemm_chunk_rows(const GemmCfg& c);
 int gemm_group_cols(const GemmCfg& c);
 size_t gemm_lds_bytes(const GemmCfg& c);
