@@ -19,8 +19,9 @@
 //     inline asm, so the compiler inserts no conservative drains; each wave waits on vmcnt for
 //     exactly the stage it is about to read and on lgkmcnt for its fragments.
 // Rows come from an identity map, a device list, or -- fused -- from the fold flags: every
-// workgroup compacts them in LDS (ascending row order) and workgroup (0,0) also publishes the
-// recompute list, per-branch offsets, row -> slot map and fold sources
+// workgroup compacts them in LDS (ascending row order) and the grid's last workgroup, one with
+// no tile of the product, also publishes the recompute list, per-branch offsets, row -> slot map
+// and fold sources
 // [SpecFold summary, App. B: compaction and source resolution feed the projection].
 // Epilogues: fp32 partial sums (reduced in a fixed order by the next kernel, so results are
 // deterministic), or SwiGLU for the FFN's gate/up projection, where a wave's two weight tiles
@@ -532,7 +533,11 @@ __global__ __launch_bounds__(256 + 64 * LW) void gemm_kernel(const GemmArgs p) {
         uint8_t* s_fold = reinterpret_cast<uint8_t*>(s_rows + p.fc_R);
         int* s_tot = reinterpret_cast<int*>(smem + T::LDS + ((static_cast<size_t>(p.fc_R) * 5 + 15) & ~size_t(15)));
         int* s_par = s_tot + 4;
-        M = compact_in_lds(p, s_rows, s_fold, s_tot, s_par, blockIdx.x == 0 && blockIdx.y == 0);   // (group 0, chunk 0)
+        // the grid's last workgroup publishes: busy workgroups take the lowest ids and the launcher
+        // adds a row of idle ones, so the publishing work (the list, the row map and every row's
+        // fold source) runs beside the projection instead of delaying one of its tiles
+        M = compact_in_lds(p, s_rows, s_fold, s_tot, s_par,
+                           blockIdx.x == gridDim.x - 1 && blockIdx.y == gridDim.y - 1);
     } else {
         M = p.m_count ? p.m_count[0] : p.m_fixed;
     }
@@ -612,7 +617,8 @@ hipError_t launch_shape(GemmArgs a, const GemmCfg& c, int splits, hipStream_t st
     static std::atomic<size_t> cap{0};
     hipError_t e = raise_lds_cap(reinterpret_cast<const void*>(kern), lds, cap);
     if (e != hipSuccess) return e;
-    const dim3 grid(((groups + 7) / 8) * 8 * a.m_chunks, splits);
+    // a fused compaction gets eight more (idle) workgroups, the last of which publishes
+    const dim3 grid(((groups + 7) / 8) * 8 * a.m_chunks + (a.fc_fold ? 8 : 0), splits);
     hipLaunchKernelGGL(kern, grid, dim3(256 + 64 * LW), lds, st, a);
     return hipGetLastError();
 }

@@ -70,7 +70,8 @@ struct GemmArgs {
     uint16_t* act;           // [m_cap][F]              (SwiGLU epilogue)
     int F;
     // fused compaction (fc_fold non-NULL): rows = recompute rows of the fold flags, compacted
-    // in LDS by every workgroup; workgroup (0,0) publishes the list and the fold sources
+    // in LDS by every workgroup; the grid's last workgroup (an idle one) publishes the list and
+    // the fold sources
     const uint8_t* fc_fold;
     int fc_R, fc_N, fc_nb;
     ParentMap fc_par;
