@@ -257,8 +257,9 @@ def layer_main(args, wl, emit=True):
         calls = max(1, args.stage_calls)
         skip = min(3, calls - 1)                  # untimed first calls
         for k in range(calls):
-            # an untraced call first, so the traced call's first launch follows queued work the way
-            # every launch of a stack does (not a launch onto an idle GPU)
+            # an untraced call first (the traced call's weight copy is then not the last one
+            # read), both queued behind a spin kernel
+            hold_queue(torch, 2.0)
             sf.verify_layer(sh, parent, lws[(k + 1) % n_copies], pf, None, H_in, delta, H_out, ws, stats=stats)
             sf.verify_layer(sh, parent, lws[k % n_copies], pf, None, H_in, delta, H_out, ws, stats=stats,
                             trace=tm.trace)
@@ -502,6 +503,26 @@ def measured_traffic(record=None):
     return rec.get("traffic_bytes") if rec.get("source_sha256") == h.hexdigest() else None
 
 
+_SPIN = {}
+
+
+def hold_queue(torch, ms):
+    """Put a spin kernel of about ``ms`` milliseconds on the current stream: the launches the
+    host queues behind it meanwhile run back to back when it ends, so per-launch event timing
+    measures the GPU and not the host's enqueue rate (an eager call that outruns the host would
+    otherwise count the host's gaps into the next launch), and the first traced launch follows
+    queued work as every launch of a stack does (not a launch onto an idle GPU)."""
+    if "cycles_per_ms" not in _SPIN:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        e0.record()
+        torch.cuda._sleep(2_000_000)
+        e1.record()
+        torch.cuda.synchronize()
+        _SPIN["cycles_per_ms"] = 2_000_000 / max(e0.elapsed_time(e1), 1e-3)
+    torch.cuda._sleep(int(ms * _SPIN["cycles_per_ms"]))
+
+
 def time_graph(torch, fns, rounds=5, warmup_replays=1, warmup_s=0.5, check=None, reps=1):
     """Capture fns (callables launching on the current stream) in one HIP graph, replay it untimed
     for at least `warmup_replays` replays and `warmup_s` seconds, then time `rounds` rounds of
@@ -696,9 +717,9 @@ def stack_measure(torch, sf, wl, layers, steps, args, dev, with_head=False, keep
 
 def stack_stage_times(torch, sf, ctx, delta, n_steps=0):
     """Event-timed duration of every launch of every layer over n_steps eager passes (default:
-    one per input step, the mix the timed graphs run), each traced pass queued behind an
-    untraced one (so no layer's first launch starts on an idle GPU).  Returns per-layer stage
-    dicts (microseconds, mean over the passes) and per-layer M."""
+    one per input step, the mix the timed graphs run), each traced pass queued behind a spin
+    kernel (hold_queue), so its launches run back to back as in the replayed graphs.  Returns
+    per-layer stage dicts (microseconds, mean over the passes) and per-layer M."""
     import numpy as np
 
     L, S = ctx["L"], ctx["S"]
@@ -707,7 +728,7 @@ def stack_stage_times(torch, sf, ctx, delta, n_steps=0):
     Ms = []
     n = min(n_steps, S) if n_steps > 0 else S
     for s in range(n):
-        ctx["run_step"]((s + 1) % S, delta, stats=False)
+        hold_queue(torch, 20.0)
         ctx["run_step"](s, delta, stats=True, traces=timers)
         torch.cuda.synchronize()
         Ms.append(ctx["cnt"][:, 0].cpu().numpy().copy())
