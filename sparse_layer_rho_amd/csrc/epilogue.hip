@@ -186,16 +186,17 @@ __global__ __launch_bounds__(1024) void oproj_epilogue_kernel(const float* __res
 // workgroup (b, part): reduces slot b (when b < M) into every row that inherits from it, over
 // the part-th of the gridDim.y ranges of column quads; also writes NaN into those columns of row
 // b when row b's source slot is invalid.  The parts spread each slot's split partials (its
-// largest input) over several CUs.
+// largest input) over several CUs.  The rows that can inherit from slot b are the rows at its
+// position n (a fold source is an ancestor's row at the same position), so their residual
+// rows are requested with the partials, before it is known which of them inherit: two round
+// trips (the slot's row, then everything else) instead of three.
 template <int SPL, int MAXU>
-__global__ __launch_bounds__(1024) void down_epilogue_kernel(const float* __restrict__ part, int splits, int m_cap,
+__global__ __launch_bounds__(128) void down_epilogue_kernel(const float* __restrict__ part, int splits, int m_cap,
                                                              const int32_t* m_count, const int32_t* rec_rows,
                                                              const int32_t* __restrict__ src_slot, int nb, int N,
                                                              int D, const uint16_t* __restrict__ h_mid,
                                                              uint16_t* __restrict__ H_out) {
-    constexpr int kBatch = 4;                      // inheriting rows loaded per round trip
-    __shared__ int s_rows[kMaxBranches];
-    __shared__ int s_cnt;
+    constexpr int kSpec = 12;                      // branches whose residual rows are loaded speculatively
     const int b = blockIdx.x, tid = threadIdx.x, B = blockDim.x;
     const int R = nb * N;
     const int D4 = D >> 2;
@@ -213,52 +214,70 @@ __global__ __launch_bounds__(1024) void down_epilogue_kernel(const float* __rest
     }
     if (b >= M || row < 0 || row >= R) return;
     const int n = row % N;
-    // second round trip: the slot's partials and the source slots of every row at position n
+    // second round trip: the slot's partials, the source slots of the rows at position n (the
+    // rows that can inherit from slot b) and, speculatively, the residual rows of the first
+    // kSpec of them, so the rows that do inherit need no third round trip
     const __amdgpu_buffer_rsrc_t rP = make_rsrc(part, static_cast<uint32_t>(static_cast<size_t>(splits) * m_cap * D * 4));
     const __amdgpu_buffer_rsrc_t rH = make_rsrc(h_mid, static_cast<uint32_t>(static_cast<size_t>(R) * D * 2));
     const uint32_t stride = static_cast<uint32_t>(m_cap) * D * 4;
-    const int cand = tid < nb ? src_slot[tid * N + n] : -1;   // first, so it is waited for alone
+    // every wave loads the candidates' source slots itself (lane t: branch t), first, so they
+    // are waited for alone
+    const int lane = tid & (kWave - 1);
+    const int cand = lane < nb ? src_slot[lane * N + n] : -1;
     f32x4 pv[MAXU][SPL];
 #pragma unroll
     for (int k = 0; k < MAXU; ++k) {
         const int u = u0 + tid + k * B;
         load_splits<SPL>(pv[k], rP, u < u1 ? (static_cast<uint32_t>(b) * D + 4 * u) * 4 : kOob, stride, splits);
     }
-    if (tid == 0) s_cnt = 0;
-    __syncthreads();
-    if (cand == b) s_rows[atomicAdd(&s_cnt, 1)] = tid * N + n;
+    uint2 hv[kSpec][MAXU];
+#pragma unroll
+    for (int t = 0; t < kSpec; ++t)
+#pragma unroll
+        for (int k = 0; k < MAXU; ++k) {
+            const int u = u0 + tid + k * B;
+            hv[t][k] = buf_load8(rH, t < nb && u < u1 ? (static_cast<uint32_t>(t * N + n) * D + 4 * u) * 2 : kOob);
+        }
+    __builtin_amdgcn_sched_barrier(0);
+    const uint64_t hit = __ballot(cand == b);      // uniform: the branches that inherit from b
     f32x4 f[MAXU];
 #pragma unroll
     for (int k = 0; k < MAXU; ++k) f[k] = add_splits<SPL>(pv[k]);
-    __syncthreads();
-    const int cnt = __builtin_amdgcn_readfirstlane(s_cnt);      // uniform: scalar loop control
-    for (int t0 = 0; t0 < cnt; t0 += kBatch) {
-        // the batch's rows from LDS in one round trip (indices clamped, so no read depends on a
-        // branch), then their residual rows in one more
-        int rows[kBatch];
 #pragma unroll
-        for (int t = 0; t < kBatch; ++t) rows[t] = s_rows[min(t0 + t, cnt - 1)];
-        uint2 hv[kBatch][MAXU];
+    for (int t = 0; t < kSpec; ++t) {
+        if (!((hit >> t) & 1)) continue;
 #pragma unroll
-        for (int t = 0; t < kBatch; ++t)
+        for (int k = 0; k < MAXU; ++k) {
+            const int u = u0 + tid + k * B;
+            if (u >= u1) continue;
+            float h[4];
+            unpack4(hv[t][k], h);
 #pragma unroll
-            for (int k = 0; k < MAXU; ++k) {
-                const int u = u0 + tid + k * B;
-                const bool valid = t0 + t < cnt && u < u1;
-                hv[t][k] = buf_load8(rH, valid ? (static_cast<uint32_t>(rows[t]) * D + 4 * u) * 2 : kOob);
-            }
+            for (int e = 0; e < 4; ++e) h[e] += f[k][e];
+            *reinterpret_cast<uint2*>(H_out + static_cast<size_t>(t * N + n) * D + 4 * u) = pack4(h);
+        }
+    }
+    // the speculative loads are needed on every path (else the compiler sinks a row's load
+    // into the branch that stores it, behind a round trip of its own)
+    uint32_t keep = 0;
 #pragma unroll
-        for (int t = 0; t < kBatch; ++t)
+    for (int t = 0; t < kSpec; ++t)
 #pragma unroll
-            for (int k = 0; k < MAXU; ++k) {
-                const int u = u0 + tid + k * B;
-                if (t0 + t >= cnt || u >= u1) continue;
-                float h[4];
-                unpack4(hv[t][k], h);
+        for (int k = 0; k < MAXU; ++k) keep ^= hv[t][k].x ^ hv[t][k].y;
+    asm volatile("" ::"v"(keep));
+    // branches past the first kSpec: one round trip per branch
+    for (int t = kSpec; t < nb; ++t) {
+        if (!((hit >> t) & 1)) continue;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) h[e] += f[k][e];
-                *reinterpret_cast<uint2*>(H_out + static_cast<size_t>(rows[t]) * D + 4 * u) = pack4(h);
-            }
+        for (int k = 0; k < MAXU; ++k) {
+            const int u = u0 + tid + k * B;
+            if (u >= u1) continue;
+            float h[4];
+            unpack4(buf_load8(rH, (static_cast<uint32_t>(t * N + n) * D + 4 * u) * 2), h);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] += f[k][e];
+            *reinterpret_cast<uint2*>(H_out + static_cast<size_t>(t * N + n) * D + 4 * u) = pack4(h);
+        }
     }
 }
 
@@ -319,16 +338,12 @@ hipError_t launch_down_epilogue(const float* part, int splits, int m_cap, const 
     const int D4 = D >> 2, parts = (D4 + 127) / 128;
     const int qp = (D4 + parts - 1) / parts, block = quad_block(qp);
     const int per = (qp + block - 1) / block;
-    if (per > 2) return hipErrorInvalidValue;
+    if (per > 1 || block > 128) return hipErrorInvalidValue;     // the kernel's launch bounds
     const dim3 grid(R > m_cap ? R : m_cap, parts);
     return with_spl(splits, [&](auto spl) {
         constexpr int SPL = decltype(spl)::value;
-        if (per == 1)
-            hipLaunchKernelGGL((down_epilogue_kernel<SPL, 1>), grid, dim3(block), 0, st, part, splits, m_cap, m_count,
-                               rec_rows, src_slot, nb, N, D, h_mid, H_out);
-        else
-            hipLaunchKernelGGL((down_epilogue_kernel<SPL, 2>), grid, dim3(block), 0, st, part, splits, m_cap, m_count,
-                               rec_rows, src_slot, nb, N, D, h_mid, H_out);
+        hipLaunchKernelGGL((down_epilogue_kernel<SPL, 1>), grid, dim3(block), 0, st, part, splits, m_cap, m_count,
+                           rec_rows, src_slot, nb, N, D, h_mid, H_out);
         return hipGetLastError();
     });
 }
