@@ -31,6 +31,10 @@ def test_verify_layer_matches_oracle(name):
     (Shape(9, 8, 192, 6, 3, 32, 320, 100), "chain"),         # deep fold chains, ragged prefix chunk
     (Shape(17, 64, 256, 8, 2, 64, 320, 300), "random"),      # R = 1088: GEMMs loop over row passes
     (Shape(5, 33, 128, 2, 2, 64, 128, 513), "star"),         # N not a multiple of 16
+    # the branch limit: rows of branches past the down epilogue's 12 speculatively loaded
+    # candidates inherit too
+    (Shape(64, 8, 128, 4, 2, 32, 192, 40), "chain"),
+    (Shape(64, 8, 128, 4, 2, 32, 192, 40), "random"),
 ])
 def test_verify_layer_edge_shapes(shape, tree):
     case = LayerCase(shape, 11, tree=tree, random_norm=True, weight_scale=8.0)
